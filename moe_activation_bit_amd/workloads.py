@@ -1,0 +1,194 @@
+"""Seeded synthetic workloads for the fused SwiGLU + top-k weight + FP8/FP4 cast.
+
+This module only draws inputs (random streams, bf16 rounding of samples,
+routing-weight normalisation); it holds none of the activation or
+quantisation arithmetic.  The tests, the benchmark and the oracle's harness
+all draw their inputs here, so both sides of every comparison see the same
+bytes.
+
+Shapes follow the MoE layout described in "【DeepSeek】TileKernels从入门到精通"
+ch.2 (a packed ``[num_expanded_tokens, 2*hidden]`` bf16 tensor, gate on the
+left half, up on the right half, one top-k weight per expanded row).
+
+Every value is a pure function of (workload, seed, tensor name, element
+index), so any row of a large tensor can be regenerated alone.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SYNTH_LIB = os.path.join(_HERE, "libsynth.so")
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, value distributions and cast options."""
+
+    name: str
+    rows: int                      # expanded rows (tokens x top-k); 0 = drawn per seed
+    hidden: int
+    sigma: float                   # std-dev of the bf16 activations
+    fmt: str                       # "fp8" (E4M3) or "fp4" (E2M1)
+    group_size: int                # 0 = one scale per row
+    scale_fmt: str                 # "fp32" or "ue8m0"
+    clamp_limit: Optional[float]   # None = no clamp
+    weights: str                   # "uniform" | "renorm8" | "zero30"
+    outlier_p: float = 0.0         # probability of replacing an element by +-outlier
+    outlier_value: float = 0.0
+    max_rows: int = 0              # for rows == 0: rows ~ U{1..max_rows}
+
+    @property
+    def code_bytes_per_row(self) -> int:
+        return self.hidden if self.fmt == "fp8" else self.hidden // 2
+
+    @property
+    def groups_per_row(self) -> int:
+        return 1 if self.group_size == 0 else self.hidden // self.group_size
+
+    @property
+    def scale_itemsize(self) -> int:
+        return 4 if self.scale_fmt == "fp32" else 1
+
+    def algorithmic_bytes(self, n: int) -> int:
+        """Bytes the step must move at least once: x + topk_weight + codes + scales."""
+        per_row = 4 * self.hidden + 4 + self.code_bytes_per_row + self.groups_per_row * self.scale_itemsize
+        return n * per_row
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # tiny per-token FP8 case, small enough for the oracle on every element
+        Workload("fp8_per_token_n256_h1024", 256, 1024, 1.0, "fp8", 0, "fp32", None, "uniform"),
+        # 4096 tokens x top-8, per-block FP8, power-of-two scales
+        Workload("fp8_g128_ue8m0_n32768_h2048", 32768, 2048, 2.0, "fp8", 128, "ue8m0", None, "renorm8"),
+        # 16384 tokens x top-8 prefill with 0.1% outliers at +-50 and clamp 10
+        Workload("fp8_per_token_clamp10_n131072_h2048", 131072, 2048, 3.0, "fp8", 0, "fp32", 10.0,
+                 "renorm8", outlier_p=0.001, outlier_value=50.0),
+        # FP4 E2M1 per-block with power-of-two scales
+        Workload("fp4_g32_ue8m0_n65536_h4096", 65536, 4096, 1.0, "fp4", 32, "ue8m0", None, "uniform"),
+        # ragged decode batch: rows drawn per seed in [1, 1000], 30% zero weights
+        Workload("fp8_g128_fp32_ragged_h7168", 0, 7168, 1.0, "fp8", 128, "fp32", None, "zero30",
+                 max_rows=1000),
+    ]
+}
+
+# The benchmark's headline workload: the per-block FP8 case.
+HEADLINE = "fp8_g128_ue8m0_n32768_h2048"
+
+
+_lib = None
+
+
+def _synth():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SYNTH_LIB):
+            raise RuntimeError(f"{SYNTH_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(SYNTH_LIB)
+        lib.synth_key.restype = ctypes.c_uint64
+        lib.synth_key.argtypes = [ctypes.c_char_p]
+        lib.synth_u64.restype = ctypes.c_uint64
+        lib.synth_u64.argtypes = [ctypes.c_uint64, ctypes.c_int64]
+        lib.synth_uniform.restype = None
+        lib.synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_normal_bf16.restype = None
+        lib.synth_normal_bf16.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_double, ctypes.c_void_p]
+        lib.synth_outliers_bf16.restype = None
+        lib.synth_outliers_bf16.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                            ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def stream_key(workload: str, seed: int, tensor: str) -> int:
+    return _synth().synth_key(f"{workload}/{seed}/{tensor}".encode())
+
+
+def uniform(key: int, first: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.float64)
+    if count:
+        _synth().synth_uniform(key, first, count, out.ctypes.data)
+    return out
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def num_rows(w: Workload, seed: int) -> int:
+    if w.rows:
+        return w.rows
+    u = uniform(stream_key(w.name, seed, "rows"), 0, 1)[0]
+    return 1 + int(math.floor(u * w.max_rows))
+
+
+def make_x(w: Workload, seed: int, rows: Optional[Sequence[int]] = None,
+           out: Optional[np.ndarray] = None) -> np.ndarray:
+    """bf16 bits of x, shape [len(rows), 2*hidden] (all rows when rows is None)."""
+    lib = _synth()
+    n = num_rows(w, seed)
+    width = 2 * w.hidden
+    if rows is None:
+        row_list = None
+        count_rows = n
+    else:
+        row_list = [int(r) for r in rows]
+        count_rows = len(row_list)
+    x = out if out is not None else np.empty((count_rows, width), dtype=np.uint16)
+    assert x.shape == (count_rows, width) and x.dtype == np.uint16 and x.flags.c_contiguous
+    k_norm = stream_key(w.name, seed, "x")
+    k_p = stream_key(w.name, seed, "outlier_p")
+    k_s = stream_key(w.name, seed, "outlier_sign")
+    base = x.ctypes.data
+
+    def fill(span):
+        lo, hi = span  # local row range
+        for i in range(lo, hi):
+            r = i if row_list is None else row_list[i]
+            ptr = base + i * width * 2
+            first = r * width
+            lib.synth_normal_bf16(k_norm, first, width, w.sigma, ptr)
+            if w.outlier_p > 0:
+                lib.synth_outliers_bf16(k_p, k_s, first, width, w.outlier_p, w.outlier_value, ptr)
+
+    if count_rows:
+        nt = min(_threads(), count_rows)
+        step = (count_rows + nt - 1) // nt
+        spans = [(i, min(count_rows, i + step)) for i in range(0, count_rows, step)]
+        if len(spans) == 1:
+            fill(spans[0])
+        else:
+            with ThreadPoolExecutor(len(spans)) as ex:
+                list(ex.map(fill, spans))
+    return x
+
+
+def make_w(w: Workload, seed: int) -> np.ndarray:
+    """fp32 top-k routing weights, shape [rows]."""
+    n = num_rows(w, seed)
+    u = uniform(stream_key(w.name, seed, "w"), 0, n)
+    if w.weights == "uniform":
+        out = u
+    elif w.weights == "renorm8":
+        # each token's 8 expanded rows are consecutive; its weights sum to 1
+        out = np.empty(n, dtype=np.float64)
+        for t0 in range(0, n, 8):
+            grp = u[t0:t0 + 8]
+            out[t0:t0 + 8] = grp / grp.sum()
+    elif w.weights == "zero30":
+        z = uniform(stream_key(w.name, seed, "w_zero"), 0, n)
+        out = np.where(z < 0.3, 0.0, u)
+    else:
+        raise ValueError(w.weights)
+    return out.astype(np.float32)

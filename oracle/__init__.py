@@ -1,0 +1,155 @@
+"""The oracle: a plain CPU statement of the fused SwiGLU + top-k weight +
+FP8/FP4 cast (see oracle.c for the sources it follows and every reading it
+takes).  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+benchmark's CPU-baseline leg may use it; the GPU library never does.
+
+numpy in, numpy out.  x is the bf16 bit pattern as uint16 [n, 2*hidden].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+
+FP8 = 8
+FP4 = 4
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+FMT_MAX = {FP8: 448.0, FP4: 6.0}
+
+_lib = None
+
+
+def build_command(out: str = LIB_PATH) -> list:
+    return ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-o", out, SOURCE,
+            "-lquadmath", "-lm"]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        lib.oracle_sigmoid.restype = c.c_float
+        lib.oracle_sigmoid.argtypes = [c.c_float]
+        lib.oracle_e4m3.restype = c.c_uint8
+        lib.oracle_e4m3.argtypes = [c.c_float]
+        lib.oracle_e2m1.restype = c.c_uint8
+        lib.oracle_e2m1.argtypes = [c.c_float]
+        lib.oracle_ue8m0_exponent.restype = c.c_int
+        lib.oracle_ue8m0_exponent.argtypes = [c.c_float, c.c_float]
+        lib.oracle_encode.restype = c.c_int
+        lib.oracle_encode.argtypes = [c.c_int, c.c_void_p, c.c_int64, c.c_void_p]
+        lib.oracle_swiglu_forward.restype = c.c_int
+        lib.oracle_swiglu_forward.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_float,
+                                              c.c_void_p, c.c_void_p]
+        lib.oracle_cast.restype = c.c_int
+        lib.oracle_cast.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_int,
+                                    c.c_void_p, c.c_void_p]
+        lib.oracle_swiglu_cast.restype = c.c_int
+        lib.oracle_swiglu_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int64,
+                                           c.c_float, c.c_int, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def sigmoid(g: float) -> float:
+    return float(np.float32(_load().oracle_sigmoid(float(g))))
+
+
+def e4m3(q: float) -> int:
+    return int(_load().oracle_e4m3(float(q)))
+
+
+def e2m1(q: float) -> int:
+    return int(_load().oracle_e2m1(float(q)))
+
+
+def encode(q: np.ndarray, fmt: int) -> np.ndarray:
+    """One code byte per fp32 value (E4M3 for fmt 8, E2M1 for fmt 4)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.empty(q.shape, dtype=np.uint8)
+    if _load().oracle_encode(fmt, q.ctypes.data, q.size, out.ctypes.data):
+        raise ValueError("oracle_encode failed")
+    return out
+
+
+def ue8m0_exponent(amax: float, fmt: int) -> int:
+    return int(_load().oracle_ue8m0_exponent(float(amax), FMT_MAX[fmt]))
+
+
+def _clamp_arg(clamp_limit: Optional[float]) -> float:
+    return math.inf if clamp_limit is None else float(clamp_limit)
+
+
+def _x(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint16 and x.ndim == 2 and x.shape[1] % 2 == 0
+    return x
+
+
+def _w(w: Optional[np.ndarray], n: int) -> Optional[np.ndarray]:
+    if w is None:
+        return None
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.shape == (n,)
+    return w
+
+
+def swiglu_forward(x: np.ndarray, w: Optional[np.ndarray],
+                   clamp_limit: Optional[float] = None) -> Tuple[np.ndarray, int]:
+    """First stage of the unfused reference: fp32 y [n, hidden] and the clamp count."""
+    x = _x(x)
+    n, hidden = x.shape[0], x.shape[1] // 2
+    w = _w(w, n)
+    y = np.empty((n, hidden), dtype=np.float32)
+    cnt = np.zeros(1, dtype=np.int64)
+    rc = _load().oracle_swiglu_forward(x.ctypes.data, None if w is None else w.ctypes.data, n, hidden,
+                                       _clamp_arg(clamp_limit), y.ctypes.data, cnt.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_swiglu_forward failed ({rc})")
+    return y, int(cnt[0])
+
+
+def _out(n: int, hidden: int, group_size: int, fmt: int, scale_fmt: int):
+    groups = 1 if group_size == 0 else hidden // group_size
+    codes = np.empty((n, hidden if fmt == FP8 else hidden // 2), dtype=np.uint8)
+    scales = np.empty((n, groups), dtype=np.float32 if scale_fmt == SCALE_FP32 else np.uint8)
+    return codes, scales
+
+
+def cast(y: np.ndarray, group_size: int, fmt: int, scale_fmt: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Second stage of the unfused reference: codes and scales from fp32 rows."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    n, hidden = y.shape
+    codes, scales = _out(n, hidden, group_size, fmt, scale_fmt)
+    rc = _load().oracle_cast(y.ctypes.data, n, hidden, group_size, fmt, scale_fmt, codes.ctypes.data,
+                             scales.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_cast failed ({rc})")
+    return codes, scales
+
+
+def swiglu_cast(x: np.ndarray, w: Optional[np.ndarray], group_size: int, clamp_limit: Optional[float],
+                fmt: int, scale_fmt: int) -> Tuple[np.ndarray, np.ndarray, int]:
+    """The fused step, row by row: (codes, scales, clamped_count)."""
+    x = _x(x)
+    n, hidden = x.shape[0], x.shape[1] // 2
+    w = _w(w, n)
+    codes, scales = _out(n, hidden, group_size, fmt, scale_fmt)
+    cnt = np.zeros(1, dtype=np.int64)
+    rc = _load().oracle_swiglu_cast(x.ctypes.data, None if w is None else w.ctypes.data, n, hidden,
+                                    group_size, _clamp_arg(clamp_limit), fmt, scale_fmt,
+                                    codes.ctypes.data, scales.ctypes.data, cnt.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_swiglu_cast failed ({rc})")
+    return codes, scales, int(cnt[0])

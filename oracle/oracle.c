@@ -1,0 +1,299 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, scalar CPU statement of the fused activation-quantisation
+ * step of an MoE expert: SwiGLU on a packed [gate | up] bf16 row, optional
+ * clamp with a clamp counter, scaling by the token's top-k routing weight,
+ * an abs-max per token or per column group, and the cast to FP8 E4M3 or
+ * FP4 E2M1 codes with an fp32 or UE8M0 (power-of-two) scale.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  The GPU library never calls it, and the two share no
+ * code, headers, tables or constants.
+ *
+ * Sources (pages on DeepSeek's TileKernels library):
+ *  [Tutorial]  "【DeepSeek】TileKernels从入门到精通" (zhichai.net/topic/177618752)
+ *              ch.2 "解剖麻雀（SwiGLU与Quant的单次Kernel融合）": sections
+ *              "内存的“连体双胞胎”：布局的艺术" (packed gate|up row),
+ *              "算子融合的“三重境界”" (sigmoid(x_L)*x_L, then * x_R, then the
+ *              top-k weight, then abs-max -> scale factor -> FP8), and
+ *              "守门员 Clamp" (clamp of the left value and its counter);
+ *              ch.5 "越过性能红线" (the unfused reference: swiglu_forward then
+ *              cast).
+ *  [Summary]   "TileKernels from Beginner to Master: DeepSeek's
+ *              TileLang-Powered GPU Kernel Guide" (zhichai.net/en/topic/
+ *              177618752), "Chapter 2: Anatomy of SwiGLU + Quant
+ *              Single-Kernel Fusion".
+ *  [Overview]  "TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式"
+ *              (zhichai.net/topic/177618740), "3. Quantization" table
+ *              (FP8 E4M3 per-token/per-block, FP4 E2M1, UE8M0 scales) and
+ *              the per-block vs per-token note under it.
+ *  [Essay]     "TileLang在DeepSeek-V4中的工业实战" (yunpan.plus/t/24864-1-1),
+ *              third point on precision and bitwise alignment (no fast-math,
+ *              IEEE operations, FMA fusion changes bits).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - sigma(g) is the correctly rounded fp32 value of 1/(1+e^-g); it is
+ *    evaluated here in binary128 and rounded once to fp32.
+ *  - a = RN(g*sigma), b = RN(a*u), y = RN(b*w): three fp32 products in the
+ *    order the Tutorial lists them, no fused multiply-add, y kept in fp32.
+ *  - clamp: gate g <- min(g, L) (counted when g > L), up u <- clamp(u,-L,L).
+ *  - fp32 scale s = RN(amax/fmt_max); codes from q = RN(y * inv) with
+ *    inv = min(RN(fmt_max/amax), FLT_MAX).
+ *  - UE8M0: smallest k with fmt_max*2^k >= amax (clamped to [-127,127]),
+ *    stored as the byte k+127; inv = 2^-k.
+ *  - casts round to nearest, ties to even, saturate at +-fmt_max and keep
+ *    the sign of zero; FP4 element 2i goes to the low nibble of byte i.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared oracle.c -lquadmath -lm
+ * (no -ffast-math, no FMA contraction: every fp32 operation is one IEEE
+ * operation rounded to nearest-even).
+ */
+#include <float.h>
+#include <math.h>
+#include <quadmath.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_FP8 8
+#define ORACLE_FP4 4
+#define ORACLE_SCALE_FP32 0
+#define ORACLE_SCALE_UE8M0 1
+
+/* bf16 is the upper half of an fp32: widening is exact. */
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* sigma(g) = 1 / (1 + e^-g), correctly rounded to fp32.
+ * Binary128 keeps about 112 bits, far more than the closest approach of any
+ * bf16 gate's sigmoid to an fp32 rounding midpoint, so the single final
+ * rounding is the correct one. */
+float oracle_sigmoid(float g)
+{
+    __float128 e = expq(-(__float128)g);
+    __float128 s = 1 / (1 + e);
+    return (float)s;
+}
+
+/* FP8 E4M3 (OCP "FN" variant: bias 7, no infinities, 0x7F/0xFF are NaN and
+ * never produced).  Normal codes: 2^(e-7) * (1 + m/8), e in 1..15;
+ * subnormals: 2^-6 * m/8.  Largest finite value 448.
+ * Round to nearest, ties to the even code, saturate, keep the sign. */
+uint8_t oracle_e4m3(float q)
+{
+    uint8_t sign = signbit(q) ? 0x80 : 0x00;
+    double a = fabs((double)q);
+    int code;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < 0x1p-6) {
+        /* subnormal range, step 2^-9; n == 8 is the smallest normal */
+        code = (int)nearbyint(a * 0x1p9);
+    } else {
+        int e;
+        frexp(a, &e);
+        e -= 1; /* a = 1.f * 2^e, e in [-6, 8] */
+        /* a / 2^(e-3) lies in [8, 16); 16 carries into the next binade */
+        code = ((e + 7) << 3) + (int)nearbyint(ldexp(a, 3 - e)) - 8;
+    }
+    if (code > 0x7E)
+        code = 0x7E;
+    return sign | (uint8_t)code;
+}
+
+/* FP4 E2M1: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Normal codes:
+ * 2^(e-1) * (1 + m/2), e in 1..3; subnormal: 0.5 * m.
+ * Round to nearest, ties to the even code, saturate, keep the sign. */
+uint8_t oracle_e2m1(float q)
+{
+    uint8_t sign = signbit(q) ? 0x8 : 0x0;
+    double a = fabs((double)q);
+    int code;
+    if (a >= 6.0)
+        return sign | 0x7;
+    if (a < 1.0) {
+        code = (int)nearbyint(a * 2.0); /* step 0.5; 2 is the value 1.0 */
+    } else {
+        int e;
+        frexp(a, &e);
+        e -= 1; /* e in {0, 1, 2} */
+        code = ((e + 1) << 1) + (int)nearbyint(ldexp(a, 1 - e)) - 2;
+    }
+    if (code > 7)
+        code = 7;
+    return sign | (uint8_t)code;
+}
+
+/* UE8M0: the smallest k in [-127, 127] with fmt_max * 2^k >= amax, found by
+ * counting up with exact double comparisons; returns k. */
+int oracle_ue8m0_exponent(float amax, float fmt_max)
+{
+    int k = -127;
+    while (k < 127 && ldexp((double)fmt_max, k) < (double)amax)
+        ++k;
+    return k;
+}
+
+static float fmt_max_of(int fmt) { return fmt == ORACLE_FP8 ? 448.0f : 6.0f; }
+
+/* The per-group tail: amax -> scale (+ inverse) -> codes.
+ * y[0..len) are one group's fp32 values; codes are written as one byte per
+ * element (the caller packs FP4 nibbles). */
+static void quantize_group(const float* y, int64_t len, int fmt, int scale_fmt,
+                           uint8_t* code_out, float* scale_f32, uint8_t* scale_u8)
+{
+    const float fmt_max = fmt_max_of(fmt);
+    float amax = 0.0f;
+    for (int64_t j = 0; j < len; ++j) {
+        float m = fabsf(y[j]);
+        if (m > amax)
+            amax = m;
+    }
+    float inv;
+    if (scale_fmt == ORACLE_SCALE_FP32) {
+        *scale_f32 = amax / fmt_max;
+        inv = fmt_max / amax; /* +inf when amax == 0 */
+        if (inv > FLT_MAX)
+            inv = FLT_MAX;
+    } else {
+        int k = oracle_ue8m0_exponent(amax, fmt_max);
+        *scale_u8 = (uint8_t)(k + 127);
+        inv = ldexpf(1.0f, -k);
+    }
+    for (int64_t j = 0; j < len; ++j) {
+        float q = y[j] * inv;
+        code_out[j] = fmt == ORACLE_FP8 ? oracle_e4m3(q) : oracle_e2m1(q);
+    }
+}
+
+static int check_args(int64_t n, int64_t hidden, int64_t group_size, int fmt, int scale_fmt)
+{
+    if (n < 0 || hidden <= 0 || group_size < 0)
+        return 1;
+    if (group_size != 0 && hidden % group_size != 0)
+        return 1;
+    if (fmt != ORACLE_FP8 && fmt != ORACLE_FP4)
+        return 1;
+    if (fmt == ORACLE_FP4 && hidden % 2 != 0)
+        return 1;
+    if (scale_fmt != ORACLE_SCALE_FP32 && scale_fmt != ORACLE_SCALE_UE8M0)
+        return 1;
+    return 0;
+}
+
+/* Stage 1 of the unfused reference (Tutorial ch.5 "越过性能红线"):
+ * y[r, j] = RN(RN(RN(g*sigma(g)) * u) * w[r]) with g = x[r, j],
+ * u = x[r, hidden + j] (Tutorial ch.2 layout section), after the optional
+ * clamp (Tutorial ch.2 "守门员 Clamp").  clamp_limit = +inf means no clamp.
+ * w == NULL means no weight.  *clamped_count (if given) is increased by the
+ * number of gate values strictly above the limit. */
+int oracle_swiglu_forward(const uint16_t* x, const float* w, int64_t n, int64_t hidden,
+                          float clamp_limit, float* y, int64_t* clamped_count)
+{
+    if (n < 0 || hidden <= 0)
+        return 1;
+    int64_t count = 0;
+    for (int64_t r = 0; r < n; ++r) {
+        const uint16_t* row = x + r * 2 * hidden;
+        const float wr = w ? w[r] : 1.0f;
+        for (int64_t j = 0; j < hidden; ++j) {
+            float g = bf16_to_float(row[j]);
+            float u = bf16_to_float(row[hidden + j]);
+            if (g > clamp_limit) {
+                g = clamp_limit;
+                ++count;
+            }
+            if (u > clamp_limit)
+                u = clamp_limit;
+            if (u < -clamp_limit)
+                u = -clamp_limit;
+            float sig = oracle_sigmoid(g);
+            float a = g * sig;
+            float b = a * u;
+            float yv = w ? b * wr : b;
+            y[r * hidden + j] = yv;
+        }
+    }
+    if (clamped_count)
+        *clamped_count += count;
+    return 0;
+}
+
+/* Stage 2 of the unfused reference: cast fp32 rows y[n, hidden] to codes and
+ * scales.  group_size 0 means one group per row (per-token).  FP8 codes are
+ * [n, hidden] bytes; FP4 codes are [n, hidden/2] bytes with element 2i in the
+ * low nibble.  Scales are [n, hidden/G] (fp32 or UE8M0 bytes), row-major. */
+int oracle_cast(const float* y, int64_t n, int64_t hidden, int64_t group_size, int fmt,
+                int scale_fmt, uint8_t* codes, void* scales)
+{
+    if (check_args(n, hidden, group_size, fmt, scale_fmt))
+        return 1;
+    const int64_t G = group_size ? group_size : hidden;
+    const int64_t groups = hidden / G;
+    uint8_t* tmp = (uint8_t*)malloc((size_t)hidden);
+    if (!tmp)
+        return 2;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t k = 0; k < groups; ++k) {
+            float* sf = (float*)scales + r * groups + k;
+            uint8_t* su = (uint8_t*)scales + r * groups + k;
+            quantize_group(y + r * hidden + k * G, G, fmt, scale_fmt, tmp + k * G, sf, su);
+        }
+        if (fmt == ORACLE_FP8) {
+            memcpy(codes + r * hidden, tmp, (size_t)hidden);
+        } else {
+            for (int64_t i = 0; i < hidden / 2; ++i)
+                codes[r * (hidden / 2) + i] = (uint8_t)(tmp[2 * i] | (tmp[2 * i + 1] << 4));
+        }
+    }
+    free(tmp);
+    return 0;
+}
+
+/* The fused form (Tutorial ch.2; Summary ch.2): one row at a time, the row's
+ * fp32 values never leave this loop.  Same arguments as the two stages
+ * combined. */
+int oracle_swiglu_cast(const uint16_t* x, const float* w, int64_t n, int64_t hidden,
+                       int64_t group_size, float clamp_limit, int fmt, int scale_fmt,
+                       uint8_t* codes, void* scales, int64_t* clamped_count)
+{
+    if (check_args(n, hidden, group_size, fmt, scale_fmt))
+        return 1;
+    float* row_y = (float*)malloc((size_t)hidden * sizeof(float));
+    if (!row_y)
+        return 2;
+    const int64_t groups = hidden / (group_size ? group_size : hidden);
+    const int64_t code_bytes = fmt == ORACLE_FP8 ? hidden : hidden / 2;
+    const size_t scale_bytes = scale_fmt == ORACLE_SCALE_FP32 ? sizeof(float) : 1;
+    for (int64_t r = 0; r < n; ++r) {
+        const float* wr = w ? w + r : NULL;
+        int rc = oracle_swiglu_forward(x + r * 2 * hidden, wr, 1, hidden, clamp_limit, row_y,
+                                       clamped_count);
+        if (rc == 0)
+            rc = oracle_cast(row_y, 1, hidden, group_size, fmt, scale_fmt, codes + r * code_bytes,
+                             (uint8_t*)scales + (size_t)(r * groups) * scale_bytes);
+        if (rc) {
+            free(row_y);
+            return rc;
+        }
+    }
+    free(row_y);
+    return 0;
+}
+
+/* Element-wise cast of fp32 values to codes (one byte per value), for codec
+ * sweeps: fmt 8 -> oracle_e4m3, fmt 4 -> oracle_e2m1. */
+int oracle_encode(int fmt, const float* q, int64_t n, uint8_t* out)
+{
+    if (fmt != ORACLE_FP8 && fmt != ORACLE_FP4)
+        return 1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fmt == ORACLE_FP8 ? oracle_e4m3(q[i]) : oracle_e2m1(q[i]);
+    return 0;
+}

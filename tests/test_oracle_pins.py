@@ -1,0 +1,293 @@
+"""Pins of the oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-worked
+rows (tests/golden), an exact-rational brute-force evaluator (tests/exact.py),
+a library routine (torch's float8_e4m3fn cast), 60-digit decimal arithmetic,
+closed forms and invariants.
+"""
+import json
+import math
+import os
+from fractions import Fraction as Fr
+
+import numpy as np
+import pytest
+
+import exact as E
+import oracle
+from moe_activation_bit_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_rows.json")
+
+
+def _row_x(gate, up):
+    return np.array([[E.float_to_bf16(v) for v in gate] + [E.float_to_bf16(v) for v in up]], dtype=np.uint16)
+
+
+def _hand_rows():
+    return json.load(open(GOLDEN))["rows"]
+
+
+@pytest.mark.parametrize("row", _hand_rows(), ids=lambda r: r["name"])
+def test_hand_rows_oracle(row):
+    x = _row_x(row["gate"], row["up"])
+    w = np.array([row["weight"]], dtype=np.float32)
+    codes, scales, cnt = oracle.swiglu_cast(x, w, row["group"], row["clamp"], row["fmt"], row["scale_fmt"])
+    assert codes[0].tolist() == row["codes"]
+    if row["scale_fmt"] == 0:
+        assert scales[0].tolist() == row["scales_f32"]
+    else:
+        assert scales[0].tolist() == row["scales_u8"]
+    assert cnt == row["count"]
+    if "y" in row:
+        y, cnt2 = oracle.swiglu_forward(x, w, row["clamp"])
+        assert [float(v) for v in y[0]] == row["y"]
+        assert [math.copysign(1, v) for v in y[0]] == [math.copysign(1, v) for v in row["y"]]
+        assert cnt2 == row["count"]
+
+
+@pytest.mark.parametrize("row", _hand_rows(), ids=lambda r: r["name"])
+def test_hand_rows_exact_evaluator(row):
+    gh = [E.float_to_bf16(v) for v in row["gate"]]
+    uh = [E.float_to_bf16(v) for v in row["up"]]
+    y, cnt = E.swiglu_row(gh, uh, row["weight"], row["clamp"])
+    codes, scales = E.cast_row(y, row["group"], row["fmt"], row["scale_fmt"])
+    if row["fmt"] == 4:
+        codes = E.pack_fp4(codes)
+    assert codes == row["codes"]
+    assert scales == (row["scales_f32"] if row["scale_fmt"] == 0 else row["scales_u8"])
+    assert cnt == row["count"]
+
+
+def test_sigmoid_exhaustive_bf16():
+    """sigma(g) for every finite bf16 g equals the correctly rounded fp32 of 1/(1+e^-g)."""
+    h = np.arange(65536, dtype=np.uint32)
+    g = (h << 16).view(np.float32)
+    bad = []
+    for v in g[np.isfinite(g)]:
+        v = float(v)
+        got = oracle.sigmoid(v)
+        want = E.sigmoid_f32(v)
+        if np.float32(got).view(np.uint32) != np.float32(want).view(np.uint32):
+            bad.append((v, got, want))
+    assert not bad, bad[:10]
+
+
+def test_sigmoid_random_fp32():
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([rng.uniform(-30, 30, 600), rng.standard_normal(300) * 1e-4,
+                           [10.0, 2.5, 7.75, 1e-30, -1e-30, 17.3, 17.4, -103.9, -104.1]]).astype(np.float32)
+    for v in vals:
+        assert oracle.sigmoid(float(v)) == E.sigmoid_f32(float(v)), float(v)
+
+
+def _f32_sweep(lo_bits, hi_bits, stride, offset=0):
+    return np.arange(lo_bits + offset, hi_bits, stride, dtype=np.uint32).view(np.float32)
+
+
+def test_e4m3_matches_torch_cast_sweep():
+    """Library routine: torch's float8_e4m3fn cast is round-to-nearest-even and
+    agrees with a saturating cast wherever no saturation happens (|q| <= 448)."""
+    torch = pytest.importorskip("torch")
+    hi = np.float32(448.0).view(np.uint32)
+    for off in (0, 5):
+        q = _f32_sweep(0, int(hi) + 1, 13, off)
+        for chunk in np.array_split(q, 8):
+            for sgn in (1.0, -1.0):
+                c = (chunk * np.float32(sgn)).astype(np.float32)
+                ref = torch.from_numpy(c).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                got = oracle.encode(c, 8)
+                mism = np.nonzero(ref != got)[0]
+                assert mism.size == 0, [(float(c[i]), got[i], ref[i]) for i in mism[:5]]
+
+
+def test_e4m3_saturates():
+    q = np.array([448.0, 448.00003, 463.99997, 464.0, 464.00003, 480.0, 1e6, 3.4e38], dtype=np.float32)
+    for s in (1, -1):
+        got = oracle.encode(q * s, 8)
+        assert (got == (0x7E if s > 0 else 0xFE)).all(), got
+
+
+def _neighbours(v, k):
+    b = int(np.float32(v).view(np.uint32))
+    return [np.uint32(b + d).view(np.float32) for d in range(-k, k + 1) if 0 <= b + d]
+
+
+def test_e4m3_brute_force_at_every_midpoint():
+    vals = E.E4M3
+    pts = []
+    for c in range(126):
+        mid = (vals[c] + vals[c + 1]) / 2
+        pts += _neighbours(np.float32(float(mid)), 3)
+        pts += _neighbours(np.float32(float(vals[c])), 1)
+    pts += [np.float32(v) for v in (0.0, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -149, 440.0, 447.9, 456.0)]
+    for p in pts:
+        for s in (1.0, -1.0):
+            q = float(np.float32(p) * np.float32(s))
+            assert oracle.e4m3(q) == E.nearest_code(q, E.E4M3, 0x80), q
+    assert oracle.e4m3(-0.0) == 0x80 and oracle.e4m3(0.0) == 0x00
+
+
+def test_e2m1_brute_force_sweep():
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    hi = int(np.float32(8.0).view(np.uint32))
+    q = _f32_sweep(0, hi, 11)
+    for chunk in np.array_split(q, 24):
+        a = chunk.astype(np.float64)
+        d = np.abs(a[:, None] - vals[None, :])
+        first = d.argmin(1)
+        last = 7 - d[:, ::-1].argmin(1)
+        want = np.where(first % 2 == 0, first, last).astype(np.uint8)
+        assert np.array_equal(oracle.encode(chunk, 4), want)
+        assert np.array_equal(oracle.encode(-chunk, 4), want | 0x8)
+
+
+def test_e2m1_ties():
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6, 7.0: 7}
+    for v, c in ties.items():
+        assert oracle.e2m1(v) == c and oracle.e2m1(-v) == c | 8
+
+
+def _ue8m0_points(fmt_max):
+    pts = [0.0, 2.0 ** -149, 2.0 ** -126, 1e-38, 3.4e38, float(np.finfo(np.float32).max)]
+    for k in range(-127, 121):
+        v = np.float32(fmt_max * 2.0 ** k)
+        if np.isfinite(v) and v > 0:
+            pts += [float(x) for x in _neighbours(v, 1)]
+    rng = np.random.default_rng(3)
+    pts += list((2.0 ** rng.uniform(-140, 127, 400)).astype(np.float32).astype(float))
+    return [p for p in pts if np.isfinite(np.float32(p))]
+
+
+@pytest.mark.parametrize("fmt", [8, 4])
+def test_ue8m0_closed_form(fmt):
+    fmt_max = 448.0 if fmt == 8 else 6.0
+    for amax in _ue8m0_points(fmt_max):
+        amax = float(np.float32(amax))
+        k = oracle.ue8m0_exponent(amax, fmt)
+        assert Fr(fmt_max) * Fr(2) ** k >= Fr(amax), (amax, k)
+        if k > -127:
+            assert Fr(fmt_max) * Fr(2) ** (k - 1) < Fr(amax), (amax, k)
+        assert k == E.ue8m0_k(amax, fmt_max)
+
+
+CASES = [  # (hidden, group, fmt, scale_fmt, clamp)
+    (16, 0, 8, 0, None), (16, 8, 8, 1, None), (16, 0, 4, 1, 2.5), (16, 8, 4, 0, None),
+    (24, 8, 8, 0, 1.0), (8, 0, 8, 1, 0.75), (16, 4, 4, 1, None), (32, 16, 8, 0, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=str)
+def test_oracle_matches_exact_evaluator_on_tiny_rows(case):
+    hidden, group, fmt, sfmt, clamp = case
+    base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    rng = np.random.default_rng(hidden * 31 + group)
+    rows = 6
+    x = np.empty((rows, 2 * hidden), dtype=np.uint16)
+    for r in range(rows):
+        full = wl.make_x(base, r, rows=[r])[0]
+        x[r] = full[: 2 * hidden]
+    # exact ties and specials: a gate exactly at the limit, signed zeros, big values
+    x[0, 0] = E.float_to_bf16(clamp if clamp is not None else 1.0)
+    x[1, 1] = 0x8000
+    x[1, hidden] = 0x8000
+    x[2, 2] = E.float_to_bf16(-96.0)
+    w = rng.uniform(0, 1, rows).astype(np.float32)
+    w[3] = 0.0
+    w[4] = 1e-20
+    codes, scales, cnt = oracle.swiglu_cast(x, w, group, clamp, fmt, sfmt)
+    y, cnt_y = oracle.swiglu_forward(x, w, clamp)
+    total = 0
+    for r in range(rows):
+        gate, up = x[r, :hidden].tolist(), x[r, hidden:].tolist()
+        ey, ec = E.swiglu_row(gate, up, float(w[r]), clamp)
+        total += ec
+        assert [float(v) for v in y[r]] == ey
+        assert np.array_equal(np.signbit(y[r]), np.signbit(np.array(ey, dtype=np.float32)))
+        ecodes, escales = E.cast_row(ey, group, fmt, sfmt)
+        if fmt == 4:
+            ecodes = E.pack_fp4(ecodes)
+        assert codes[r].tolist() == ecodes, r
+        assert scales[r].tolist() == escales, r
+    assert cnt == total == cnt_y
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_fused_equals_composition(name):
+    w = wl.WORKLOADS[name]
+    rows = 24
+    x = wl.make_x(w, 1, rows=range(rows))
+    wt = wl.make_w(w, 1)[:rows] if wl.num_rows(w, 1) >= rows else np.resize(wl.make_w(w, 1), rows)
+    fmt = 8 if w.fmt == "fp8" else 4
+    sfmt = 0 if w.scale_fmt == "fp32" else 1
+    codes, scales, cnt = oracle.swiglu_cast(x, wt, w.group_size, w.clamp_limit, fmt, sfmt)
+    y, cnt_y = oracle.swiglu_forward(x, wt, w.clamp_limit)
+    c2, s2 = oracle.cast(y, w.group_size, fmt, sfmt)
+    assert np.array_equal(codes, c2) and np.array_equal(scales.view(np.uint8), s2.view(np.uint8))
+    assert cnt == cnt_y
+    # batch invariance: a slice computed alone equals the same rows of the batch
+    c3, s3, _ = oracle.swiglu_cast(x[5:11], wt[5:11], w.group_size, w.clamp_limit, fmt, sfmt)
+    assert np.array_equal(c3, codes[5:11]) and np.array_equal(s3.view(np.uint8), scales[5:11].view(np.uint8))
+
+
+def _spacing(v: Fr, fmt: int) -> Fr:
+    a = abs(v)
+    if fmt == 8:
+        if a < Fr(2) ** -6:
+            return Fr(2) ** -9
+        e = math.floor(math.log2(a))
+        return Fr(2) ** (e - 3)
+    if a < 1:
+        return Fr(1, 2)
+    e = math.floor(math.log2(a))
+    return Fr(2) ** (e - 1)
+
+
+@pytest.mark.parametrize("fmt,sfmt,group", [(8, 0, 0), (8, 1, 128), (4, 1, 32), (4, 0, 0), (8, 0, 128)])
+def test_invariants(fmt, sfmt, group):
+    w_ = wl.WORKLOADS["fp8_g128_ue8m0_n32768_h2048"]
+    rows, hidden = 6, w_.hidden
+    x = wl.make_x(w_, 2, rows=range(rows))
+    wt = wl.make_w(w_, 2)[:rows].copy()
+    wt[0] = 0.0
+    codes, scales, _ = oracle.swiglu_cast(x, wt, group, None, fmt, sfmt)
+    y, _ = oracle.swiglu_forward(x, wt, None)
+    fmt_max = 448.0 if fmt == 8 else 6.0
+    G = group or hidden
+    # zero routing weight: every code is a zero of the value's sign
+    if fmt == 8:
+        assert set(codes[0].tolist()) <= {0x00, 0x80}
+        per_elem = codes
+    else:
+        assert set((codes[0] & 0x7).tolist()) == {0}
+        per_elem = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(rows, hidden)
+    assert (scales[0] == 0).all() if sfmt == 0 else (scales[0] == 0).all()
+    for r in range(1, rows):
+        for k in range(hidden // G):
+            grp = y[r, k * G:(k + 1) * G]
+            amax = float(np.abs(grp).max())
+            if sfmt == 0:
+                s = float(scales[r, k])
+                assert s == E.round_f32(Fr(amax) / Fr(fmt_max))  # scale = RN(amax / fmt_max)
+                s_fr = Fr(s)
+            else:
+                kk = int(scales[r, k]) - 127
+                assert Fr(fmt_max) * Fr(2) ** kk >= Fr(amax) > Fr(fmt_max) * Fr(2) ** (kk - 1)  # minimal
+                s_fr = Fr(2) ** kk
+            for j in range(0, G, 7):  # dequantisation error within half a step (+ fp32 slack)
+                v = E.decode(int(per_elem[r, k * G + j]), fmt)
+                yv = Fr(float(grp[j]))
+                assert abs(v * s_fr - yv) <= _spacing(v, fmt) * s_fr / 2 + abs(yv) * Fr(1, 2 ** 21)
+
+
+def test_clamp_count_and_infinite_limit():
+    w_ = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    rows = 16
+    x = wl.make_x(w_, 0, rows=range(rows))
+    wt = wl.make_w(w_, 0)[:rows]
+    _, cnt = oracle.swiglu_forward(x, wt, 10.0)
+    gate = x[:, : w_.hidden].astype(np.uint32) << 16
+    assert cnt == int((gate.view(np.float32) > 10.0).sum()) > 0
+    a = oracle.swiglu_cast(x, wt, 0, math.inf, 8, 0)
+    b = oracle.swiglu_cast(x, wt, 0, None, 8, 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] == 0
