@@ -1,0 +1,144 @@
+/*
+ * tk.h -- C ABI of the fused SwiGLU + MoE top-k weight + FP8/FP4 cast for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one launch, one HBM read of the input, one HBM write of the
+ * output) follows DeepSeek's TileKernels kernel
+ * swiglu_forward_and_per_token_cast as described in
+ *   "【DeepSeek】TileKernels从入门到精通" (zhichai.net/topic/177618752),
+ *   ch.2 "解剖麻雀（SwiGLU与Quant的单次Kernel融合）":
+ *     - "内存的“连体双胞胎”：布局的艺术": the input is one packed bf16 tensor
+ *       [num_expanded_tokens, 2*hidden]; gate = left half, up = right half
+ *       at column offset hidden;
+ *     - "算子融合的“三重境界”": sigmoid(gate)*gate, times up, times the
+ *       row's top-k routing weight, then the abs-max of the result gives the
+ *       scale factor and the values are cast to FP8 in registers;
+ *     - "守门员 Clamp": optional clamp of the gate against a limit, with an
+ *       atomically accumulated count of clamped values;
+ *   and "TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式"
+ *   (zhichai.net/topic/177618740), "3. Quantization": FP8 E4M3 per-token or
+ *   per-block, FP4 E2M1, and UE8M0 (power-of-two) scale factors.
+ *
+ * Per row r (j < hidden, g = x[r, j], u = x[r, hidden + j], both bf16):
+ *   clamp (if clamp_limit is finite): count g > L; g = min(g, L);
+ *                                     u = min(max(u, -L), L)
+ *   a = RN(g * sigma(g))   sigma(g) = 1/(1+e^-g), correctly rounded to fp32
+ *   b = RN(a * u);  y = RN(b * topk_weight[r])   (fp32, no fused multiply-add)
+ *   per group of G consecutive columns (G = hidden when group_size == 0):
+ *     amax = max |y|
+ *     TK_SCALE_FP32 : scale = RN(amax / fmt_max), inv = min(RN(fmt_max/amax), FLT_MAX)
+ *     TK_SCALE_UE8M0: k = smallest integer with fmt_max * 2^k >= amax
+ *                     (at least -127); scale byte = k + 127, inv = 2^-k
+ *     code = cast(RN(y * inv)), round to nearest even, saturating
+ *   fmt_max = 448 (FP8 E4M3, OCP "FN" encoding) or 6 (FP4 E2M1).
+ *   Dequantisation is code * scale (scale = 2^(byte-127) for UE8M0).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is DEVICE memory owned by the caller.  The library
+ *    allocates nothing per call; it keeps per device a CU count and a
+ *    32 KiB sigmoid table in static device memory, set up by tk_init or by
+ *    the first call on that device.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return after the launch is enqueued.
+ *  - Outputs must not overlap inputs.
+ *  - n == 0 returns TK_OK and launches nothing.
+ *  - Errors are returned, never thrown; on any error nothing is launched
+ *    except for TK_ERR_HIP, which reports a failed launch or device query.
+ */
+#ifndef TK_H_
+#define TK_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TK_SCALE_FP32 = 0,  /* one fp32 per group */
+    TK_SCALE_UE8M0 = 1  /* one byte per group: biased exponent of a power of two */
+} tk_scale_fmt;
+
+typedef enum {
+    TK_OK = 0,
+    TK_ERR_INVALID_ARG = 1, /* a documented precondition does not hold */
+    TK_ERR_UNSUPPORTED = 2, /* valid request outside the shapes the kernels cover */
+    TK_ERR_HIP = 3          /* HIP runtime error (launch, device query) */
+} tk_status;
+
+/*
+ * tk_init: one-time set-up of `device` (its CU count and the sigmoid table).
+ * The first tk_swiglu_cast_* call on a device does this itself and blocks
+ * until it is finished; call tk_init beforehand to take that cost out of the
+ * first call (required before capturing calls into a HIP graph).
+ * Thread-safe.  The caller's current device is left unchanged.
+ * Errors: TK_ERR_INVALID_ARG for a device index out of range, TK_ERR_HIP.
+ */
+tk_status tk_init(int device);
+
+/*
+ * tk_swiglu_cast_fp8: the fused step with FP8 E4M3 codes.
+ *
+ *  x             bf16 [n, 2*hidden], row-major; columns [0, hidden) are the
+ *                gate, [hidden, 2*hidden) the up projection.  16-byte aligned.
+ *  topk_weight   fp32 [n], the routing weight of each expanded row, 4-byte
+ *                aligned; NULL means weight 1 (the last product is skipped).
+ *  n             rows (num_expanded_tokens), 0 <= n < 2^31.
+ *  hidden        columns per half; > 0 and a multiple of 8.
+ *  group_size    0 = one scale per row (per-token); otherwise the width of a
+ *                column group with its own scale: a multiple of 8 dividing
+ *                hidden.
+ *  clamp_limit   L > 0; +INFINITY disables the clamp (the count is then 0).
+ *  scale_fmt     TK_SCALE_FP32 or TK_SCALE_UE8M0.
+ *  codes         uint8 [n, hidden], E4M3 codes, 8-byte aligned.
+ *  scales        [n, hidden/G] row-major (G = hidden when group_size == 0):
+ *                fp32 (4-byte aligned) or uint8 UE8M0 bytes.
+ *  clamped_count int64 on the device, or NULL.  The number of gate values
+ *                strictly above L is ADDED to it (the caller zeroes it).
+ *  stream        hipStream_t to launch on.
+ *
+ * Returns TK_ERR_INVALID_ARG when: n < 0 or n >= 2^31; hidden <= 0 or not a
+ * multiple of 8; group_size < 0, not a multiple of 8 or not dividing hidden;
+ * clamp_limit is NaN or <= 0; scale_fmt is unknown; n > 0 and x, codes or
+ * scales is NULL; a pointer breaks its alignment; an output overlaps an input.
+ * Returns TK_ERR_UNSUPPORTED when the group (in units of 8 columns) is not a
+ * power of two up to 64 and not a multiple of 64, or when one group spans more
+ * than 8192 columns.
+ */
+tk_status tk_swiglu_cast_fp8(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                             int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt,
+                             void* codes, void* scales, int64_t* clamped_count, void* stream);
+
+/*
+ * tk_swiglu_cast_fp4: the same step with FP4 E2M1 codes (fmt_max = 6).
+ * codes is uint8 [n, hidden/2], 4-byte aligned: element 2i of a row is the
+ * low nibble of byte i, element 2i+1 the high nibble; each nibble is
+ * sign(1) | exponent(2) | mantissa(1).  Everything else as tk_swiglu_cast_fp8.
+ */
+tk_status tk_swiglu_cast_fp4(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                             int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt,
+                             void* codes, void* scales, int64_t* clamped_count, void* stream);
+
+/*
+ * tk_swiglu_forward: the first stage of the same operation on its own, the
+ * "swiglu_forward" of the unfused reference in "【DeepSeek】TileKernels从入门到
+ * 精通" ch.5 "越过性能红线" (swiglu_forward, then cast): writes
+ * y = RN(RN(RN(g*sigma(g))*u)*topk_weight) in fp32 with the same clamp and
+ * counter, and no cast.  Exposes every bit of the fused kernel's activation
+ * (same device code) and is the first kernel of the unfused two-pass path.
+ *
+ *  y  fp32 [n, hidden], row-major, 16-byte aligned, caller-owned device memory.
+ *  Other arguments, conventions and errors as tk_swiglu_cast_fp8 (there is no
+ *  group, format or scale, so TK_ERR_UNSUPPORTED never occurs).
+ */
+tk_status tk_swiglu_forward(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                            float clamp_limit, float* y, int64_t* clamped_count, void* stream);
+
+/* tk_status_str: a static, human-readable name for a status code. */
+const char* tk_status_str(tk_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TK_H_ */

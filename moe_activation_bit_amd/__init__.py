@@ -1,0 +1,123 @@
+"""Python binding of the MI355X fused SwiGLU + top-k weight + FP8/FP4 cast.
+
+Argument marshalling only: every function here forwards to the C ABI in
+``include/tk.h`` (library ``libtk.so`` built from ``csrc/tk_swiglu_cast.hip``)
+under the same name.  All arithmetic runs in the library's HIP kernels; there
+is no CPU fallback, and importing a function whose library is missing raises.
+
+Tensor arguments may be torch tensors (their ``data_ptr()`` is passed) or raw
+device addresses as ints; ``None`` is a null pointer.  ``stream`` defaults to
+torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+from typing import Any, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtk.so")
+
+__all__ = [
+    "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "LIB_PATH", "load_library",
+    "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_status_str",
+]
+
+TK_SCALE_FP32 = 0
+TK_SCALE_UE8M0 = 1
+
+
+class TkStatus(enum.IntEnum):
+    TK_OK = 0
+    TK_ERR_INVALID_ARG = 1
+    TK_ERR_UNSUPPORTED = 2
+    TK_ERR_HIP = 3
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+# the exported symbols and their C signatures, as declared in include/tk.h
+_CAST_ARGS = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+              ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+              ctypes.c_void_p]
+SIGNATURES = {
+    "tk_init": (ctypes.c_int, [ctypes.c_int]),
+    "tk_swiglu_cast_fp8": (ctypes.c_int, _CAST_ARGS),
+    "tk_swiglu_cast_fp4": (ctypes.c_int, _CAST_ARGS),
+    "tk_swiglu_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libtk.so (fails loudly when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first (__graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Any) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream: Any) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def tk_init(device: int) -> TkStatus:
+    return TkStatus(load_library().tk_init(int(device)))
+
+
+def _cast(fn_name: str, x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
+          clamped_count, stream) -> TkStatus:
+    lib = load_library()
+    fn = getattr(lib, fn_name)
+    rc = fn(_ptr(x), _ptr(topk_weight), int(n), int(hidden), int(group_size), float(clamp_limit),
+            int(scale_fmt), _ptr(codes), _ptr(scales), _ptr(clamped_count), _stream(stream))
+    return TkStatus(rc)
+
+
+def tk_swiglu_cast_fp8(x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
+                       clamped_count=None, stream=None) -> TkStatus:
+    """See tk_swiglu_cast_fp8 in include/tk.h."""
+    return _cast("tk_swiglu_cast_fp8", x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt,
+                 codes, scales, clamped_count, stream)
+
+
+def tk_swiglu_cast_fp4(x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
+                       clamped_count=None, stream=None) -> TkStatus:
+    """See tk_swiglu_cast_fp4 in include/tk.h."""
+    return _cast("tk_swiglu_cast_fp4", x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt,
+                 codes, scales, clamped_count, stream)
+
+
+def tk_swiglu_forward(x, topk_weight, n, hidden, clamp_limit, y, clamped_count=None,
+                      stream=None) -> TkStatus:
+    """See tk_swiglu_forward in include/tk.h."""
+    rc = load_library().tk_swiglu_forward(_ptr(x), _ptr(topk_weight), int(n), int(hidden), float(clamp_limit),
+                                          _ptr(y), _ptr(clamped_count), _stream(stream))
+    return TkStatus(rc)
+
+
+def tk_status_str(status: int) -> str:
+    return load_library().tk_status_str(int(status)).decode()

@@ -1,0 +1,764 @@
+// tk_swiglu_cast.hip -- fused SwiGLU + MoE top-k weight + FP8/FP4 cast for
+// MI355X (gfx950, CDNA4), behind the C ABI declared in include/tk.h.
+//
+// The operation is DeepSeek TileKernels' swiglu_forward_and_per_token_cast as
+// described in "【DeepSeek】TileKernels从入门到精通" (zhichai.net/topic/
+// 177618752) ch.2 (packed gate|up row; sigmoid(x_L)*x_L*x_R*topk_weight;
+// abs-max -> scale -> cast; clamp with an atomic counter; persistent grid),
+// with the formats of "TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式"
+// (zhichai.net/topic/177618740) "3. Quantization" (E4M3 / E2M1, per-token or
+// per-block, UE8M0 scales).
+//
+// gfx950 design (no code from the pages' TileLang/CUDA kernel):
+//  - A wavefront of 64 lanes owns one "unit": up to SPU "steps" of one row,
+//    where a step is 512 columns: lane l reads 16 bytes (8 bf16) of the gate
+//    half and 16 bytes of the up half at column 8*(64*step + l).  Loads are
+//    128-bit and fully coalesced (1 KiB per wave instruction).
+//  - sigma(g) comes from a 32 KiB table in LDS indexed by the bf16 bits of g
+//    (the gate is bf16, so sigma has only 65536 possible inputs; outside the
+//    4096 tabulated magnitudes it is constant in fp32).  The table holds the
+//    correctly rounded fp32 sigma and is computed on the GPU once per device.
+//  - Group abs-max: lane-local max over 8 values, then DPP butterflies inside
+//    the 2^j lanes of a group (quad_perm, row_half_mirror, row_mirror), or a
+//    whole-wave reduction for per-token / 512k-column groups.
+//  - Casts use the gfx950 converters: v_cvt_pk_fp8_f32 (OCP E4M3, round to
+//    nearest even) and v_cvt_scalef32_pk_fp4_f32 with scale 1 (E2M1, round to
+//    nearest even, saturating).  Quantised values never exceed fmt_max by
+//    more than one fp32 ulp, so the E4M3 converter's lack of saturation above
+//    464 is never reached.
+//  - A persistent grid sized from the CU count; every wave strides over units.
+//  - The clamp counter is reduced per wave with ballots and added to the
+//    int64 counter with one vector atomic per wave.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "tk.h"
+
+namespace {
+
+constexpr int kWaveSize = 64;
+constexpr int kSlotCols = 8;                     // columns per lane per step (16 B of bf16)
+constexpr int kStepCols = kWaveSize * kSlotCols; // 512
+constexpr int kMaxStepsPerUnit = 16;             // largest row-reduced group: 8192 columns
+
+// Sigmoid table: magnitudes m of bf16 bit patterns in [kLutFirst, kLutFirst+kLutSize),
+// one (sigma(+g), sigma(-g)) pair per magnitude.  Below 2^-25 sigma rounds to
+// 0.5 and at 127.5 and beyond it rounds to 1 (positive) or 0 (negative) in fp32,
+// so clamping the magnitude into the table range is exact.
+constexpr uint32_t kLutFirst = 0x3300u; // bf16 2^-25
+constexpr uint32_t kLutLast = 0x42FFu;  // bf16 127.5
+constexpr int kLutSize = 4096;
+static_assert(kLutLast - kLutFirst + 1 == kLutSize, "table span");
+
+__device__ float2 g_sigma_lut[kLutSize];
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// ---------------------------------------------------------------------------
+// Correctly rounded fp32 sigmoid for table set-up and for the clamp limit.
+// |g| < 2^-12: Taylor series 1/2 + g/4 - g^3/48 + g^5/480 (next term below
+//   2^-96), summed as a double-double with Knuth's TwoSum; the double-double
+//   is rounded to fp32 once, the low word deciding exact fp64 midpoints.
+// otherwise: 1/(1+exp(-g)) in fp64.  Its error (a few fp64 ulps) is far below
+//   the distance of any bf16 gate's sigmoid from an fp32 rounding midpoint
+//   (at least 5.8e-5 fp32 ulps for |g| >= 2^-12); for other fp32 inputs it is
+//   correct unless sigma lies within ~2^-50 of a midpoint.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e)
+{
+    s = a + b;
+    const double bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+__device__ float round_dd_to_float(double hi, double lo)
+{
+    const float f = (float)hi;
+    const double df = (double)f;
+    if (df == hi || lo == 0.0)
+        return f;
+    const float f2 = nextafterf(f, hi > df ? INFINITY : -INFINITY);
+    const double mid = 0.5 * (df + (double)f2); // exact
+    if (mid != hi)
+        return f; // hi is not a tie, so hi + lo rounds like hi
+    // hi sits exactly on the midpoint between f and f2: lo decides.
+    return ((lo > 0.0) == (hi > df)) ? f2 : f;
+}
+
+__device__ float sigmoid_rn(float gf)
+{
+    const double g = (double)gf;
+    if (fabs(g) < 0x1p-12) {
+        if (fabs(g) < 0x1p-40)
+            return 0.5f; // |g/4| is far below half an ulp of 0.5
+        double s, e;
+        two_sum(0.5, 0.25 * g, s, e);
+        const double g2 = g * g;
+        const double c = g * g2 * (-1.0 / 48.0 + g2 * (1.0 / 480.0));
+        double hi, lo;
+        two_sum(s, e + c, hi, lo);
+        return round_dd_to_float(hi, lo);
+    }
+    return (float)(1.0 / (1.0 + exp(-g)));
+}
+
+__global__ void sigma_lut_init_kernel()
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= kLutSize)
+        return;
+    const float g = as_float((kLutFirst + (uint32_t)i) << 16);
+    g_sigma_lut[i] = make_float2(sigmoid_rn(g), sigmoid_rn(-g));
+}
+
+// ---------------------------------------------------------------------------
+// Kernel
+// ---------------------------------------------------------------------------
+struct Params {
+    const uint4* x;         // [n][2*slots] 16-byte lane slots (gate slots, then up slots)
+    const float* w;         // [n] or null
+    uint8_t* codes;         // fp8: [n][hidden]; fp4: [n][hidden/2]
+    void* scales;           // [n][groups_row], fp32 or uint8
+    unsigned long long* count;
+    uint32_t slots;         // hidden / 8
+    uint32_t steps_row;     // ceil(slots / 64)
+    uint32_t upr;           // units per row
+    uint32_t spu;           // steps per unit (<= SPU)
+    uint32_t units;         // n * upr
+    uint32_t gl_log2;       // per-block: lanes per group = 1 << gl_log2
+    uint32_t groups_row;    // scales per row
+    float clamp;            // L (clamp variants)
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, t));
+}
+
+// max over the 2^gl_log2 consecutive lanes of each group (all lanes active)
+__device__ __forceinline__ float group_max(float v, uint32_t gl_log2)
+{
+    if (gl_log2 >= 1) v = dpp_max<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    if (gl_log2 >= 2) v = dpp_max<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if (gl_log2 >= 3) v = dpp_max<0x141>(v); // row_half_mirror: quads of 8 lanes
+    if (gl_log2 >= 4) v = dpp_max<0x140>(v); // row_mirror: halves of 16 lanes
+    if (gl_log2 >= 5) v = fmaxf(v, __shfl_xor(v, 16));
+    if (gl_log2 >= 6) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = dpp_max<0xB1>(v);
+    v = dpp_max<0x4E>(v);
+    v = dpp_max<0x141>(v);
+    v = dpp_max<0x140>(v);
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// sigma(g) for a gate whose bf16 bits sit in bits [pos, pos+16) of `word`;
+// gbits is the fp32 bit pattern of the same gate (its sign selects the entry).
+template <int POS>
+__device__ __forceinline__ float lut_sigma(const float2* lut, uint32_t word, uint32_t gbits)
+{
+    const uint32_t m = __builtin_amdgcn_ubfe(word, POS, 15);                 // |g| as bf16 bits
+    const uint32_t c = min(max(m, kLutFirst), kLutLast) - kLutFirst;         // v_med3_u32
+    const float2 pr = lut[c];
+    return ((int32_t)gbits < 0) ? pr.y : pr.x;
+}
+
+// One element: gate and up are the bf16 halves at bit POS of `gword` / `uword`.
+// a = RN(g * sigma(g)) (or the clamped gate's activation), b = RN(a * u),
+// y = RN(b * w); three fp32 products, never fused.
+template <int POS, bool CLAMP>
+__device__ __forceinline__ float swiglu_elem(const float2* lut, uint32_t gword, uint32_t uword, float w,
+                                             float limit, float a_limit, unsigned long long& clamped)
+{
+    const uint32_t gbits = POS ? (gword & 0xFFFF0000u) : (gword << 16);
+    float u = as_float(POS ? (uword & 0xFFFF0000u) : (uword << 16));
+    const float g = as_float(gbits);
+    float a = g * lut_sigma<POS>(lut, gword, gbits);
+    if constexpr (CLAMP) {
+        const bool over = g > limit;
+        clamped += __builtin_popcountll(__ballot(over));
+        a = over ? a_limit : a;
+        u = __builtin_amdgcn_fmed3f(u, -limit, limit);
+    }
+    const float b = a * u;
+    return b * w;
+}
+
+__device__ __forceinline__ void load_lut_to_lds(float2* lut)
+{
+    const uint4* src = reinterpret_cast<const uint4*>(g_sigma_lut);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    for (int i = threadIdx.x; i < kLutSize / 2; i += blockDim.x)
+        dst[i] = src[i];
+    __syncthreads();
+}
+
+template <int FMT>
+struct FmtTraits;
+template <>
+struct FmtTraits<8> {
+    static constexpr float kMax = 448.0f;         // 1.75 * 2^8
+    static constexpr int kExpBias = 127 + 8;      // biased exponent of 448
+    static constexpr uint32_t kMant = 0x600000u;  // mantissa field of 1.75
+};
+template <>
+struct FmtTraits<4> {
+    static constexpr float kMax = 6.0f;           // 1.5 * 2^2
+    static constexpr int kExpBias = 127 + 2;
+    static constexpr uint32_t kMant = 0x400000u;  // mantissa field of 1.5
+};
+
+// Scale of one group from its abs-max.  Returns the multiplier applied before
+// the cast and writes the stored scale representation.
+template <int FMT, int SFMT>
+__device__ __forceinline__ float group_scale(float amax, float& scale_f32, uint32_t& scale_u8)
+{
+    using T = FmtTraits<FMT>;
+    if constexpr (SFMT == TK_SCALE_FP32) {
+        scale_f32 = amax / T::kMax;                   // IEEE division, round to nearest even
+        return fminf(T::kMax / amax, FLT_MAX);        // amax == 0 -> +inf -> FLT_MAX
+    } else {
+        // smallest k with fmt_max * 2^k >= amax: compare amax = 1.M * 2^(E-127)
+        // with fmt_max = 1.F * 2^P; k = E - 127 - P + (M > F), at least -127.
+        const uint32_t bits = as_uint(amax);
+        int k = (int)(bits >> 23) - T::kExpBias + ((bits & 0x7FFFFFu) > T::kMant ? 1 : 0);
+        k = max(k, -127);
+        scale_u8 = (uint32_t)(k + 127);
+        return as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
+    }
+}
+
+__device__ __forceinline__ uint2 pack_fp8(const float* q)
+{
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+    return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ uint32_t pack_fp4(const float* q)
+{
+    uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[2], q[3], 1.0f, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[4], q[5], 1.0f, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[6], q[7], 1.0f, 3);
+    return v;
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_codes(const Params& p, uint32_t row, uint32_t slot, const float* q)
+{
+    if constexpr (FMT == 8) {
+        uint2* dst = reinterpret_cast<uint2*>(p.codes + (size_t)row * (p.slots * 8u)) + slot;
+        *dst = pack_fp8(q);
+    } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + (size_t)row * (p.slots * 4u)) + slot;
+        *dst = pack_fp4(q);
+    }
+}
+
+template <int SFMT>
+__device__ __forceinline__ void store_scale(const Params& p, size_t idx, float s32, uint32_t s8)
+{
+    if constexpr (SFMT == TK_SCALE_FP32)
+        static_cast<float*>(p.scales)[idx] = s32;
+    else
+        static_cast<uint8_t*>(p.scales)[idx] = (uint8_t)s8;
+}
+
+constexpr int kThreads = 256;
+
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED>
+__global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
+{
+    __shared__ float2 lut[kLutSize];
+    load_lut_to_lds(lut);
+
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t waves_per_block = kThreads / kWaveSize;
+    const uint32_t wave = blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize);
+    const uint32_t nwaves = gridDim.x * waves_per_block;
+
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = p.clamp;
+        a_limit = limit * sigmoid_rn(limit); // the activation of a clamped gate
+    }
+    unsigned long long clamped = 0;
+
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t unit_in_row = u - row * p.upr;
+        const uint32_t step0 = unit_in_row * p.spu;
+        const uint32_t nst = min(p.spu, p.steps_row - step0);
+        const uint4* xg = p.x + (size_t)row * (2u * p.slots);
+        const uint4* xu = xg + p.slots;
+        const float wr = p.w ? p.w[row] : 1.0f;
+
+        uint4 G[SPU], U[SPU];
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            const uint32_t slot = (step0 + s) * kWaveSize + lane;
+            if (s < (int)nst && slot < p.slots) {
+                G[s] = xg[slot];
+                U[s] = xu[slot];
+            } else {
+                G[s] = make_uint4(0, 0, 0, 0);
+                U[s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        float y[SPU][8];
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            const uint32_t gw[4] = {G[s].x, G[s].y, G[s].z, G[s].w};
+            const uint32_t uw[4] = {U[s].x, U[s].y, U[s].z, U[s].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    y[s][2 * k + h] = h ? swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped)
+                                        : swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped);
+                }
+            }
+        }
+
+        if constexpr (ROWRED) {
+            float m = 0.0f;
+#pragma unroll
+            for (int s = 0; s < SPU; ++s)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    m = fmaxf(m, fabsf(y[s][j]));
+            const float amax = wave_max(m);
+            float s32 = 0.0f;
+            uint32_t s8 = 0;
+            const float inv = group_scale<FMT, SFMT>(amax, s32, s8);
+#pragma unroll
+            for (int s = 0; s < SPU; ++s) {
+                const uint32_t slot = (step0 + s) * kWaveSize + lane;
+                if (s < (int)nst && slot < p.slots) {
+                    float q[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        q[j] = y[s][j] * inv;
+                    store_codes<FMT>(p, row, slot, q);
+                }
+            }
+            if (lane == 0)
+                store_scale<SFMT>(p, (size_t)row * p.groups_row + unit_in_row, s32, s8);
+        } else {
+#pragma unroll
+            for (int s = 0; s < SPU; ++s) {
+                if (s < (int)nst) {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        m = fmaxf(m, fabsf(y[s][j]));
+                    const float amax = group_max(m, p.gl_log2);
+                    float s32 = 0.0f;
+                    uint32_t s8 = 0;
+                    const float inv = group_scale<FMT, SFMT>(amax, s32, s8);
+                    const uint32_t slot = (step0 + s) * kWaveSize + lane;
+                    if (slot < p.slots) {
+                        float q[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            q[j] = y[s][j] * inv;
+                        store_codes<FMT>(p, row, slot, q);
+                        if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
+                            store_scale<SFMT>(p, (size_t)row * p.groups_row + (slot >> p.gl_log2), s32, s8);
+                    }
+                }
+            }
+        }
+    }
+
+    if constexpr (CLAMP) {
+        if (p.count && lane == 0 && clamped)
+            atomicAdd(p.count, clamped);
+    }
+}
+
+// The unfused first stage (swiglu_forward): fp32 y [n][hidden], same
+// per-element arithmetic as the fused kernel.  Thread t of the grid-stride
+// loop owns one 8-column lane slot of one row.
+template <bool CLAMP>
+__global__ __launch_bounds__(kThreads) void swiglu_forward_kernel(const uint4* __restrict__ x,
+                                                                  const float* __restrict__ w,
+                                                                  float4* __restrict__ y, uint32_t n,
+                                                                  uint32_t slots, float limit_in,
+                                                                  unsigned long long* count)
+{
+    __shared__ float2 lut[kLutSize];
+    load_lut_to_lds(lut);
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = limit_in;
+        a_limit = limit * sigmoid_rn(limit);
+    }
+    unsigned long long clamped = 0;
+    const uint64_t total = (uint64_t)n * slots;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    // every lane runs the same trip count so that the clamp ballots see whole waves
+    const uint64_t first = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t wave_first = first - (threadIdx.x & (kWaveSize - 1));
+    for (uint64_t base = wave_first; base < total; base += stride) {
+        const uint64_t t = base + (threadIdx.x & (kWaveSize - 1));
+        const bool active = t < total;
+        const uint32_t row = active ? (uint32_t)(t / slots) : 0;
+        const uint32_t slot = active ? (uint32_t)(t - (uint64_t)row * slots) : 0;
+        uint4 G = make_uint4(0, 0, 0, 0), U = make_uint4(0, 0, 0, 0);
+        float wr = 1.0f;
+        if (active) {
+            G = x[(size_t)row * 2 * slots + slot];
+            U = x[(size_t)row * 2 * slots + slots + slot];
+            wr = w ? w[row] : 1.0f;
+        }
+        const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
+        const uint32_t uw[4] = {U.x, U.y, U.z, U.w};
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped);
+            v[2 * k + 1] = swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped);
+        }
+        if (active) {
+            y[2 * t] = make_float4(v[0], v[1], v[2], v[3]);
+            y[2 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    }
+    if constexpr (CLAMP) {
+        if (count && (threadIdx.x & (kWaveSize - 1)) == 0 && clamped)
+            atomicAdd(count, clamped);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+struct DeviceState {
+    std::mutex mu;
+    bool ready = false;
+    int cus = 0;
+};
+DeviceState g_dev[kMaxDevices];
+
+tk_status init_device(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return TK_ERR_INVALID_ARG;
+    DeviceState& st = g_dev[dev];
+    std::lock_guard<std::mutex> lock(st.mu);
+    if (st.ready)
+        return TK_OK;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess)
+        return TK_ERR_HIP;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess)
+        return TK_ERR_HIP;
+    tk_status rc = TK_OK;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        rc = TK_ERR_HIP;
+    } else {
+        hipLaunchKernelGGL(sigma_lut_init_kernel, dim3((kLutSize + 255) / 256), dim3(256), 0, nullptr);
+        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess)
+            rc = TK_ERR_HIP;
+    }
+    if (rc == TK_OK) {
+        st.cus = cus;
+        st.ready = true;
+    }
+    if (prev != dev)
+        (void)hipSetDevice(prev);
+    return rc;
+}
+
+tk_status ensure_device(int& dev);
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn)
+{
+    if (!a || !b || an == 0 || bn == 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED>
+void launch_one(const Params& p, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED>), dim3(blocks), dim3(kThreads), 0,
+                       stream, p);
+}
+
+template <int FMT, int SFMT, bool CLAMP, bool ROWRED>
+bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
+{
+    switch (spu_max) {
+    case 1: launch_one<FMT, SFMT, CLAMP, 1, ROWRED>(p, blocks, stream); return true;
+    case 2: launch_one<FMT, SFMT, CLAMP, 2, ROWRED>(p, blocks, stream); return true;
+    case 4: launch_one<FMT, SFMT, CLAMP, 4, ROWRED>(p, blocks, stream); return true;
+    case 8: launch_one<FMT, SFMT, CLAMP, 8, ROWRED>(p, blocks, stream); return true;
+    case 16: launch_one<FMT, SFMT, CLAMP, 16, ROWRED>(p, blocks, stream); return true;
+    default: return false;
+    }
+}
+
+template <int FMT>
+bool dispatch(int sfmt, bool clamp, bool rowred, int spu_max, const Params& p, int blocks, hipStream_t s)
+{
+#define TK_BRANCH(SF, CL, RR)                                                                           \
+    if (sfmt == SF && clamp == CL && rowred == RR)                                                      \
+        return launch_spu<FMT, SF, CL, RR>(spu_max, p, blocks, s);
+    TK_BRANCH(TK_SCALE_FP32, false, false)
+    TK_BRANCH(TK_SCALE_FP32, false, true)
+    TK_BRANCH(TK_SCALE_FP32, true, false)
+    TK_BRANCH(TK_SCALE_FP32, true, true)
+    TK_BRANCH(TK_SCALE_UE8M0, false, false)
+    TK_BRANCH(TK_SCALE_UE8M0, false, true)
+    TK_BRANCH(TK_SCALE_UE8M0, true, false)
+    TK_BRANCH(TK_SCALE_UE8M0, true, true)
+#undef TK_BRANCH
+    return false;
+}
+
+uint32_t pow2_at_least(uint32_t v)
+{
+    uint32_t p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+constexpr int kBlocksPerCU = 4;
+
+tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t hidden, int64_t group_size,
+                      float clamp_limit, int scale_fmt, void* codes, void* scales, int64_t* clamped_count,
+                      void* stream)
+{
+    // ---- validation: no HIP call before every argument is checked ----
+    if (n < 0 || n >= (int64_t)INT_MAX)
+        return TK_ERR_INVALID_ARG;
+    if (hidden <= 0 || hidden % kSlotCols != 0 || hidden > (int64_t)INT_MAX / 4)
+        return TK_ERR_INVALID_ARG;
+    if (group_size < 0 || (group_size != 0 && (group_size % kSlotCols != 0 || hidden % group_size != 0)))
+        return TK_ERR_INVALID_ARG;
+    if (std::isnan(clamp_limit) || clamp_limit <= 0.0f)
+        return TK_ERR_INVALID_ARG;
+    if (scale_fmt != TK_SCALE_FP32 && scale_fmt != TK_SCALE_UE8M0)
+        return TK_ERR_INVALID_ARG;
+    if (n > 0 && (!x || !codes || !scales))
+        return TK_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 4) || !aligned(codes, fmt == 8 ? 8 : 4) ||
+        !aligned(clamped_count, 8) || (scale_fmt == TK_SCALE_FP32 && !aligned(scales, 4)))
+        return TK_ERR_INVALID_ARG;
+    const int64_t G = group_size ? group_size : hidden;
+    const int64_t groups_row = hidden / G;
+    const size_t x_bytes = (size_t)n * (size_t)hidden * 4u;
+    const size_t w_bytes = w ? (size_t)n * 4u : 0;
+    const size_t c_bytes = (size_t)n * (size_t)(fmt == 8 ? hidden : hidden / 2);
+    const size_t s_bytes = (size_t)n * (size_t)groups_row * (scale_fmt == TK_SCALE_FP32 ? 4u : 1u);
+    const size_t k_bytes = clamped_count ? 8u : 0u;
+    if (n > 0 && (overlaps(codes, c_bytes, x, x_bytes) || overlaps(codes, c_bytes, w, w_bytes) ||
+                  overlaps(scales, s_bytes, x, x_bytes) || overlaps(scales, s_bytes, w, w_bytes) ||
+                  overlaps(codes, c_bytes, scales, s_bytes) || overlaps(clamped_count, k_bytes, x, x_bytes) ||
+                  overlaps(clamped_count, k_bytes, w, w_bytes) || overlaps(clamped_count, k_bytes, codes, c_bytes) ||
+                  overlaps(clamped_count, k_bytes, scales, s_bytes)))
+        return TK_ERR_INVALID_ARG;
+
+    // ---- shape -> kernel variant ----
+    const uint32_t slots = (uint32_t)(hidden / kSlotCols);
+    const uint32_t steps_row = (slots + kWaveSize - 1) / kWaveSize;
+    const uint32_t gslots = (uint32_t)(G / kSlotCols);
+    Params p{};
+    bool rowred;
+    uint32_t spu_max;
+    if (G == hidden) {
+        if (steps_row > (uint32_t)kMaxStepsPerUnit)
+            return TK_ERR_UNSUPPORTED;
+        rowred = true;
+        p.spu = steps_row;
+        p.upr = 1;
+        spu_max = pow2_at_least(steps_row);
+    } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
+        rowred = false;
+        p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
+        spu_max = steps_row >= 4 && n >= 1024 ? 4u : (steps_row >= 2 && n >= 256 ? 2u : 1u);
+        if (spu_max > steps_row)
+            spu_max = pow2_at_least(steps_row);
+        p.spu = spu_max;
+        p.upr = (steps_row + p.spu - 1) / p.spu;
+    } else if (gslots % kWaveSize == 0) {
+        const uint32_t k = gslots / kWaveSize;
+        if (k > (uint32_t)kMaxStepsPerUnit)
+            return TK_ERR_UNSUPPORTED;
+        rowred = true;
+        p.spu = k;
+        p.upr = (uint32_t)groups_row;
+        spu_max = pow2_at_least(k);
+    } else {
+        return TK_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)n * p.upr >= (uint64_t)INT_MAX)
+        return TK_ERR_UNSUPPORTED;
+    if (n == 0)
+        return TK_OK;
+
+    int dev = 0;
+    {
+        const tk_status rc = ensure_device(dev);
+        if (rc != TK_OK)
+            return rc;
+    }
+
+    p.x = static_cast<const uint4*>(x);
+    p.w = w;
+    p.codes = static_cast<uint8_t*>(codes);
+    p.scales = scales;
+    p.count = reinterpret_cast<unsigned long long*>(clamped_count);
+    p.slots = slots;
+    p.steps_row = steps_row;
+    p.units = (uint32_t)(n * p.upr);
+    p.groups_row = (uint32_t)groups_row;
+    const bool clamp = !std::isinf(clamp_limit);
+    p.clamp = clamp_limit;
+
+    const uint32_t waves_per_block = kThreads / kWaveSize;
+    const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
+    const uint32_t cap = (uint32_t)g_dev[dev].cus * kBlocksPerCU;
+    const int blocks = (int)(want < cap ? want : cap);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool ok = fmt == 8 ? dispatch<8>(scale_fmt, clamp, rowred, (int)spu_max, p, blocks, s)
+                             : dispatch<4>(scale_fmt, clamp, rowred, (int)spu_max, p, blocks, s);
+    if (!ok)
+        return TK_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess)
+        return TK_ERR_HIP;
+    return TK_OK;
+}
+
+tk_status ensure_device(int& dev)
+{
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TK_ERR_HIP;
+    if (!g_dev[dev].ready)
+        return init_device(dev);
+    return TK_OK;
+}
+
+tk_status swiglu_forward(const void* x, const float* w, int64_t n, int64_t hidden, float clamp_limit,
+                         float* y, int64_t* clamped_count, void* stream)
+{
+    if (n < 0 || n >= (int64_t)INT_MAX)
+        return TK_ERR_INVALID_ARG;
+    if (hidden <= 0 || hidden % kSlotCols != 0 || hidden > (int64_t)INT_MAX / 4)
+        return TK_ERR_INVALID_ARG;
+    if (std::isnan(clamp_limit) || clamp_limit <= 0.0f)
+        return TK_ERR_INVALID_ARG;
+    if (n > 0 && (!x || !y))
+        return TK_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 4) || !aligned(y, 16) || !aligned(clamped_count, 8))
+        return TK_ERR_INVALID_ARG;
+    const size_t x_bytes = (size_t)n * (size_t)hidden * 4u;
+    const size_t w_bytes = w ? (size_t)n * 4u : 0;
+    const size_t y_bytes = (size_t)n * (size_t)hidden * 4u;
+    const size_t k_bytes = clamped_count ? 8u : 0u;
+    if (n > 0 && (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, w, w_bytes) ||
+                  overlaps(clamped_count, k_bytes, x, x_bytes) || overlaps(clamped_count, k_bytes, w, w_bytes) ||
+                  overlaps(clamped_count, k_bytes, y, y_bytes)))
+        return TK_ERR_INVALID_ARG;
+    if (n == 0)
+        return TK_OK;
+    int dev = 0;
+    const tk_status rc = ensure_device(dev);
+    if (rc != TK_OK)
+        return rc;
+    const uint32_t slots = (uint32_t)(hidden / kSlotCols);
+    const uint64_t total = (uint64_t)n * slots;
+    const uint64_t want = (total + kThreads - 1) / kThreads;
+    const uint64_t cap = (uint64_t)g_dev[dev].cus * kBlocksPerCU;
+    const int blocks = (int)(want < cap ? want : cap);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto* cnt = reinterpret_cast<unsigned long long*>(clamped_count);
+    if (std::isinf(clamp_limit))
+        hipLaunchKernelGGL(swiglu_forward_kernel<false>, dim3(blocks), dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), w, reinterpret_cast<float4*>(y), (uint32_t)n, slots,
+                           clamp_limit, cnt);
+    else
+        hipLaunchKernelGGL(swiglu_forward_kernel<true>, dim3(blocks), dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), w, reinterpret_cast<float4*>(y), (uint32_t)n, slots,
+                           clamp_limit, cnt);
+    return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+tk_status tk_swiglu_forward(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                            float clamp_limit, float* y, int64_t* clamped_count, void* stream)
+{
+    return swiglu_forward(x, topk_weight, n, hidden, clamp_limit, y, clamped_count, stream);
+}
+
+tk_status tk_init(int device)
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess)
+        return TK_ERR_HIP;
+    if (device < 0 || device >= count)
+        return TK_ERR_INVALID_ARG;
+    return init_device(device);
+}
+
+tk_status tk_swiglu_cast_fp8(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                             int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt, void* codes,
+                             void* scales, int64_t* clamped_count, void* stream)
+{
+    return swiglu_cast(8, x, topk_weight, n, hidden, group_size, clamp_limit, (int)scale_fmt, codes, scales,
+                       clamped_count, stream);
+}
+
+tk_status tk_swiglu_cast_fp4(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
+                             int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt, void* codes,
+                             void* scales, int64_t* clamped_count, void* stream)
+{
+    return swiglu_cast(4, x, topk_weight, n, hidden, group_size, clamp_limit, (int)scale_fmt, codes, scales,
+                       clamped_count, stream);
+}
+
+const char* tk_status_str(tk_status status)
+{
+    switch (status) {
+    case TK_OK: return "TK_OK";
+    case TK_ERR_INVALID_ARG: return "TK_ERR_INVALID_ARG";
+    case TK_ERR_UNSUPPORTED: return "TK_ERR_UNSUPPORTED";
+    case TK_ERR_HIP: return "TK_ERR_HIP";
+    }
+    return "TK_UNKNOWN_STATUS";
+}
+
+} // extern "C"

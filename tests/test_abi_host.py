@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/tk.h declares, and rejects bad arguments before making
+any HIP call (fake, never-dereferenced device addresses are used)."""
+import math
+import os
+import re
+
+import pytest
+
+import moe_activation_bit_amd as tk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tk.h")
+
+OK, INVALID, UNSUPPORTED = tk.TkStatus.TK_OK, tk.TkStatus.TK_ERR_INVALID_ARG, tk.TkStatus.TK_ERR_UNSUPPORTED
+FP32, UE8M0 = tk.TK_SCALE_FP32, tk.TK_SCALE_UE8M0
+INF = math.inf
+
+# fake device addresses: aligned, far apart, never dereferenced
+X, W, C, S, K = 0x7000_0000_0000, 0x7100_0000_0000, 0x7200_0000_0000, 0x7300_0000_0000, 0x7400_0000_0000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:tk_status|const char\s*\*)\s*(tk_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(["tk_init", "tk_status_str", "tk_swiglu_cast_fp4", "tk_swiglu_cast_fp8",
+                                         "tk_swiglu_forward"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tk.load_library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert name in tk.SIGNATURES, name
+        assert callable(getattr(tk, name)), name  # binding of the same name
+
+
+def test_status_strings():
+    for st in tk.TkStatus:
+        assert tk.tk_status_str(st) == st.name
+    assert tk.tk_status_str(99) == "TK_UNKNOWN_STATUS"
+
+
+def cast8(**kw):
+    a = dict(x=X, topk_weight=W, n=4, hidden=1024, group_size=0, clamp_limit=INF, scale_fmt=FP32, codes=C,
+             scales=S, clamped_count=None, stream=0)
+    a.update(kw)
+    return tk.tk_swiglu_cast_fp8(**a)
+
+
+def cast4(**kw):
+    a = dict(x=X, topk_weight=W, n=4, hidden=1024, group_size=32, clamp_limit=INF, scale_fmt=UE8M0, codes=C,
+             scales=S, clamped_count=None, stream=0)
+    a.update(kw)
+    return tk.tk_swiglu_cast_fp4(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=-1), dict(n=2 ** 31), dict(hidden=0), dict(hidden=-8), dict(hidden=12), dict(group_size=-8),
+    dict(group_size=12), dict(group_size=48), dict(clamp_limit=float("nan")), dict(clamp_limit=0.0),
+    dict(clamp_limit=-1.0), dict(clamp_limit=-INF), dict(scale_fmt=2), dict(x=None), dict(codes=None),
+    dict(scales=None), dict(x=X + 8), dict(codes=C + 4), dict(topk_weight=W + 2), dict(clamped_count=K + 4),
+    dict(codes=X), dict(scales=X + 64), dict(codes=W), dict(scales=C + 16), dict(clamped_count=S),
+], ids=str)
+def test_fp8_invalid_arguments(kw):
+    assert cast8(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=1028), dict(codes=C + 2), dict(group_size=24), dict(scales=S + 1, scale_fmt=FP32),
+], ids=str)
+def test_fp4_invalid_arguments(kw):
+    assert cast4(**kw) == INVALID
+
+
+def test_ue8m0_scales_need_no_alignment_and_n0_is_a_noop():
+    # n == 0 returns before any HIP call, with or without pointers
+    assert cast8(n=0) == OK
+    assert cast8(n=0, x=None, codes=None, scales=None) == OK
+    assert cast4(n=0, scales=S + 1) == OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=48, group_size=24),        # 3 lane slots per group: not a power of two
+    dict(hidden=1536, group_size=768),     # 96 slots: neither <= 64 and a power of two, nor a multiple of 64
+    dict(hidden=8200, group_size=0),       # per-token group longer than 8192 columns
+    dict(hidden=16384, group_size=16384),
+], ids=str)
+def test_unsupported_shapes(kw):
+    assert cast8(**kw) == UNSUPPORTED
+    assert cast8(n=0, **kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(hidden=4), dict(y=None), dict(y=X + 4), dict(y=X),
+                                dict(clamp_limit=float("nan"))], ids=str)
+def test_swiglu_forward_invalid_arguments(kw):
+    a = dict(x=X, topk_weight=W, n=4, hidden=1024, clamp_limit=INF, y=C, clamped_count=None, stream=0)
+    a.update(kw)
+    assert tk.tk_swiglu_forward(**a) == INVALID
+
+
+def test_init_rejects_bad_device():
+    # tk_init validates the index against the device count (0 here: no GPU)
+    assert tk.tk_init(-1) in (INVALID, tk.TkStatus.TK_ERR_HIP)

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle.
+
+Bar: bit-exact codes, scales and clamp counts (the kernel's sigmoid is the
+correctly rounded fp32 one, like the oracle's, so no tolerance is needed).
+Every output buffer is surrounded by canary bands that must stay untouched.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_activation_bit_amd as tk
+import oracle
+from moe_activation_bit_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+PAD = 256
+OK = tk.TkStatus.TK_OK
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def fmt_of(w):
+    return 8 if w.fmt == "fp8" else 4
+
+
+def sfmt_of(w):
+    return tk.TK_SCALE_FP32 if w.scale_fmt == "fp32" else tk.TK_SCALE_UE8M0
+
+
+class Out:
+    """Device outputs with canary bands before and after each buffer."""
+
+    def __init__(self, n, hidden, group, fmt, sfmt):
+        self.n, self.hidden, self.fmt, self.sfmt = n, hidden, fmt, sfmt
+        self.groups = 1 if group == 0 else hidden // group
+        self.cols = hidden if fmt == 8 else hidden // 2
+        self.sitem = 4 if sfmt == tk.TK_SCALE_FP32 else 1
+        self.cbuf = torch.full((n * self.cols + 2 * PAD,), 0xA5, dtype=torch.uint8, device=DEV)
+        self.sbuf = torch.full((n * self.groups * self.sitem + 2 * PAD,), 0x5A, dtype=torch.uint8, device=DEV)
+        self.kbuf = torch.zeros(3, dtype=torch.int64, device=DEV)
+        self.kbuf[0] = -7
+        self.kbuf[2] = -9
+
+    @property
+    def codes_ptr(self):
+        return self.cbuf.data_ptr() + PAD
+
+    @property
+    def scales_ptr(self):
+        return self.sbuf.data_ptr() + PAD
+
+    @property
+    def count_ptr(self):
+        return self.kbuf.data_ptr() + 8
+
+    def fetch(self):
+        torch.cuda.synchronize()
+        c = self.cbuf.cpu().numpy()
+        s = self.sbuf.cpu().numpy()
+        k = self.kbuf.cpu().numpy()
+        assert (c[:PAD] == 0xA5).all() and (c[len(c) - PAD:] == 0xA5).all(), "codes canary overwritten"
+        assert (s[:PAD] == 0x5A).all() and (s[len(s) - PAD:] == 0x5A).all(), "scales canary overwritten"
+        assert k[0] == -7 and k[2] == -9, "count canary overwritten"
+        codes = c[PAD:len(c) - PAD].reshape(self.n, self.cols)
+        sb = s[PAD:len(s) - PAD]
+        scales = (sb.view(np.float32) if self.sitem == 4 else sb).reshape(self.n, self.groups)
+        return codes, scales, int(k[1])
+
+
+def run_cast(x, w, hidden, group, clamp, fmt, sfmt, xd=None, wd=None, stream=None):
+    n = x.shape[0] if x is not None else xd.shape[0]
+    if xd is None:
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+    if wd is None and w is not None:
+        wd = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(DEV)
+    out = Out(n, hidden, group, fmt, sfmt)
+    fn = tk.tk_swiglu_cast_fp8 if fmt == 8 else tk.tk_swiglu_cast_fp4
+    rc = fn(xd, wd, n, hidden, group, math.inf if clamp is None else clamp, sfmt, out.codes_ptr, out.scales_ptr,
+            out.count_ptr, stream)
+    assert rc == OK, tk.tk_status_str(rc)
+    return out.fetch()
+
+
+def assert_same(got, want, what=""):
+    gc, gs, gk = got
+    wc, ws, wk = want
+    if not np.array_equal(gc, wc):
+        bad = np.argwhere(gc != wc)
+        r, c = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} code bytes differ; first at row {r} col {c}: "
+                             f"gpu {gc[r, c]:#x} oracle {wc[r, c]:#x}")
+    if not np.array_equal(gs.view(np.uint8), ws.view(np.uint8)):
+        bad = np.argwhere(gs.view(np.uint8).reshape(gs.shape[0], -1) != ws.view(np.uint8).reshape(ws.shape[0], -1))
+        raise AssertionError(f"{what}: scales differ at {bad[:5].tolist()}: gpu {gs.ravel()[:4]} oracle {ws.ravel()[:4]}")
+    assert gk == wk, f"{what}: clamp count gpu {gk} oracle {wk}"
+
+
+def test_init():
+    say("tk_init(0)")
+    assert tk.tk_init(0) == OK
+
+
+def run_forward(x, w, hidden, clamp):
+    n = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+    wd = None if w is None else torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(DEV)
+    y = torch.full((n * hidden + 128,), float("nan"), dtype=torch.float32, device=DEV)
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    rc = tk.tk_swiglu_forward(xd, wd, n, hidden, math.inf if clamp is None else clamp, y.data_ptr() + 256, cnt)
+    assert rc == OK
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    assert np.isnan(yy[:64]).all() and np.isnan(yy[64 + n * hidden:]).all(), "y canary overwritten"
+    return yy[64:64 + n * hidden].reshape(n, hidden), int(cnt.item())
+
+
+@pytest.mark.parametrize("clamp", [None, 10.0, 0.3])
+def test_activation_every_bf16_gate(clamp):
+    """y = a = RN(g*sigma(g)) for all 65536 gate bit patterns (non-finite ones
+    replaced by 0): every bit of the kernel's sigmoid path against the oracle."""
+    say("activation over all bf16 gates, clamp", clamp)
+    hidden = 4096
+    g = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite((g.astype(np.uint32) << 16).view(np.float32))
+    g = np.where(finite, g, 0).astype(np.uint16).reshape(16, hidden)
+    up = np.full_like(g, 0x3F80)  # 1.0
+    x = np.concatenate([g, up], axis=1)
+    y, cnt = run_forward(x, None, hidden, clamp)
+    yo, co = oracle.swiglu_forward(x, None, clamp)
+    assert np.array_equal(y.view(np.uint32), yo.view(np.uint32)), np.argwhere(y.view(np.uint32) != yo.view(np.uint32))[:5]
+    assert cnt == co
+
+
+def test_swiglu_forward_workload_rows():
+    w = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    say("swiglu_forward 331 rows", w.name)
+    x = wl.make_x(w, 3, rows=range(331))
+    wt = wl.make_w(w, 3)[:331]
+    y, cnt = run_forward(x, wt, w.hidden, w.clamp_limit)
+    yo, co = oracle.swiglu_forward(x, wt, w.clamp_limit)
+    assert np.array_equal(y.view(np.uint32), yo.view(np.uint32))
+    assert cnt == co > 0
+
+
+def oracle_cast(x, w, wk):
+    return oracle.swiglu_cast(x, w, wk.group_size, wk.clamp_limit, fmt_of(wk), sfmt_of(wk))
+
+
+def test_tiny_workload_all_rows_and_determinism():
+    w = wl.WORKLOADS["fp8_per_token_n256_h1024"]
+    for seed in (0, 1, 2):
+        say(w.name, "seed", seed)
+        x, wt = wl.make_x(w, seed), wl.make_w(w, seed)
+        got = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
+        assert_same(got, oracle_cast(x, wt, w), f"{w.name} seed {seed}")
+        again = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
+        assert_same(again, got, "determinism")
+
+
+@pytest.mark.parametrize("name", ["fp8_g128_ue8m0_n32768_h2048", "fp8_per_token_clamp10_n131072_h2048",
+                                  "fp4_g32_ue8m0_n65536_h4096"])
+def test_workload_reduced_rows(name):
+    """1037 rows of each large workload (several units per wave, ragged against the grid)."""
+    w = wl.WORKLOADS[name]
+    rows = 1037
+    say(name, "reduced", rows)
+    x = wl.make_x(w, 0, rows=range(rows))
+    wt = wl.make_w(w, 0)[:rows]
+    got = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
+    assert_same(got, oracle_cast(x, wt, w), name)
+
+
+def test_ragged_decode_every_seed():
+    w = wl.WORKLOADS["fp8_g128_fp32_ragged_h7168"]
+    rng = np.random.default_rng(11)
+    for seed in range(10):
+        n = wl.num_rows(w, seed)
+        say(w.name, "seed", seed, "rows", n)
+        x, wt = wl.make_x(w, seed), wl.make_w(w, seed)
+        got = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
+        rows = np.arange(n) if n <= 96 else np.unique(np.concatenate(
+            [np.arange(32), np.arange(n - 32, n), rng.choice(n, 32, replace=False)]))
+        want = oracle_cast(x[rows], wt[rows], w)
+        assert_same((got[0][rows], got[1][rows], 0), (want[0], want[1], 0), f"{w.name} seed {seed}")
+        assert (wt == 0).any() or n < 5
+
+
+@pytest.mark.parametrize("name", ["fp8_g128_ue8m0_n32768_h2048", "fp8_per_token_clamp10_n131072_h2048",
+                                  "fp4_g32_ue8m0_n65536_h4096"])
+def test_workload_full_size_sampled(name):
+    """Full size, launched as the benchmark launches it; the oracle checks a
+    sample of rows, properties are checked on every row."""
+    w = wl.WORKLOADS[name]
+    n = wl.num_rows(w, 0)
+    say(name, "full size", n)
+    x, wt = wl.make_x(w, 0), wl.make_w(w, 0)
+    got = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n), rng.choice(n, 24, replace=False)]))
+    want = oracle_cast(x[rows], wt[rows], w)
+    assert_same((got[0][rows], got[1][rows], 0), (want[0], want[1], 0), name)
+    codes, scales, cnt = got
+    if w.fmt == "fp8":
+        assert not ((codes & 0x7F) == 0x7F).any(), "NaN code produced"
+    if w.clamp_limit is not None:
+        gate = x[:, : w.hidden].astype(np.uint32) << 16
+        assert cnt == int((gate.view(np.float32) > w.clamp_limit).sum())
+    if w.scale_fmt == "fp32":
+        assert np.isfinite(scales).all() and (scales >= 0).all()
+
+
+SHAPES = [  # (hidden, group, fmt, scale_fmt, clamp, weighted)
+    (8, 0, 8, 0, None, True), (8, 8, 4, 1, 0.5, True), (1000, 0, 8, 0, 2.0, True), (1000, 8, 8, 1, None, False),
+    (1000, 40, 8, 0, None, True), (2048, 16, 8, 1, None, True), (2048, 64, 4, 0, 1.5, True),
+    (2048, 256, 8, 0, None, True), (2048, 512, 4, 1, None, True), (2048, 1024, 8, 1, 3.0, True),
+    (3072, 1536, 8, 0, None, True), (8192, 0, 8, 0, 5.0, True), (8192, 0, 4, 1, None, False), (7168, 128, 4, 0, None, True),
+    (512, 0, 4, 0, None, True), (1536, 0, 8, 1, None, True), (64, 32, 8, 0, None, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_shapes_groups_and_formats(shape):
+    hidden, group, fmt, sfmt, clamp, weighted = shape
+    slots = hidden // 8
+    gslots = (group or hidden) // 8
+    supported = group == 0 and slots <= 16 * 64 or (group and ((gslots & (gslots - 1)) == 0 and gslots <= 64
+                                                              or gslots % 64 == 0 and gslots // 64 <= 16))
+    base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    rows = 67
+    say("shape", shape)
+    full = wl.make_x(base, 4, rows=range(rows))
+    x = np.concatenate([full[:, :hidden], full[:, 2048:2048 + hidden]], axis=1) if hidden <= 2048 else \
+        np.tile(full, (1, (2 * hidden + 4095) // 4096))[:, :2 * hidden]
+    x = np.ascontiguousarray(x)
+    wt = wl.make_w(base, 4)[:rows] if weighted else None
+    if not supported:
+        n = x.shape[0]
+        out = Out(n, hidden, group, fmt, sfmt)
+        fn = tk.tk_swiglu_cast_fp8 if fmt == 8 else tk.tk_swiglu_cast_fp4
+        xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+        rc = fn(xd, None, n, hidden, group, math.inf, sfmt, out.codes_ptr, out.scales_ptr, None, None)
+        assert rc == tk.TkStatus.TK_ERR_UNSUPPORTED
+        return
+    got = run_cast(x, wt, hidden, group, clamp, fmt, sfmt)
+    want = oracle.swiglu_cast(x, wt, group, clamp, fmt, sfmt)
+    assert_same(got, want, str(shape))
+
+
+def test_batch_invariance_and_pointer_offsets():
+    w = wl.WORKLOADS["fp8_g128_ue8m0_n32768_h2048"]
+    n = 1500
+    say("batch invariance", n)
+    x, wt = wl.make_x(w, 1, rows=range(n)), wl.make_w(w, 1)[:n]
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+    wd = torch.from_numpy(wt).to(DEV)
+    full = run_cast(None, None, w.hidden, w.group_size, None, 8, 1, xd=xd, wd=wd)
+    for r0, k in [(0, 1), (1, 1), (777, 64), (1499, 1), (100, 1400)]:
+        part = run_cast(None, None, w.hidden, w.group_size, None, 8, 1, xd=xd[r0:r0 + k], wd=wd[r0:r0 + k])
+        assert_same(part, (full[0][r0:r0 + k], full[1][r0:r0 + k], 0), f"rows {r0}+{k}")
+
+
+def test_infinite_limit_equals_unclamped_and_huge_limit():
+    w = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    say("clamp limits")
+    x, wt = wl.make_x(w, 2, rows=range(300)), wl.make_w(w, 2)[:300]
+    a = run_cast(x, wt, w.hidden, 0, None, 8, 0)
+    b = run_cast(x, wt, w.hidden, 0, 3.0e38, 8, 0)
+    assert_same(a, b, "inf vs huge limit")
+    assert a[2] == 0 and b[2] == 0
+    c = run_cast(x, wt, w.hidden, 128, 10.0, 8, 1)
+    assert_same(c, oracle.swiglu_cast(x, wt, 128, 10.0, 8, 1), "clamp per-block ue8m0")
+
+
+def test_zero_rows_and_zero_values():
+    say("n = 0 and zero inputs")
+    out = Out(4, 1024, 0, 8, 0)
+    xd = torch.zeros((4, 2048), dtype=torch.int16, device=DEV)
+    rc = tk.tk_swiglu_cast_fp8(xd, None, 0, 1024, 0, math.inf, 0, out.codes_ptr, out.scales_ptr, out.count_ptr)
+    assert rc == OK
+    torch.cuda.synchronize()
+    assert (out.cbuf.cpu().numpy() == 0xA5).all(), "n == 0 must not write"
+    x = np.zeros((5, 2048), dtype=np.uint16)
+    x[1, :1024] = 0x8000  # -0 gates
+    x[2, 1024:] = 0x8000  # -0 ups
+    x[3] = wl.make_x(wl.WORKLOADS["fp8_per_token_n256_h1024"], 0, rows=[3])[0]
+    wt = np.array([1, 1, 1, 0, 0.5], dtype=np.float32)
+    for fmt, sfmt, g in [(8, 0, 0), (8, 1, 128), (4, 1, 32), (4, 0, 0)]:
+        got = run_cast(x, wt, 1024, g, None, fmt, sfmt)
+        assert_same(got, oracle.swiglu_cast(x, wt, g, None, fmt, sfmt), f"zeros {fmt} {sfmt} {g}")
+
+
+def test_side_stream():
+    w = wl.WORKLOADS["fp4_g32_ue8m0_n65536_h4096"]
+    say("side stream")
+    x, wt = wl.make_x(w, 1, rows=range(200)), wl.make_w(w, 1)[:200]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run_cast(x, wt, w.hidden, w.group_size, None, 4, 1, stream=s)
+    assert_same(got, oracle_cast(x, wt, w), "side stream")
