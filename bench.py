@@ -3,14 +3,22 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one launch of the fused kernel over one whole batch of the
-workload (inputs resident in HBM).  The timed region is exactly K steps
-bracketed by device synchronisations; per-launch durations come from HIP
-events recorded on the launch stream.  Inputs and outputs rotate over
-several buffer sets whose combined footprint is far above the 256 MB
-Infinity Cache, so every launch streams from HBM.
+workload (inputs resident in HBM).  The timed region is exactly K
+back-to-back steps bracketed by device synchronisations and by two HIP
+events on the launch stream (GPU time per launch = event time / K).  Inputs
+and outputs rotate over several buffer sets whose combined footprint is far
+above the 256 MB Infinity Cache, so every launch streams from HBM.
 
 Prints one JSON line on stdout.  The CPU baseline is the oracle, timed on a
 bounded sample of the same workload's rows on the host's cores.
+
+HBM traffic (roofline.traffic) comes from two rocprofv3 counter runs of
+`bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration`, one with
+`--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`; `bench.py --summarize-pmc
+FETCH.csv WRITE.csv` scales the fused kernel's per-dispatch counters by what
+the same counters read for a plain elementwise copy of known size and writes
+profiles/traffic_<workload>.json (tagged with the kernel source digest; a
+stale record is ignored).
 """
 from __future__ import annotations
 
@@ -47,6 +55,110 @@ def traffic_for(workload: str, launches_bytes: float):
     if rec.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+COPY_CAL_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
+def copy_calibration(torch, dev):
+    """A plain elementwise copy of known size (read COPY_CAL_BYTES, write
+    COPY_CAL_BYTES) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the fused kernel, scaled by
+    the calibration copy's readings; writes profiles/traffic_<workload>.json."""
+    from moe_activation_bit_amd import workloads as wl
+
+    w = wl.WORKLOADS[workload]
+    n = wl.num_rows(w, 0)
+
+    def per_dispatch(rows, counter, pick):
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r.get("Counter_Name") == counter and pick(r.get("Kernel_Name", ""))]
+        return sum(vals) / len(vals) if vals else None, len(vals)
+
+    fused = lambda k: "swiglu_cast_kernel" in k
+    copy = lambda k: "MulFunctor" in k  # torch.mul(src, 1.0, out=dst): the calibration copy
+    f_rows, w_rows = _pmc_rows(fetch_csv), _pmc_rows(write_csv)
+    f_kib, nf = per_dispatch(f_rows, "FETCH_SIZE", fused)
+    w_kib, nw = per_dispatch(w_rows, "WRITE_SIZE", fused)
+    cf_kib, ncf = per_dispatch(f_rows, "FETCH_SIZE", copy)
+    cw_kib, ncw = per_dispatch(w_rows, "WRITE_SIZE", copy)
+    if None in (f_kib, w_kib, cf_kib, cw_kib):
+        raise SystemExit("counter rows missing: fused %s/%s copy %s/%s" % (nf, nw, ncf, ncw))
+    fetch_scale = (COPY_CAL_BYTES / 1024.0) / cf_kib
+    write_scale = (COPY_CAL_BYTES / 1024.0) / cw_kib
+    fetch_bytes = f_kib * 1024.0 * fetch_scale
+    write_bytes = w_kib * 1024.0 * write_scale
+    rec = {
+        "workload": workload,
+        "kernel_source_sha256_16": kernel_source_digest(),
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+        "copy_fetch_kib_per_dispatch": cf_kib, "copy_write_kib_per_dispatch": cw_kib,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "hbm_bytes_per_launch": round(fetch_bytes + write_bytes),
+        "algorithmic_bytes_per_launch": w.algorithmic_bytes(n),
+        "dispatches": {"fused_fetch": nf, "fused_write": nw, "copy_fetch": ncf, "copy_write": ncw},
+    }
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def stream_ceiling(torch, dev, in_bytes: int, reps: int = 30):
+    """GB/s of plain streaming kernels moving the workload's bytes: read-4 /
+    write-1 (x in, one byte out per four read) and read-only."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_activation_bit_amd", "libstreamceil.so"))
+    lib.stream_read4_write1.restype = ctypes.c_int
+    lib.stream_read4_write1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.stream_read_only.restype = ctypes.c_int
+    lib.stream_read_only.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    in_bytes -= in_bytes % 32
+    sets = 3
+    ins = [torch.ones(in_bytes // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
+    outs = [torch.empty(in_bytes // 16, dtype=torch.int32, device=dev) for _ in range(sets)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+
+    def timed(fn, nbytes):
+        for i in range(3):
+            fn(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (ev0.elapsed_time(ev1) / 1e3 / reps) / 1e9
+
+    def rw(i):
+        assert lib.stream_read4_write1(ins[i % sets].data_ptr(), outs[i % sets].data_ptr(), in_bytes, sh) == 0
+
+    def ro(i):
+        assert lib.stream_read_only(ins[i % sets].data_ptr(), in_bytes, sink.data_ptr(), sh) == 0
+
+    res = {"read4_write1_GBs": round(timed(rw, in_bytes + in_bytes // 4), 1),
+           "read_only_GBs": round(timed(ro, in_bytes), 1),
+           "read_bytes": in_bytes,
+           "kernel": "non-persistent, 32 B read + 8 B written per thread, non-temporal"}
+    del ins, outs
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, seed: int, rows: int):
@@ -90,7 +202,16 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain elementwise copy of known size first (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        from moe_activation_bit_amd import workloads as wl
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload or wl.HEADLINE)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -115,6 +236,8 @@ def main():
     assert tk.tk_init(0) == tk.TkStatus.TK_OK
 
     log(f"[bench] workload {name}: rows {n}, hidden {w.hidden}, steps {args.steps}, warmup {args.warmup}")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     x_host = wl.make_x(w, args.seed)
     w_host = wl.make_w(w, args.seed)
     sets = []
@@ -195,6 +318,11 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        log("[bench] streaming ceiling ...")
+        ceil = stream_ceiling(torch, dev, 4 * w.hidden * n)
+        out["roofline"]["measured_ceiling"] = ceil
+        out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["read4_write1_GBs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_rows)

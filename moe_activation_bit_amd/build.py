@@ -2,6 +2,7 @@
 
 libtk.so    -- the HIP kernels and C ABI (hipcc, gfx950)
 libsynth.so -- the seeded input generator (plain C)
+libstreamceil.so -- plain streaming kernels that measure the HBM ceiling
 """
 from __future__ import annotations
 
@@ -36,6 +37,8 @@ def build_commands():
     return {
         "libtk.so": [HIPCC] + HIP_FLAGS + ["-o", os.path.join(HERE, "libtk.so"),
                                            os.path.join(CSRC, "tk_swiglu_cast.hip")],
+        "libstreamceil.so": [HIPCC] + HIP_FLAGS + ["-o", os.path.join(HERE, "libstreamceil.so"),
+                                                   os.path.join(CSRC, "stream_ceiling.hip")],
         "libsynth.so": ["gcc", "-O2", "-fPIC", "-shared", "-o", os.path.join(HERE, "libsynth.so"),
                         os.path.join(CSRC, "synth.c"), "-lm"],
     }

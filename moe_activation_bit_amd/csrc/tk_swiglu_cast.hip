@@ -10,23 +10,27 @@
 // per-block, UE8M0 scales).
 //
 // gfx950 design (no code from the pages' TileLang/CUDA kernel):
-//  - A wavefront of 64 lanes owns one "unit": up to SPU "steps" of one row,
-//    where a step is 512 columns: lane l reads 16 bytes (8 bf16) of the gate
-//    half and 16 bytes of the up half at column 8*(64*step + l).  Loads are
-//    128-bit and fully coalesced (1 KiB per wave instruction).
+//  - A wavefront of 64 lanes owns one "unit": SPU "steps" of one row, where a
+//    step is 512 columns: lane l reads 16 bytes (8 bf16) of the gate half and
+//    16 bytes of the up half at column 8*(64*step + l).  Loads are 128-bit,
+//    fully coalesced (1 KiB per wave instruction) and non-temporal; the row
+//    base is wave-uniform (scalar registers), lanes add a 32-bit offset.
 //  - sigma(g) comes from a 32 KiB table in LDS indexed by the bf16 bits of g
 //    (the gate is bf16, so sigma has only 65536 possible inputs; outside the
 //    4096 tabulated magnitudes it is constant in fp32).  The table holds the
 //    correctly rounded fp32 sigma and is computed on the GPU once per device.
-//  - Group abs-max: lane-local max over 8 values, then DPP butterflies inside
-//    the 2^j lanes of a group (quad_perm, row_half_mirror, row_mirror), or a
-//    whole-wave reduction for per-token / 512k-column groups.
+//  - Group abs-max: lane-local max over 8 values, then DPP butterflies on the
+//    bit patterns (v_max_u32_dpp) inside the 2^j lanes of a group
+//    (quad_perm, row_half_mirror, row_mirror), or a whole-wave reduction for
+//    per-token / 512k-column groups.
 //  - Casts use the gfx950 converters: v_cvt_pk_fp8_f32 (OCP E4M3, round to
 //    nearest even) and v_cvt_scalef32_pk_fp4_f32 with scale 1 (E2M1, round to
 //    nearest even, saturating).  Quantised values never exceed fmt_max by
 //    more than one fp32 ulp, so the E4M3 converter's lack of saturation above
-//    464 is never reached.
-//  - A persistent grid sized from the CU count; every wave strides over units.
+//    464 is never reached.  Codes leave with non-temporal stores.
+//  - A persistent grid of two 256-thread workgroups per CU (measured best on
+//    MI355X); every wave strides over units, so the LDS table is filled once
+//    per workgroup.
 //  - The clamp counter is reduced per wave with ballots and added to the
 //    int64 counter with one vector atomic per wave.
 #include <hip/hip_runtime.h>
@@ -44,7 +48,6 @@ namespace {
 
 constexpr int kWaveSize = 64;
 constexpr int kSlotCols = 8;                     // columns per lane per step (16 B of bf16)
-constexpr int kStepCols = kWaveSize * kSlotCols; // 512
 constexpr int kMaxStepsPerUnit = 16;             // largest row-reduced group: 8192 columns
 
 // Sigmoid table: magnitudes m of bf16 bit patterns in [kLutFirst, kLutFirst+kLutSize),
@@ -137,39 +140,51 @@ struct Params {
     float clamp;            // L (clamp variants)
 };
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// Abs-max reductions run on the bit patterns of non-negative floats, whose
+// unsigned order is their numeric order; umax with identity 0 folds into a
+// single v_max_u32_dpp per butterfly step.
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v)
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v)
 {
-    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return fmaxf(v, __builtin_bit_cast(float, t));
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
 }
 
 // max over the 2^gl_log2 consecutive lanes of each group (all lanes active)
-__device__ __forceinline__ float group_max(float v, uint32_t gl_log2)
+__device__ __forceinline__ uint32_t group_umax(uint32_t v, uint32_t gl_log2)
 {
-    if (gl_log2 >= 1) v = dpp_max<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
-    if (gl_log2 >= 2) v = dpp_max<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-    if (gl_log2 >= 3) v = dpp_max<0x141>(v); // row_half_mirror: quads of 8 lanes
-    if (gl_log2 >= 4) v = dpp_max<0x140>(v); // row_mirror: halves of 16 lanes
-    if (gl_log2 >= 5) v = fmaxf(v, __shfl_xor(v, 16));
-    if (gl_log2 >= 6) v = fmaxf(v, __shfl_xor(v, 32));
+    if (gl_log2 >= 1) v = dpp_umax<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    if (gl_log2 >= 2) v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if (gl_log2 >= 3) v = dpp_umax<0x141>(v); // row_half_mirror: quads of 8 lanes
+    if (gl_log2 >= 4) v = dpp_umax<0x140>(v); // row_mirror: halves of 16 lanes
+    if (gl_log2 >= 5) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    if (gl_log2 >= 6) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
 {
-    v = dpp_max<0xB1>(v);
-    v = dpp_max<0x4E>(v);
-    v = dpp_max<0x141>(v);
-    v = dpp_max<0x140>(v);
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+    v = dpp_umax<0xB1>(v);
+    v = dpp_umax<0x4E>(v);
+    v = dpp_umax<0x141>(v);
+    v = dpp_umax<0x140>(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 
-// sigma(g) for a gate whose bf16 bits sit in bits [pos, pos+16) of `word`;
+typedef float2 LutT;
+__device__ __forceinline__ void load_lut_to_lds(float2* lut)
+{
+    const uint4* src = reinterpret_cast<const uint4*>(g_sigma_lut);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    for (int i = threadIdx.x; i < kLutSize / 2; i += blockDim.x)
+        dst[i] = src[i];
+    __syncthreads();
+}
+// sigma(g) for a gate whose bf16 bits sit in bits [POS, POS+16) of `word`;
 // gbits is the fp32 bit pattern of the same gate (its sign selects the entry).
 template <int POS>
 __device__ __forceinline__ float lut_sigma(const float2* lut, uint32_t word, uint32_t gbits)
@@ -180,12 +195,16 @@ __device__ __forceinline__ float lut_sigma(const float2* lut, uint32_t word, uin
     return ((int32_t)gbits < 0) ? pr.y : pr.x;
 }
 
+constexpr int kLutLdsBytes = kLutSize * 8;
+
 // One element: gate and up are the bf16 halves at bit POS of `gword` / `uword`.
 // a = RN(g * sigma(g)) (or the clamped gate's activation), b = RN(a * u),
-// y = RN(b * w); three fp32 products, never fused.
+// y = RN(b * w); three fp32 products, never fused.  `counts` is false on lanes
+// past the end of the row, whose gates must not enter the clamp count.
 template <int POS, bool CLAMP>
-__device__ __forceinline__ float swiglu_elem(const float2* lut, uint32_t gword, uint32_t uword, float w,
-                                             float limit, float a_limit, unsigned long long& clamped)
+__device__ __forceinline__ float swiglu_elem(const LutT* lut, uint32_t gword, uint32_t uword, float w,
+                                             float limit, float a_limit, unsigned long long& clamped,
+                                             bool counts = true)
 {
     const uint32_t gbits = POS ? (gword & 0xFFFF0000u) : (gword << 16);
     float u = as_float(POS ? (uword & 0xFFFF0000u) : (uword << 16));
@@ -193,21 +212,12 @@ __device__ __forceinline__ float swiglu_elem(const float2* lut, uint32_t gword, 
     float a = g * lut_sigma<POS>(lut, gword, gbits);
     if constexpr (CLAMP) {
         const bool over = g > limit;
-        clamped += __builtin_popcountll(__ballot(over));
+        clamped += __builtin_popcountll(__ballot(over && counts));
         a = over ? a_limit : a;
         u = __builtin_amdgcn_fmed3f(u, -limit, limit);
     }
     const float b = a * u;
     return b * w;
-}
-
-__device__ __forceinline__ void load_lut_to_lds(float2* lut)
-{
-    const uint4* src = reinterpret_cast<const uint4*>(g_sigma_lut);
-    uint4* dst = reinterpret_cast<uint4*>(lut);
-    for (int i = threadIdx.x; i < kLutSize / 2; i += blockDim.x)
-        dst[i] = src[i];
-    __syncthreads();
 }
 
 template <int FMT>
@@ -225,53 +235,48 @@ struct FmtTraits<4> {
     static constexpr uint32_t kMant = 0x400000u;  // mantissa field of 1.5
 };
 
-// Scale of one group from its abs-max.  Returns the multiplier applied before
-// the cast and writes the stored scale representation.
+// Scale of one group from the bit pattern of its abs-max.  Returns the
+// multiplier applied before the cast (2^-k for UE8M0) and writes the stored
+// scale representation.
 template <int FMT, int SFMT>
-__device__ __forceinline__ float group_scale(float amax, float& scale_f32, uint32_t& scale_u8)
+__device__ __forceinline__ float group_scale(uint32_t amax_bits, float& scale_f32, uint32_t& scale_u8)
 {
     using T = FmtTraits<FMT>;
     if constexpr (SFMT == TK_SCALE_FP32) {
+        const float amax = as_float(amax_bits);
         scale_f32 = amax / T::kMax;                   // IEEE division, round to nearest even
         return fminf(T::kMax / amax, FLT_MAX);        // amax == 0 -> +inf -> FLT_MAX
     } else {
         // smallest k with fmt_max * 2^k >= amax: compare amax = 1.M * 2^(E-127)
         // with fmt_max = 1.F * 2^P; k = E - 127 - P + (M > F), at least -127.
-        const uint32_t bits = as_uint(amax);
-        int k = (int)(bits >> 23) - T::kExpBias + ((bits & 0x7FFFFFu) > T::kMant ? 1 : 0);
+        int k = (int)(amax_bits >> 23) - T::kExpBias + ((amax_bits & 0x7FFFFFu) > T::kMant ? 1 : 0);
         k = max(k, -127);
         scale_u8 = (uint32_t)(k + 127);
         return as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
     }
 }
 
-__device__ __forceinline__ uint2 pack_fp8(const float* q)
-{
-    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
-    return make_uint2(lo, hi);
-}
-
-__device__ __forceinline__ uint32_t pack_fp4(const float* q)
-{
-    uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
-    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[2], q[3], 1.0f, 1);
-    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[4], q[5], 1.0f, 2);
-    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[6], q[7], 1.0f, 3);
-    return v;
-}
-
+// q = RN(y * inv), cast, and one non-temporal store of the lane's 8 codes.
 template <int FMT>
-__device__ __forceinline__ void store_codes(const Params& p, uint32_t row, uint32_t slot, const float* q)
+__device__ __forceinline__ void quantize_store(uint8_t* row_codes, uint32_t slot, const float* y, float inv)
 {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        q[j] = y[j] * inv;
     if constexpr (FMT == 8) {
-        uint2* dst = reinterpret_cast<uint2*>(p.codes + (size_t)row * (p.slots * 8u)) + slot;
-        *dst = pack_fp8(q);
+        uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+        uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+        const v2u v = {lo, hi};
+        __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(row_codes) + slot);
     } else {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + (size_t)row * (p.slots * 4u)) + slot;
-        *dst = pack_fp4(q);
+        uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[2], q[3], 1.0f, 1);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[4], q[5], 1.0f, 2);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[6], q[7], 1.0f, 3);
+        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(row_codes) + slot);
     }
 }
 
@@ -286,110 +291,133 @@ __device__ __forceinline__ void store_scale(const Params& p, size_t idx, float s
 
 constexpr int kThreads = 256;
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED>
+// Streaming 16-byte load, marked non-temporal: the input is read exactly once.
+__device__ __forceinline__ uint4 load16(const uint4* p)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The data of one unit held in registers between its load and its use.
+template <int SPU>
+struct Unit {
+    uint4 g[SPU], u[SPU];
+    uint32_t row, unit_in_row, step0, nst;
+    float w;
+};
+
+template <int SPU, bool ROWRED, bool PARTIAL>
+__device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t lane, Unit<SPU>& d)
+{
+    d.row = u / p.upr;
+    d.unit_in_row = u - d.row * p.upr;
+    d.step0 = d.unit_in_row * p.spu;
+    d.nst = ROWRED ? min(p.spu, p.steps_row - d.step0) : (uint32_t)SPU;
+    // uniform row bases (scalar registers) + a 32-bit per-lane byte offset
+    const char* xg = reinterpret_cast<const char*>(p.x) + (size_t)d.row * (p.slots * 32u);
+    const char* xu = xg + p.slots * 16u;
+    const uint32_t lane_off = (d.step0 * kWaveSize + lane) * 16u;
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        if (!ROWRED || s < (int)d.nst) {
+            uint32_t off = lane_off + (uint32_t)s * (kWaveSize * 16u);
+            if (PARTIAL) // lanes past the row end re-read its last slot
+                off = min(off, (p.slots - 1u) * 16u);
+            d.g[s] = load16(reinterpret_cast<const uint4*>(xg + off));
+            d.u[s] = load16(reinterpret_cast<const uint4*>(xu + off));
+        }
+    }
+    d.w = p.w ? p.w[d.row] : 1.0f;
+}
+
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
+__device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
+                                             float limit, float a_limit, unsigned long long& clamped)
+{
+    float y[SPU][8];
+    uint32_t mbits[SPU];
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        if (!ROWRED || s < (int)d.nst) {
+            const uint32_t gw[4] = {d.g[s].x, d.g[s].y, d.g[s].z, d.g[s].w};
+            const uint32_t uw[4] = {d.u[s].x, d.u[s].y, d.u[s].z, d.u[s].w};
+            const bool valid = !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots;
+            float m = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[s][2 * k] = swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], d.w, limit, a_limit, clamped, valid);
+                y[s][2 * k + 1] = swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], d.w, limit, a_limit, clamped, valid);
+                m = fmaxf(m, fmaxf(fabsf(y[s][2 * k]), fabsf(y[s][2 * k + 1])));
+            }
+            if (!valid)
+                m = 0.0f;
+            mbits[s] = as_uint(m);
+        }
+    }
+    uint8_t* row_codes = p.codes + (size_t)d.row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+    if constexpr (ROWRED) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int s = 0; s < SPU; ++s)
+            if (s < (int)d.nst)
+                mb = max(mb, mbits[s]);
+        mb = wave_umax(mb);
+        float s32 = 0.0f;
+        uint32_t s8 = 0;
+        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            if (s < (int)d.nst) {
+                const uint32_t slot = (d.step0 + s) * kWaveSize + lane;
+                if (!PARTIAL || slot < p.slots)
+                    quantize_store<FMT>(row_codes, slot, y[s], inv);
+            }
+        }
+        if (lane == 0)
+            store_scale<SFMT>(p, (size_t)d.row * p.groups_row + d.unit_in_row, s32, s8);
+    } else {
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            const uint32_t mb = group_umax(mbits[s], p.gl_log2);
+            float s32 = 0.0f;
+            uint32_t s8 = 0;
+            const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+            const uint32_t slot = (d.step0 + s) * kWaveSize + lane;
+            if (!PARTIAL || slot < p.slots) {
+                quantize_store<FMT>(row_codes, slot, y[s], inv);
+                if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
+                    store_scale<SFMT>(p, (size_t)d.row * p.groups_row + (slot >> p.gl_log2), s32, s8);
+            }
+        }
+    }
+}
+
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
-    __shared__ float2 lut[kLutSize];
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    LutT* lut = reinterpret_cast<LutT*>(lut_raw);
     load_lut_to_lds(lut);
 
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t waves_per_block = kThreads / kWaveSize;
-    const uint32_t wave = blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize);
+    // wave-uniform by construction; readfirstlane lets the compiler keep all
+    // unit bookkeeping (row, step, addresses) in scalar registers
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
 
     float limit = 0.0f, a_limit = 0.0f;
     if constexpr (CLAMP) {
         limit = p.clamp;
-        a_limit = limit * sigmoid_rn(limit); // the activation of a clamped gate
+        a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
     }
     unsigned long long clamped = 0;
 
     for (uint32_t u = wave; u < p.units; u += nwaves) {
-        const uint32_t row = u / p.upr;
-        const uint32_t unit_in_row = u - row * p.upr;
-        const uint32_t step0 = unit_in_row * p.spu;
-        const uint32_t nst = min(p.spu, p.steps_row - step0);
-        const uint4* xg = p.x + (size_t)row * (2u * p.slots);
-        const uint4* xu = xg + p.slots;
-        const float wr = p.w ? p.w[row] : 1.0f;
-
-        uint4 G[SPU], U[SPU];
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            const uint32_t slot = (step0 + s) * kWaveSize + lane;
-            if (s < (int)nst && slot < p.slots) {
-                G[s] = xg[slot];
-                U[s] = xu[slot];
-            } else {
-                G[s] = make_uint4(0, 0, 0, 0);
-                U[s] = make_uint4(0, 0, 0, 0);
-            }
-        }
-
-        float y[SPU][8];
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            const uint32_t gw[4] = {G[s].x, G[s].y, G[s].z, G[s].w};
-            const uint32_t uw[4] = {U[s].x, U[s].y, U[s].z, U[s].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    y[s][2 * k + h] = h ? swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped)
-                                        : swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], wr, limit, a_limit, clamped);
-                }
-            }
-        }
-
-        if constexpr (ROWRED) {
-            float m = 0.0f;
-#pragma unroll
-            for (int s = 0; s < SPU; ++s)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    m = fmaxf(m, fabsf(y[s][j]));
-            const float amax = wave_max(m);
-            float s32 = 0.0f;
-            uint32_t s8 = 0;
-            const float inv = group_scale<FMT, SFMT>(amax, s32, s8);
-#pragma unroll
-            for (int s = 0; s < SPU; ++s) {
-                const uint32_t slot = (step0 + s) * kWaveSize + lane;
-                if (s < (int)nst && slot < p.slots) {
-                    float q[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        q[j] = y[s][j] * inv;
-                    store_codes<FMT>(p, row, slot, q);
-                }
-            }
-            if (lane == 0)
-                store_scale<SFMT>(p, (size_t)row * p.groups_row + unit_in_row, s32, s8);
-        } else {
-#pragma unroll
-            for (int s = 0; s < SPU; ++s) {
-                if (s < (int)nst) {
-                    float m = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        m = fmaxf(m, fabsf(y[s][j]));
-                    const float amax = group_max(m, p.gl_log2);
-                    float s32 = 0.0f;
-                    uint32_t s8 = 0;
-                    const float inv = group_scale<FMT, SFMT>(amax, s32, s8);
-                    const uint32_t slot = (step0 + s) * kWaveSize + lane;
-                    if (slot < p.slots) {
-                        float q[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            q[j] = y[s][j] * inv;
-                        store_codes<FMT>(p, row, slot, q);
-                        if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
-                            store_scale<SFMT>(p, (size_t)row * p.groups_row + (slot >> p.gl_log2), s32, s8);
-                    }
-                }
-            }
-        }
+        Unit<SPU> d;
+        load_unit<SPU, ROWRED, PARTIAL>(p, u, lane, d);
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, d, limit, a_limit, clamped);
     }
 
     if constexpr (CLAMP) {
@@ -408,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_forward_kernel(const uint4* _
                                                                   uint32_t slots, float limit_in,
                                                                   unsigned long long* count)
 {
-    __shared__ float2 lut[kLutSize];
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    LutT* lut = reinterpret_cast<LutT*>(lut_raw);
     load_lut_to_lds(lut);
     float limit = 0.0f, a_limit = 0.0f;
     if constexpr (CLAMP) {
@@ -506,40 +535,47 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn)
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED>
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 void launch_one(const Params& p, int blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED>), dim3(blocks), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads),
+                       0, stream, p);
 }
 
-template <int FMT, int SFMT, bool CLAMP, bool ROWRED>
+template <int FMT, int SFMT, bool CLAMP, bool ROWRED, bool PARTIAL>
 bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
 {
     switch (spu_max) {
-    case 1: launch_one<FMT, SFMT, CLAMP, 1, ROWRED>(p, blocks, stream); return true;
-    case 2: launch_one<FMT, SFMT, CLAMP, 2, ROWRED>(p, blocks, stream); return true;
-    case 4: launch_one<FMT, SFMT, CLAMP, 4, ROWRED>(p, blocks, stream); return true;
-    case 8: launch_one<FMT, SFMT, CLAMP, 8, ROWRED>(p, blocks, stream); return true;
-    case 16: launch_one<FMT, SFMT, CLAMP, 16, ROWRED>(p, blocks, stream); return true;
+    case 1: launch_one<FMT, SFMT, CLAMP, 1, ROWRED, PARTIAL>(p, blocks, stream); return true;
+    case 2: launch_one<FMT, SFMT, CLAMP, 2, ROWRED, PARTIAL>(p, blocks, stream); return true;
+    case 4: launch_one<FMT, SFMT, CLAMP, 4, ROWRED, PARTIAL>(p, blocks, stream); return true;
+    case 8:
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 8, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        return false;
+    case 16:
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 16, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        return false;
     default: return false;
     }
 }
 
 template <int FMT>
-bool dispatch(int sfmt, bool clamp, bool rowred, int spu_max, const Params& p, int blocks, hipStream_t s)
+bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, const Params& p, int blocks,
+              hipStream_t s)
 {
-#define TK_BRANCH(SF, CL, RR)                                                                           \
-    if (sfmt == SF && clamp == CL && rowred == RR)                                                      \
-        return launch_spu<FMT, SF, CL, RR>(spu_max, p, blocks, s);
-    TK_BRANCH(TK_SCALE_FP32, false, false)
-    TK_BRANCH(TK_SCALE_FP32, false, true)
-    TK_BRANCH(TK_SCALE_FP32, true, false)
-    TK_BRANCH(TK_SCALE_FP32, true, true)
-    TK_BRANCH(TK_SCALE_UE8M0, false, false)
-    TK_BRANCH(TK_SCALE_UE8M0, false, true)
-    TK_BRANCH(TK_SCALE_UE8M0, true, false)
-    TK_BRANCH(TK_SCALE_UE8M0, true, true)
+#define TK_BRANCH(SF, CL, RR, PA)                                                                       \
+    if (sfmt == SF && clamp == CL && rowred == RR && partial == PA)                                     \
+        return launch_spu<FMT, SF, CL, RR, PA>(spu_max, p, blocks, s);
+#define TK_BRANCH2(SF, CL, RR) TK_BRANCH(SF, CL, RR, false) TK_BRANCH(SF, CL, RR, true)
+    TK_BRANCH2(TK_SCALE_FP32, false, false)
+    TK_BRANCH2(TK_SCALE_FP32, false, true)
+    TK_BRANCH2(TK_SCALE_FP32, true, false)
+    TK_BRANCH2(TK_SCALE_FP32, true, true)
+    TK_BRANCH2(TK_SCALE_UE8M0, false, false)
+    TK_BRANCH2(TK_SCALE_UE8M0, false, true)
+    TK_BRANCH2(TK_SCALE_UE8M0, true, false)
+    TK_BRANCH2(TK_SCALE_UE8M0, true, true)
+#undef TK_BRANCH2
 #undef TK_BRANCH
     return false;
 }
@@ -552,7 +588,7 @@ uint32_t pow2_at_least(uint32_t v)
     return p;
 }
 
-constexpr int kBlocksPerCU = 4;
+constexpr int kBlocksPerCU = 2; // workgroups of 256 threads per CU in the persistent grid
 
 tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t hidden, int64_t group_size,
                       float clamp_limit, int scale_fmt, void* codes, void* scales, int64_t* clamped_count,
@@ -605,11 +641,13 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
         rowred = false;
         p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
-        spu_max = steps_row >= 4 && n >= 1024 ? 4u : (steps_row >= 2 && n >= 256 ? 2u : 1u);
-        if (spu_max > steps_row)
-            spu_max = pow2_at_least(steps_row);
-        p.spu = spu_max;
-        p.upr = (steps_row + p.spu - 1) / p.spu;
+        // steps per unit: a power of two up to 4 that divides the row's steps
+        uint32_t spu = n >= 1024 ? 4u : (n >= 256 ? 2u : 1u);
+        while (steps_row % spu)
+            spu >>= 1;
+        spu_max = spu;
+        p.spu = spu;
+        p.upr = steps_row / spu;
     } else if (gslots % kWaveSize == 0) {
         const uint32_t k = gslots / kWaveSize;
         if (k > (uint32_t)kMaxStepsPerUnit)
@@ -649,10 +687,11 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
     const uint32_t cap = (uint32_t)g_dev[dev].cus * kBlocksPerCU;
     const int blocks = (int)(want < cap ? want : cap);
+    const bool partial = (slots % kWaveSize) != 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool ok = fmt == 8 ? dispatch<8>(scale_fmt, clamp, rowred, (int)spu_max, p, blocks, s)
-                             : dispatch<4>(scale_fmt, clamp, rowred, (int)spu_max, p, blocks, s);
+    const bool ok = fmt == 8 ? dispatch<8>(scale_fmt, clamp, rowred, partial, (int)spu_max, p, blocks, s)
+                             : dispatch<4>(scale_fmt, clamp, rowred, partial, (int)spu_max, p, blocks, s);
     if (!ok)
         return TK_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess)
