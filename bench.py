@@ -34,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
-KERNEL_SOURCE = os.path.join(ROOT, "moe_activation_bit_amd", "csrc", "tk_swiglu_cast.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_activation_bit_amd", "csrc", f)
+                  for f in ("tk_swiglu_cast.hip", "tk_quant.h")]
 
 
 def log(*a):
@@ -42,7 +43,10 @@ def log(*a):
 
 
 def kernel_source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload: str, launches_bytes: float):
@@ -115,6 +119,42 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+
+
+def unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, reps, stream, fused_s):
+    """The unfused reference of the same step (swiglu_forward writes fp32 y to
+    HBM, then the stand-alone cast reads it), timed like the fused step; its
+    effective bandwidth counts the same algorithmic bytes."""
+    y = [torch.empty((n, w.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
+    cast = tk.tk_cast_fp8 if fmt == 8 else tk.tk_cast_fp4
+    sh = int(stream.cuda_stream)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        yy = y[i % 2]
+        rc = tk.tk_swiglu_forward(s["x"], s["w"], n, w.hidden, clamp, yy,
+                                  s["count"] if w.clamp_limit is not None else None, sh)
+        assert rc == tk.TkStatus.TK_OK, rc
+        rc = cast(yy, tk.TK_DTYPE_FP32, n, w.hidden, w.group_size, sfmt, s["codes"], s["scales"], sh)
+        assert rc == tk.TkStatus.TK_OK, rc
+
+    for i in range(3):
+        step(i)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(reps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) / 1e3 / reps
+    del y
+    torch.cuda.empty_cache()
+    return {"us_per_step": round(t * 1e6, 3),
+            "effective_GBs": round(w.algorithmic_bytes(n) / t / 1e9, 1),
+            "hbm_bytes_per_step": w.algorithmic_bytes(n) + 2 * 4 * w.hidden * n,
+            "fused_speedup": round(t / fused_s, 3),
+            "kernels": "tk_swiglu_forward (fp32 y out) + tk_cast (fp32 y in)"}
 
 
 def stream_ceiling(torch, dev, in_bytes: int, reps: int = 30):
@@ -203,6 +243,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling measurement")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused two-kernel comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -318,6 +359,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_unfused:
+        log("[bench] unfused two-kernel path ...")
+        out["unfused"] = unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, args.steps // 4 or 1, stream,
+                                      avg_launch_s)
     if not args.no_ceiling:
         log("[bench] streaming ceiling ...")
         ceil = stream_ceiling(torch, dev, 4 * w.hidden * n)

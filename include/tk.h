@@ -54,10 +54,33 @@
 extern "C" {
 #endif
 
+/*
+ * Scale format and layout.  n = rows, G = groups per row (hidden / group size,
+ * 1 per-token).  The column-major and packed layouts are the "TMA-aligned
+ * column-major" scale storage and the "UE8M0 packed" scale compression named in
+ * "TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式" "3. Quantization", laid out
+ * for a GEMM that reads one group's scales for consecutive rows:
+ *   TK_SCALE_FP32            fp32  [n][G] row-major
+ *   TK_SCALE_UE8M0           uint8 [n][G] row-major
+ *   TK_SCALE_FP32_COLMAJOR   fp32  [G][ld], ld = n rounded up to 4; element (r, k) at k*ld + r
+ *   TK_SCALE_UE8M0_COLMAJOR  uint8 [G][ld], ld = n rounded up to 16; element (r, k) at k*ld + r
+ *   TK_SCALE_UE8M0_PACKED    uint32 [ceil(G/4)][ld], ld = n rounded up to 4; word (j, r) holds the
+ *                            bytes of groups 4j..4j+3 of row r, group 4j in the low byte
+ * Column-major and packed buffers must be 16-byte aligned; rows r >= n of a
+ * column and bytes of groups k >= G of the last packed word are not written.
+ */
 typedef enum {
-    TK_SCALE_FP32 = 0,  /* one fp32 per group */
-    TK_SCALE_UE8M0 = 1  /* one byte per group: biased exponent of a power of two */
+    TK_SCALE_FP32 = 0,
+    TK_SCALE_UE8M0 = 1,
+    TK_SCALE_FP32_COLMAJOR = 2,
+    TK_SCALE_UE8M0_COLMAJOR = 3,
+    TK_SCALE_UE8M0_PACKED = 4
 } tk_scale_fmt;
+
+typedef enum {
+    TK_DTYPE_BF16 = 0,  /* bf16 elements (2 bytes) */
+    TK_DTYPE_FP32 = 1   /* fp32 elements (4 bytes) */
+} tk_dtype;
 
 typedef enum {
     TK_OK = 0,
@@ -89,10 +112,11 @@ tk_status tk_init(int device);
  *                column group with its own scale: a multiple of 8 dividing
  *                hidden.
  *  clamp_limit   L > 0; +INFINITY disables the clamp (the count is then 0).
- *  scale_fmt     TK_SCALE_FP32 or TK_SCALE_UE8M0.
+ *  scale_fmt     a tk_scale_fmt value (value kind and layout).
  *  codes         uint8 [n, hidden], E4M3 codes, 8-byte aligned.
- *  scales        [n, hidden/G] row-major (G = hidden when group_size == 0):
- *                fp32 (4-byte aligned) or uint8 UE8M0 bytes.
+ *  scales        one scale per group in the tk_scale_fmt layout (G = 1 when
+ *                group_size == 0): row-major fp32 (4-byte aligned) or uint8,
+ *                or a 16-byte aligned column-major / packed layout.
  *  clamped_count int64 on the device, or NULL.  The number of gate values
  *                strictly above L is ADDED to it (the caller zeroes it).
  *  stream        hipStream_t to launch on.
@@ -133,6 +157,31 @@ tk_status tk_swiglu_cast_fp4(const void* x, const float* topk_weight, int64_t n,
  */
 tk_status tk_swiglu_forward(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
                             float clamp_limit, float* y, int64_t* clamped_count, void* stream);
+
+/*
+ * tk_cast_fp8: the stand-alone cast of rows to FP8 E4M3 codes with per-token
+ * or per-block scales -- TileKernels' per_token_cast ("【DeepSeek】TileKernels从
+ * 入门到精通" ch.1 "透视底层"/"闭环"), and the "cast" of the unfused reference in
+ * ch.5 "越过性能红线".  Per row r and group of G columns:
+ *   amax = max |y|; scale and inv as in tk_swiglu_cast_fp8; code = cast(RN(y*inv))
+ * with y the input value (bf16 widened exactly to fp32, or fp32).  The same
+ * value gets the same code and scale as on the fused path.
+ *
+ *  x          [n, hidden] row-major, in_dtype elements, 16-byte aligned.
+ *  in_dtype   TK_DTYPE_BF16 or TK_DTYPE_FP32.
+ *  n, hidden, group_size, scale_fmt, codes, scales, stream: as
+ *             tk_swiglu_cast_fp8.
+ * Returns TK_ERR_INVALID_ARG for the same conditions as tk_swiglu_cast_fp8
+ * (without weight, clamp and counter) and for an unknown in_dtype;
+ * TK_ERR_UNSUPPORTED for the same group shapes.
+ */
+tk_status tk_cast_fp8(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
+                      tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream);
+
+/* tk_cast_fp4: the stand-alone cast to FP4 E2M1 codes packed two per byte
+ * (element 2i in the low nibble), fmt_max 6.  Otherwise as tk_cast_fp8. */
+tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
+                      tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream);
 
 /* tk_status_str: a static, human-readable name for a status code. */
 const char* tk_status_str(tk_status status);

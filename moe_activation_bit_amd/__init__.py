@@ -20,12 +20,19 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtk.so")
 
 __all__ = [
-    "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "LIB_PATH", "load_library",
-    "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_status_str",
+    "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "TK_SCALE_FP32_COLMAJOR", "TK_SCALE_UE8M0_COLMAJOR",
+    "TK_SCALE_UE8M0_PACKED", "TK_DTYPE_BF16", "TK_DTYPE_FP32", "LIB_PATH", "load_library",
+    "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4",
+    "tk_status_str",
 ]
 
 TK_SCALE_FP32 = 0
 TK_SCALE_UE8M0 = 1
+TK_SCALE_FP32_COLMAJOR = 2
+TK_SCALE_UE8M0_COLMAJOR = 3
+TK_SCALE_UE8M0_PACKED = 4
+TK_DTYPE_BF16 = 0
+TK_DTYPE_FP32 = 1
 
 
 class TkStatus(enum.IntEnum):
@@ -47,6 +54,10 @@ SIGNATURES = {
     "tk_swiglu_cast_fp4": (ctypes.c_int, _CAST_ARGS),
     "tk_swiglu_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_cast_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_cast_fp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -117,6 +128,22 @@ def tk_swiglu_forward(x, topk_weight, n, hidden, clamp_limit, y, clamped_count=N
     rc = load_library().tk_swiglu_forward(_ptr(x), _ptr(topk_weight), int(n), int(hidden), float(clamp_limit),
                                           _ptr(y), _ptr(clamped_count), _stream(stream))
     return TkStatus(rc)
+
+
+def _cast_only(fn_name, x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream) -> TkStatus:
+    fn = getattr(load_library(), fn_name)
+    return TkStatus(fn(_ptr(x), int(in_dtype), int(n), int(hidden), int(group_size), int(scale_fmt), _ptr(codes),
+                       _ptr(scales), _stream(stream)))
+
+
+def tk_cast_fp8(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream=None) -> TkStatus:
+    """See tk_cast_fp8 in include/tk.h."""
+    return _cast_only("tk_cast_fp8", x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream)
+
+
+def tk_cast_fp4(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream=None) -> TkStatus:
+    """See tk_cast_fp4 in include/tk.h."""
+    return _cast_only("tk_cast_fp4", x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream)
 
 
 def tk_status_str(status: int) -> str:

@@ -1,6 +1,6 @@
 """Build the package's native libraries in-tree.
 
-libtk.so    -- the HIP kernels and C ABI (hipcc, gfx950)
+libtk.so    -- the HIP kernels and C ABI (hipcc, gfx950; one object per source)
 libsynth.so -- the seeded input generator (plain C)
 libstreamceil.so -- plain streaming kernels that measure the HBM ceiling
 """
@@ -33,21 +33,36 @@ def _run(cmd):
     return proc.stdout
 
 
+OBJ_DIR = os.path.join(HERE, "_build")
+TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip"]
+
+
+def _hip_object(src):
+    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+    return obj, [HIPCC] + [f for f in HIP_FLAGS if f != "-shared"] + ["-c", "-o", obj, os.path.join(CSRC, src)]
+
+
 def build_commands():
-    return {
-        "libtk.so": [HIPCC] + HIP_FLAGS + ["-o", os.path.join(HERE, "libtk.so"),
-                                           os.path.join(CSRC, "tk_swiglu_cast.hip")],
-        "libstreamceil.so": [HIPCC] + HIP_FLAGS + ["-o", os.path.join(HERE, "libstreamceil.so"),
-                                                   os.path.join(CSRC, "stream_ceiling.hip")],
-        "libsynth.so": ["gcc", "-O2", "-fPIC", "-shared", "-o", os.path.join(HERE, "libsynth.so"),
-                        os.path.join(CSRC, "synth.c"), "-lm"],
-    }
+    """(stage 1 commands that run in parallel, stage 2 link commands)"""
+    objs = [_hip_object(s) for s in TK_SOURCES]
+    stage1 = [cmd for _, cmd in objs] + [
+        [HIPCC] + HIP_FLAGS + ["-o", os.path.join(HERE, "libstreamceil.so"), os.path.join(CSRC, "stream_ceiling.hip")],
+        ["gcc", "-O2", "-fPIC", "-shared", "-o", os.path.join(HERE, "libsynth.so"), os.path.join(CSRC, "synth.c"),
+         "-lm"],
+    ]
+    stage2 = [[HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", os.path.join(HERE, "libtk.so")]
+              + [o for o, _ in objs]]
+    return stage1, stage2
 
 
 def build(extra=None):
-    cmds = list(build_commands().values()) + list(extra or [])
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    stage1, stage2 = build_commands()
+    cmds = stage1 + list(extra or [])
     with ThreadPoolExecutor(len(cmds)) as ex:
         list(ex.map(_run, cmds))
+    for cmd in stage2:
+        _run(cmd)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,215 @@
+// tk_cast.hip -- the stand-alone per-token / per-block cast of bf16 or fp32
+// rows to FP8 E4M3 or FP4 E2M1 codes with fp32 or UE8M0 scales, behind the
+// C ABI in include/tk.h (tk_cast_fp8, tk_cast_fp4).
+//
+// It is the "per_token_cast" of "【DeepSeek】TileKernels从入门到精通" ch.1
+// ("透视底层", "闭环": a dtype/shape-specialised cast kernel with T.dynamic row
+// count and an abs-max reduction) and the "cast" of the unfused reference in
+// ch.5 "越过性能红线" (swiglu_forward, then cast).  The abs-max -> scale ->
+// cast tail is the fused kernel's (tk_quant.h), so a value quantises to the
+// same code on either path.
+//
+// gfx950 layout: as in the fused kernel a wave owns units of 512-column steps;
+// lane l holds the 8 columns of slot 64*step + l (16 bytes of bf16, or 32
+// bytes of fp32 as two 16-byte loads).  No table is needed, so the grid is
+// non-persistent: one unit per wave, which streams fastest on MI355X.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tk.h"
+#include "tk_quant.h"
+
+namespace {
+
+using namespace tk_detail;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_float(w & 0xFFFF0000u); }
+
+template <int FMT, int SFMT, bool F32IN, int SPU, bool ROWRED, bool PARTIAL>
+__global__ __launch_bounds__(kThreads) void cast_kernel(Params p)
+{
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t waves_per_block = kThreads / kWaveSize;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize));
+    const uint32_t nwaves = gridDim.x * waves_per_block;
+    constexpr uint32_t kSlotBytes = F32IN ? 32u : 16u;
+
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t unit_in_row = u - row * p.upr;
+        const uint32_t step0 = unit_in_row * p.spu;
+        const uint32_t nst = ROWRED ? min(p.spu, p.steps_row - step0) : (uint32_t)SPU;
+        const char* xr = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * kSlotBytes);
+        const uint32_t lane_off = (step0 * kWaveSize + lane) * kSlotBytes;
+
+        uint4 raw[SPU][F32IN ? 2 : 1];
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            if (!ROWRED || s < (int)nst) {
+                uint32_t off = lane_off + (uint32_t)s * (kWaveSize * kSlotBytes);
+                if (PARTIAL) // lanes past the row end re-read its last slot
+                    off = min(off, (p.slots - 1u) * kSlotBytes);
+                raw[s][0] = load16(reinterpret_cast<const uint4*>(xr + off));
+                if constexpr (F32IN)
+                    raw[s][F32IN ? 1 : 0] = load16(reinterpret_cast<const uint4*>(xr + off + 16u));
+            }
+        }
+
+        float y[SPU][8];
+        uint32_t mbits[SPU];
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            if (!ROWRED || s < (int)nst) {
+                if constexpr (F32IN) {
+                    const uint4 a = raw[s][0], b = raw[s][F32IN ? 1 : 0];
+                    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        y[s][j] = as_float(w[j]);
+                } else {
+                    const uint32_t w[4] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        y[s][2 * k] = bf16_lo(w[k]);
+                        y[s][2 * k + 1] = bf16_hi(w[k]);
+                    }
+                }
+                float m = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; j += 2)
+                    m = fmaxf(m, fmaxf(fabsf(y[s][j]), fabsf(y[s][j + 1])));
+                if (PARTIAL && (step0 + s) * kWaveSize + lane >= p.slots)
+                    m = 0.0f;
+                mbits[s] = as_uint(m);
+            }
+        }
+        quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mbits);
+    }
+}
+
+template <int FMT, int SFMT, bool F32IN, bool ROWRED, bool PARTIAL>
+bool launch_cast(int spu_max, const Params& p, int blocks, hipStream_t s)
+{
+#define TK_CAST_CASE(N)                                                                                 \
+    case N:                                                                                             \
+        hipLaunchKernelGGL((cast_kernel<FMT, SFMT, F32IN, N, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads), \
+                           0, s, p);                                                                    \
+        return true;
+    switch (spu_max) {
+        TK_CAST_CASE(1)
+        TK_CAST_CASE(2)
+        TK_CAST_CASE(4)
+    case 8:
+        if constexpr (ROWRED) {
+            hipLaunchKernelGGL((cast_kernel<FMT, SFMT, F32IN, 8, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads), 0,
+                               s, p);
+            return true;
+        }
+        return false;
+    case 16:
+        if constexpr (ROWRED) {
+            hipLaunchKernelGGL((cast_kernel<FMT, SFMT, F32IN, 16, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads),
+                               0, s, p);
+            return true;
+        }
+        return false;
+    default:
+        return false;
+    }
+#undef TK_CAST_CASE
+}
+
+template <int FMT, int SFMT, bool F32IN>
+bool dispatch_cast2(const UnitPlan& plan, const Params& p, int blocks, hipStream_t s)
+{
+    const int spu = (int)plan.spu_max;
+    if (plan.rowred)
+        return plan.partial ? launch_cast<FMT, SFMT, F32IN, true, true>(spu, p, blocks, s)
+                            : launch_cast<FMT, SFMT, F32IN, true, false>(spu, p, blocks, s);
+    return plan.partial ? launch_cast<FMT, SFMT, F32IN, false, true>(spu, p, blocks, s)
+                        : launch_cast<FMT, SFMT, F32IN, false, false>(spu, p, blocks, s);
+}
+
+template <int FMT>
+bool dispatch_cast(int sfmt, bool f32in, const UnitPlan& plan, const Params& p, int blocks, hipStream_t s)
+{
+    if (sfmt == TK_SCALE_FP32)
+        return f32in ? dispatch_cast2<FMT, TK_SCALE_FP32, true>(plan, p, blocks, s)
+                     : dispatch_cast2<FMT, TK_SCALE_FP32, false>(plan, p, blocks, s);
+    return f32in ? dispatch_cast2<FMT, TK_SCALE_UE8M0, true>(plan, p, blocks, s)
+                 : dispatch_cast2<FMT, TK_SCALE_UE8M0, false>(plan, p, blocks, s);
+}
+
+tk_status cast(int fmt, const void* x, int in_dtype, int64_t n, int64_t hidden, int64_t group_size, int scale_fmt,
+               void* codes, void* scales, void* stream)
+{
+    // ---- validation: no HIP call before every argument is checked ----
+    if (n < 0 || n >= (int64_t)INT_MAX)
+        return TK_ERR_INVALID_ARG;
+    if (hidden <= 0 || hidden % kSlotCols != 0 || hidden > (int64_t)INT_MAX / 8)
+        return TK_ERR_INVALID_ARG;
+    if (group_size < 0 || (group_size != 0 && (group_size % kSlotCols != 0 || hidden % group_size != 0)))
+        return TK_ERR_INVALID_ARG;
+    if (in_dtype != TK_DTYPE_BF16 && in_dtype != TK_DTYPE_FP32)
+        return TK_ERR_INVALID_ARG;
+    const int64_t groups_row = hidden / (group_size ? group_size : hidden);
+    ScaleSpec sp;
+    if (!scale_spec(scale_fmt, n, groups_row, sp))
+        return TK_ERR_INVALID_ARG;
+    if (n > 0 && (!x || !codes || !scales))
+        return TK_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(codes, fmt == 8 ? 8 : 4) || !aligned(scales, sp.align))
+        return TK_ERR_INVALID_ARG;
+    const size_t x_bytes = (size_t)n * (size_t)hidden * (in_dtype == TK_DTYPE_FP32 ? 4u : 2u);
+    const size_t c_bytes = (size_t)n * (size_t)(fmt == 8 ? hidden : hidden / 2);
+    const size_t s_bytes = sp.bytes;
+    if (n > 0 && (overlaps(codes, c_bytes, x, x_bytes) || overlaps(scales, s_bytes, x, x_bytes) ||
+                  overlaps(codes, c_bytes, scales, s_bytes)))
+        return TK_ERR_INVALID_ARG;
+
+    Params p{};
+    UnitPlan plan;
+    {
+        const tk_status rc = plan_units(n, hidden, group_size, n >= 1024 ? 4u : (n >= 256 ? 2u : 1u), p, plan);
+        if (rc != TK_OK)
+            return rc;
+    }
+    if (n == 0)
+        return TK_OK;
+    p.x = static_cast<const uint4*>(x);
+    p.codes = static_cast<uint8_t*>(codes);
+    p.scales = scales;
+    p.scale_layout = sp.layout;
+    p.scale_ld = sp.ld;
+
+    const uint32_t waves_per_block = kThreads / kWaveSize;
+    const int blocks = (int)((p.units + waves_per_block - 1) / waves_per_block); // one unit per wave
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool f32in = in_dtype == TK_DTYPE_FP32;
+    const bool ok = fmt == 8 ? dispatch_cast<8>(sp.kind, f32in, plan, p, blocks, s)
+                             : dispatch_cast<4>(sp.kind, f32in, plan, p, blocks, s);
+    if (!ok)
+        return TK_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+tk_status tk_cast_fp8(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
+                      tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream)
+{
+    return cast(8, x, (int)in_dtype, n, hidden, group_size, (int)scale_fmt, codes, scales, stream);
+}
+
+tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
+                      tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream)
+{
+    return cast(4, x, (int)in_dtype, n, hidden, group_size, (int)scale_fmt, codes, scales, stream);
+}
+
+} // extern "C"

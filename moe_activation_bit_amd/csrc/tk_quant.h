@@ -1,0 +1,342 @@
+// tk_quant.h -- device and host pieces shared by the fused SwiGLU + cast
+// kernels (tk_swiglu_cast.hip) and the stand-alone cast (tk_cast.hip): the
+// launch parameters, the wave/group abs-max reductions, the scale of a group
+// and the quantise-and-store tail.  The operation they implement is the
+// abs-max -> scale factor -> FP8/FP4 step of "【DeepSeek】TileKernels从入门到精通"
+// ch.2 "算子融合的“三重境界”" (step 3) with the formats of "TileLang +
+// TileKernels：DeepSeek 的 GPU 内核开发新范式" "3. Quantization".
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cstdint>
+
+#include "tk.h"
+
+namespace tk_detail {
+
+constexpr int kWaveSize = 64;
+constexpr int kSlotCols = 8;                     // columns per lane per step (16 B of bf16)
+constexpr int kMaxStepsPerUnit = 16;             // largest row-reduced group: 8192 columns
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+struct Params {
+    const uint4* x;         // [n][2*slots] 16-byte lane slots (gate slots, then up slots)
+    const float* w;         // [n] or null
+    uint8_t* codes;         // fp8: [n][hidden]; fp4: [n][hidden/2]
+    void* scales;           // [n][groups_row], fp32 or uint8
+    unsigned long long* count;
+    uint32_t slots;         // hidden / 8
+    uint32_t steps_row;     // ceil(slots / 64)
+    uint32_t upr;           // units per row
+    uint32_t spu;           // steps per unit (<= SPU)
+    uint32_t units;         // n * upr
+    uint32_t gl_log2;       // per-block: lanes per group = 1 << gl_log2
+    uint32_t groups_row;    // scales per row
+    float clamp;            // L (clamp variants)
+    uint32_t scale_layout;  // kScaleRowMajor, kScaleColMajor or kScalePacked
+    uint32_t scale_ld;      // column-major / packed: elements between consecutive groups' columns
+};
+
+// Scale layouts (the value kind -- fp32 or UE8M0 byte -- is the SFMT template):
+//   row-major [n][groups];  column-major [groups][ld] (ld >= n, 16-byte
+//   aligned columns);  packed [ceil(groups/4)][ld] 32-bit words holding the
+//   UE8M0 bytes of groups 4j..4j+3 of one row, lowest group in the low byte.
+constexpr uint32_t kScaleRowMajor = 0;
+constexpr uint32_t kScaleColMajor = 1;
+constexpr uint32_t kScalePacked = 2;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// Abs-max reductions run on the bit patterns of non-negative floats, whose
+// unsigned order is their numeric order; umax with identity 0 folds into a
+// single v_max_u32_dpp per butterfly step.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+// max over the 2^gl_log2 consecutive lanes of each group (all lanes active)
+__device__ __forceinline__ uint32_t group_umax(uint32_t v, uint32_t gl_log2)
+{
+    if (gl_log2 >= 1) v = dpp_umax<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    if (gl_log2 >= 2) v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if (gl_log2 >= 3) v = dpp_umax<0x141>(v); // row_half_mirror: quads of 8 lanes
+    if (gl_log2 >= 4) v = dpp_umax<0x140>(v); // row_mirror: halves of 16 lanes
+    if (gl_log2 >= 5) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    if (gl_log2 >= 6) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
+{
+    v = dpp_umax<0xB1>(v);
+    v = dpp_umax<0x4E>(v);
+    v = dpp_umax<0x141>(v);
+    v = dpp_umax<0x140>(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+template <int FMT>
+struct FmtTraits;
+template <>
+struct FmtTraits<8> {
+    static constexpr float kMax = 448.0f;         // 1.75 * 2^8
+    static constexpr int kExpBias = 127 + 8;      // biased exponent of 448
+    static constexpr uint32_t kMant = 0x600000u;  // mantissa field of 1.75
+};
+template <>
+struct FmtTraits<4> {
+    static constexpr float kMax = 6.0f;           // 1.5 * 2^2
+    static constexpr int kExpBias = 127 + 2;
+    static constexpr uint32_t kMant = 0x400000u;  // mantissa field of 1.5
+};
+
+// Scale of one group from the bit pattern of its abs-max.  Returns the
+// multiplier applied before the cast (2^-k for UE8M0) and writes the stored
+// scale representation.
+template <int FMT, int SFMT>
+__device__ __forceinline__ float group_scale(uint32_t amax_bits, float& scale_f32, uint32_t& scale_u8)
+{
+    using T = FmtTraits<FMT>;
+    if constexpr (SFMT == TK_SCALE_FP32) {
+        const float amax = as_float(amax_bits);
+        scale_f32 = amax / T::kMax;                   // IEEE division, round to nearest even
+        return fminf(T::kMax / amax, FLT_MAX);        // amax == 0 -> +inf -> FLT_MAX
+    } else {
+        // smallest k with fmt_max * 2^k >= amax: compare amax = 1.M * 2^(E-127)
+        // with fmt_max = 1.F * 2^P; k = E - 127 - P + (M > F), at least -127.
+        int k = (int)(amax_bits >> 23) - T::kExpBias + ((amax_bits & 0x7FFFFFu) > T::kMant ? 1 : 0);
+        k = max(k, -127);
+        scale_u8 = (uint32_t)(k + 127);
+        return as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
+    }
+}
+
+// q = RN(y * inv), cast, and one non-temporal store of the lane's 8 codes.
+template <int FMT>
+__device__ __forceinline__ void quantize_store(uint8_t* row_codes, uint32_t slot, const float* y, float inv)
+{
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        q[j] = y[j] * inv;
+    if constexpr (FMT == 8) {
+        uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+        uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+        const v2u v = {lo, hi};
+        __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(row_codes) + slot);
+    } else {
+        uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[2], q[3], 1.0f, 1);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[4], q[5], 1.0f, 2);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[6], q[7], 1.0f, 3);
+        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(row_codes) + slot);
+    }
+}
+
+// Store the scale of group k of row `row` in the requested layout.
+template <int SFMT>
+__device__ __forceinline__ void store_scale(const Params& p, uint32_t row, uint32_t k, float s32, uint32_t s8)
+{
+    size_t idx;
+    if (p.scale_layout == kScaleRowMajor)
+        idx = (size_t)row * p.groups_row + k;
+    else if (p.scale_layout == kScaleColMajor)
+        idx = (size_t)k * p.scale_ld + row;
+    else // packed: byte (k & 3) of word (k >> 2, row)
+        idx = ((size_t)(k >> 2) * p.scale_ld + row) * 4u + (k & 3u);
+    if constexpr (SFMT == TK_SCALE_FP32)
+        static_cast<float*>(p.scales)[idx] = s32;
+    else
+        static_cast<uint8_t*>(p.scales)[idx] = (uint8_t)s8;
+}
+
+constexpr int kThreads = 256;
+
+// Streaming 16-byte load, marked non-temporal: the input is read exactly once.
+__device__ __forceinline__ uint4 load16(const uint4* p)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The data of one unit held in registers between its load and its use.
+
+// The quantisation tail of one unit: y[s][j] are the unit's fp32 values (step
+// s, element j of the lane's 8-column slot), mbits[s] the lane-local abs-max of
+// step s as a bit pattern (0 for lanes past the row end).  Writes codes and
+// scales.  Per-block mode (ROWRED false): groups are 2^gl_log2 lanes of one
+// step; row mode: the whole unit is one group (per-token, or a 512k-column
+// group).
+template <int FMT, int SFMT, int SPU, bool ROWRED, bool PARTIAL>
+__device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, uint32_t row, uint32_t unit_in_row,
+                                              uint32_t step0, uint32_t nst, const float (&y)[SPU][8],
+                                              const uint32_t (&mbits)[SPU])
+{
+    uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+    if constexpr (ROWRED) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int s = 0; s < SPU; ++s)
+            if (s < (int)nst)
+                mb = max(mb, mbits[s]);
+        mb = wave_umax(mb);
+        float s32 = 0.0f;
+        uint32_t s8 = 0;
+        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            if (s < (int)nst) {
+                const uint32_t slot = (step0 + s) * kWaveSize + lane;
+                if (!PARTIAL || slot < p.slots)
+                    quantize_store<FMT>(row_codes, slot, y[s], inv);
+            }
+        }
+        if (lane == 0)
+            store_scale<SFMT>(p, row, unit_in_row, s32, s8);
+    } else {
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+            const uint32_t mb = group_umax(mbits[s], p.gl_log2);
+            float s32 = 0.0f;
+            uint32_t s8 = 0;
+            const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+            const uint32_t slot = (step0 + s) * kWaveSize + lane;
+            if (!PARTIAL || slot < p.slots) {
+                quantize_store<FMT>(row_codes, slot, y[s], inv);
+                if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
+                    store_scale<SFMT>(p, row, slot >> p.gl_log2, s32, s8);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host helpers
+// ---------------------------------------------------------------------------
+inline bool overlaps(const void* a, size_t an, const void* b, size_t bn)
+{
+    if (!a || !b || an == 0 || bn == 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline uint32_t pow2_at_least(uint32_t v)
+{
+    uint32_t p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+// A tk_scale_fmt value split into the value kind (TK_SCALE_FP32 or
+// TK_SCALE_UE8M0), the layout and its leading dimension, and the bytes the
+// scale tensor spans.  Returns false for an unknown format.
+struct ScaleSpec {
+    int kind = TK_SCALE_FP32;
+    uint32_t layout = kScaleRowMajor;
+    uint32_t ld = 0;
+    size_t bytes = 0;
+    uintptr_t align = 1;
+};
+
+inline bool scale_spec(int scale_fmt, int64_t n, int64_t groups, ScaleSpec& sp)
+{
+    const auto round_up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
+    switch (scale_fmt) {
+    case TK_SCALE_FP32:
+        sp = {TK_SCALE_FP32, kScaleRowMajor, 0, (size_t)(n * groups) * 4u, 4};
+        return true;
+    case TK_SCALE_UE8M0:
+        sp = {TK_SCALE_UE8M0, kScaleRowMajor, 0, (size_t)(n * groups), 1};
+        return true;
+    case TK_SCALE_FP32_COLMAJOR: {
+        const int64_t ld = round_up(n, 4);
+        sp = {TK_SCALE_FP32, kScaleColMajor, (uint32_t)ld, (size_t)(groups * ld) * 4u, 16};
+        return true;
+    }
+    case TK_SCALE_UE8M0_COLMAJOR: {
+        const int64_t ld = round_up(n, 16);
+        sp = {TK_SCALE_UE8M0, kScaleColMajor, (uint32_t)ld, (size_t)(groups * ld), 16};
+        return true;
+    }
+    case TK_SCALE_UE8M0_PACKED: {
+        const int64_t ld = round_up(n, 4);
+        sp = {TK_SCALE_UE8M0, kScalePacked, (uint32_t)ld, (size_t)((groups + 3) / 4 * ld) * 4u, 16};
+        return true;
+    }
+    default:
+        return false;
+    }
+}
+
+// How a [n, hidden] row set is cut into units for a group size G (0 = the
+// whole row).  Fills p.spu, p.upr, p.gl_log2, p.slots, p.steps_row, p.units,
+// p.groups_row.  Returns TK_ERR_UNSUPPORTED for groups the kernels do not
+// cover.  spu_pref: preferred steps per unit for per-block groups (a power of
+// two up to 4; reduced until it divides the row's steps).
+struct UnitPlan {
+    bool rowred = false;
+    bool partial = false;
+    uint32_t spu_max = 1; // the kernel's compile-time steps per unit
+};
+
+inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint32_t spu_pref, Params& p,
+                            UnitPlan& plan)
+{
+    const int64_t G = group_size ? group_size : hidden;
+    const uint32_t slots = (uint32_t)(hidden / kSlotCols);
+    const uint32_t steps_row = (slots + kWaveSize - 1) / kWaveSize;
+    const uint32_t gslots = (uint32_t)(G / kSlotCols);
+    if (G == hidden) {
+        if (steps_row > (uint32_t)kMaxStepsPerUnit)
+            return TK_ERR_UNSUPPORTED;
+        plan.rowred = true;
+        p.spu = steps_row;
+        p.upr = 1;
+        plan.spu_max = pow2_at_least(steps_row);
+    } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
+        plan.rowred = false;
+        p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
+        uint32_t spu = spu_pref;
+        while (steps_row % spu)
+            spu >>= 1;
+        plan.spu_max = spu;
+        p.spu = spu;
+        p.upr = steps_row / spu;
+    } else if (gslots % kWaveSize == 0) {
+        const uint32_t k = gslots / kWaveSize;
+        if (k > (uint32_t)kMaxStepsPerUnit)
+            return TK_ERR_UNSUPPORTED;
+        plan.rowred = true;
+        p.spu = k;
+        p.upr = (uint32_t)(hidden / G);
+        plan.spu_max = pow2_at_least(k);
+    } else {
+        return TK_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)n * p.upr >= (uint64_t)INT_MAX)
+        return TK_ERR_UNSUPPORTED;
+    p.slots = slots;
+    p.steps_row = steps_row;
+    p.units = (uint32_t)(n * p.upr);
+    p.groups_row = (uint32_t)(hidden / G);
+    plan.partial = (slots % kWaveSize) != 0;
+    return TK_OK;
+}
+
+} // namespace tk_detail

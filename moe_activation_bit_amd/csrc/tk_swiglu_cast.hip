@@ -43,12 +43,11 @@
 #include <mutex>
 
 #include "tk.h"
+#include "tk_quant.h"
 
 namespace {
 
-constexpr int kWaveSize = 64;
-constexpr int kSlotCols = 8;                     // columns per lane per step (16 B of bf16)
-constexpr int kMaxStepsPerUnit = 16;             // largest row-reduced group: 8192 columns
+using namespace tk_detail;
 
 // Sigmoid table: magnitudes m of bf16 bit patterns in [kLutFirst, kLutFirst+kLutSize),
 // one (sigma(+g), sigma(-g)) pair per magnitude.  Below 2^-25 sigma rounds to
@@ -60,9 +59,6 @@ constexpr int kLutSize = 4096;
 static_assert(kLutLast - kLutFirst + 1 == kLutSize, "table span");
 
 __device__ float2 g_sigma_lut[kLutSize];
-
-__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
-__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // ---------------------------------------------------------------------------
 // Correctly rounded fp32 sigmoid for table set-up and for the clamp limit.
@@ -124,57 +120,6 @@ __global__ void sigma_lut_init_kernel()
 // ---------------------------------------------------------------------------
 // Kernel
 // ---------------------------------------------------------------------------
-struct Params {
-    const uint4* x;         // [n][2*slots] 16-byte lane slots (gate slots, then up slots)
-    const float* w;         // [n] or null
-    uint8_t* codes;         // fp8: [n][hidden]; fp4: [n][hidden/2]
-    void* scales;           // [n][groups_row], fp32 or uint8
-    unsigned long long* count;
-    uint32_t slots;         // hidden / 8
-    uint32_t steps_row;     // ceil(slots / 64)
-    uint32_t upr;           // units per row
-    uint32_t spu;           // steps per unit (<= SPU)
-    uint32_t units;         // n * upr
-    uint32_t gl_log2;       // per-block: lanes per group = 1 << gl_log2
-    uint32_t groups_row;    // scales per row
-    float clamp;            // L (clamp variants)
-};
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-
-// Abs-max reductions run on the bit patterns of non-negative floats, whose
-// unsigned order is their numeric order; umax with identity 0 folds into a
-// single v_max_u32_dpp per butterfly step.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v)
-{
-    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
-}
-
-// max over the 2^gl_log2 consecutive lanes of each group (all lanes active)
-__device__ __forceinline__ uint32_t group_umax(uint32_t v, uint32_t gl_log2)
-{
-    if (gl_log2 >= 1) v = dpp_umax<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
-    if (gl_log2 >= 2) v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-    if (gl_log2 >= 3) v = dpp_umax<0x141>(v); // row_half_mirror: quads of 8 lanes
-    if (gl_log2 >= 4) v = dpp_umax<0x140>(v); // row_mirror: halves of 16 lanes
-    if (gl_log2 >= 5) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
-    if (gl_log2 >= 6) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
-{
-    v = dpp_umax<0xB1>(v);
-    v = dpp_umax<0x4E>(v);
-    v = dpp_umax<0x141>(v);
-    v = dpp_umax<0x140>(v);
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
-}
-
 typedef float2 LutT;
 __device__ __forceinline__ void load_lut_to_lds(float2* lut)
 {
@@ -220,85 +165,6 @@ __device__ __forceinline__ float swiglu_elem(const LutT* lut, uint32_t gword, ui
     return b * w;
 }
 
-template <int FMT>
-struct FmtTraits;
-template <>
-struct FmtTraits<8> {
-    static constexpr float kMax = 448.0f;         // 1.75 * 2^8
-    static constexpr int kExpBias = 127 + 8;      // biased exponent of 448
-    static constexpr uint32_t kMant = 0x600000u;  // mantissa field of 1.75
-};
-template <>
-struct FmtTraits<4> {
-    static constexpr float kMax = 6.0f;           // 1.5 * 2^2
-    static constexpr int kExpBias = 127 + 2;
-    static constexpr uint32_t kMant = 0x400000u;  // mantissa field of 1.5
-};
-
-// Scale of one group from the bit pattern of its abs-max.  Returns the
-// multiplier applied before the cast (2^-k for UE8M0) and writes the stored
-// scale representation.
-template <int FMT, int SFMT>
-__device__ __forceinline__ float group_scale(uint32_t amax_bits, float& scale_f32, uint32_t& scale_u8)
-{
-    using T = FmtTraits<FMT>;
-    if constexpr (SFMT == TK_SCALE_FP32) {
-        const float amax = as_float(amax_bits);
-        scale_f32 = amax / T::kMax;                   // IEEE division, round to nearest even
-        return fminf(T::kMax / amax, FLT_MAX);        // amax == 0 -> +inf -> FLT_MAX
-    } else {
-        // smallest k with fmt_max * 2^k >= amax: compare amax = 1.M * 2^(E-127)
-        // with fmt_max = 1.F * 2^P; k = E - 127 - P + (M > F), at least -127.
-        int k = (int)(amax_bits >> 23) - T::kExpBias + ((amax_bits & 0x7FFFFFu) > T::kMant ? 1 : 0);
-        k = max(k, -127);
-        scale_u8 = (uint32_t)(k + 127);
-        return as_float((uint32_t)(127 - k) << 23);   // 2^-k, exact
-    }
-}
-
-// q = RN(y * inv), cast, and one non-temporal store of the lane's 8 codes.
-template <int FMT>
-__device__ __forceinline__ void quantize_store(uint8_t* row_codes, uint32_t slot, const float* y, float inv)
-{
-    float q[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        q[j] = y[j] * inv;
-    if constexpr (FMT == 8) {
-        uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-        uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
-        const v2u v = {lo, hi};
-        __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(row_codes) + slot);
-    } else {
-        uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[2], q[3], 1.0f, 1);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[4], q[5], 1.0f, 2);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[6], q[7], 1.0f, 3);
-        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(row_codes) + slot);
-    }
-}
-
-template <int SFMT>
-__device__ __forceinline__ void store_scale(const Params& p, size_t idx, float s32, uint32_t s8)
-{
-    if constexpr (SFMT == TK_SCALE_FP32)
-        static_cast<float*>(p.scales)[idx] = s32;
-    else
-        static_cast<uint8_t*>(p.scales)[idx] = (uint8_t)s8;
-}
-
-constexpr int kThreads = 256;
-
-// Streaming 16-byte load, marked non-temporal: the input is read exactly once.
-__device__ __forceinline__ uint4 load16(const uint4* p)
-{
-    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// The data of one unit held in registers between its load and its use.
 template <int SPU>
 struct Unit {
     uint4 g[SPU], u[SPU];
@@ -354,42 +220,7 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
             mbits[s] = as_uint(m);
         }
     }
-    uint8_t* row_codes = p.codes + (size_t)d.row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
-    if constexpr (ROWRED) {
-        uint32_t mb = 0;
-#pragma unroll
-        for (int s = 0; s < SPU; ++s)
-            if (s < (int)d.nst)
-                mb = max(mb, mbits[s]);
-        mb = wave_umax(mb);
-        float s32 = 0.0f;
-        uint32_t s8 = 0;
-        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            if (s < (int)d.nst) {
-                const uint32_t slot = (d.step0 + s) * kWaveSize + lane;
-                if (!PARTIAL || slot < p.slots)
-                    quantize_store<FMT>(row_codes, slot, y[s], inv);
-            }
-        }
-        if (lane == 0)
-            store_scale<SFMT>(p, (size_t)d.row * p.groups_row + d.unit_in_row, s32, s8);
-    } else {
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            const uint32_t mb = group_umax(mbits[s], p.gl_log2);
-            float s32 = 0.0f;
-            uint32_t s8 = 0;
-            const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
-            const uint32_t slot = (d.step0 + s) * kWaveSize + lane;
-            if (!PARTIAL || slot < p.slots) {
-                quantize_store<FMT>(row_codes, slot, y[s], inv);
-                if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
-                    store_scale<SFMT>(p, (size_t)d.row * p.groups_row + (slot >> p.gl_log2), s32, s8);
-            }
-        }
-    }
+    quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
 }
 
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
@@ -525,16 +356,6 @@ tk_status init_device(int dev)
 
 tk_status ensure_device(int& dev);
 
-bool overlaps(const void* a, size_t an, const void* b, size_t bn)
-{
-    if (!a || !b || an == 0 || bn == 0)
-        return false;
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + bn && b0 < a0 + an;
-}
-
-bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 void launch_one(const Params& p, int blocks, hipStream_t stream)
 {
@@ -580,13 +401,6 @@ bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, cons
     return false;
 }
 
-uint32_t pow2_at_least(uint32_t v)
-{
-    uint32_t p = 1;
-    while (p < v)
-        p <<= 1;
-    return p;
-}
 
 constexpr int kBlocksPerCU = 2; // workgroups of 256 threads per CU in the persistent grid
 
@@ -603,19 +417,20 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
         return TK_ERR_INVALID_ARG;
     if (std::isnan(clamp_limit) || clamp_limit <= 0.0f)
         return TK_ERR_INVALID_ARG;
-    if (scale_fmt != TK_SCALE_FP32 && scale_fmt != TK_SCALE_UE8M0)
+    const int64_t G = group_size ? group_size : hidden;
+    const int64_t groups_row = hidden / G;
+    ScaleSpec sp;
+    if (!scale_spec(scale_fmt, n, groups_row, sp))
         return TK_ERR_INVALID_ARG;
     if (n > 0 && (!x || !codes || !scales))
         return TK_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(w, 4) || !aligned(codes, fmt == 8 ? 8 : 4) ||
-        !aligned(clamped_count, 8) || (scale_fmt == TK_SCALE_FP32 && !aligned(scales, 4)))
+    if (!aligned(x, 16) || !aligned(w, 4) || !aligned(codes, fmt == 8 ? 8 : 4) || !aligned(clamped_count, 8) ||
+        !aligned(scales, sp.align))
         return TK_ERR_INVALID_ARG;
-    const int64_t G = group_size ? group_size : hidden;
-    const int64_t groups_row = hidden / G;
     const size_t x_bytes = (size_t)n * (size_t)hidden * 4u;
     const size_t w_bytes = w ? (size_t)n * 4u : 0;
     const size_t c_bytes = (size_t)n * (size_t)(fmt == 8 ? hidden : hidden / 2);
-    const size_t s_bytes = (size_t)n * (size_t)groups_row * (scale_fmt == TK_SCALE_FP32 ? 4u : 1u);
+    const size_t s_bytes = sp.bytes;
     const size_t k_bytes = clamped_count ? 8u : 0u;
     if (n > 0 && (overlaps(codes, c_bytes, x, x_bytes) || overlaps(codes, c_bytes, w, w_bytes) ||
                   overlaps(scales, s_bytes, x, x_bytes) || overlaps(scales, s_bytes, w, w_bytes) ||
@@ -625,42 +440,13 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
         return TK_ERR_INVALID_ARG;
 
     // ---- shape -> kernel variant ----
-    const uint32_t slots = (uint32_t)(hidden / kSlotCols);
-    const uint32_t steps_row = (slots + kWaveSize - 1) / kWaveSize;
-    const uint32_t gslots = (uint32_t)(G / kSlotCols);
     Params p{};
-    bool rowred;
-    uint32_t spu_max;
-    if (G == hidden) {
-        if (steps_row > (uint32_t)kMaxStepsPerUnit)
-            return TK_ERR_UNSUPPORTED;
-        rowred = true;
-        p.spu = steps_row;
-        p.upr = 1;
-        spu_max = pow2_at_least(steps_row);
-    } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
-        rowred = false;
-        p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
-        // steps per unit: a power of two up to 4 that divides the row's steps
-        uint32_t spu = n >= 1024 ? 4u : (n >= 256 ? 2u : 1u);
-        while (steps_row % spu)
-            spu >>= 1;
-        spu_max = spu;
-        p.spu = spu;
-        p.upr = steps_row / spu;
-    } else if (gslots % kWaveSize == 0) {
-        const uint32_t k = gslots / kWaveSize;
-        if (k > (uint32_t)kMaxStepsPerUnit)
-            return TK_ERR_UNSUPPORTED;
-        rowred = true;
-        p.spu = k;
-        p.upr = (uint32_t)groups_row;
-        spu_max = pow2_at_least(k);
-    } else {
-        return TK_ERR_UNSUPPORTED;
+    UnitPlan plan;
+    {
+        const tk_status rc = plan_units(n, hidden, group_size, n >= 1024 ? 4u : (n >= 256 ? 2u : 1u), p, plan);
+        if (rc != TK_OK)
+            return rc;
     }
-    if ((uint64_t)n * p.upr >= (uint64_t)INT_MAX)
-        return TK_ERR_UNSUPPORTED;
     if (n == 0)
         return TK_OK;
 
@@ -676,10 +462,8 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     p.codes = static_cast<uint8_t*>(codes);
     p.scales = scales;
     p.count = reinterpret_cast<unsigned long long*>(clamped_count);
-    p.slots = slots;
-    p.steps_row = steps_row;
-    p.units = (uint32_t)(n * p.upr);
-    p.groups_row = (uint32_t)groups_row;
+    p.scale_layout = sp.layout;
+    p.scale_ld = sp.ld;
     const bool clamp = !std::isinf(clamp_limit);
     p.clamp = clamp_limit;
 
@@ -687,11 +471,11 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
     const uint32_t cap = (uint32_t)g_dev[dev].cus * kBlocksPerCU;
     const int blocks = (int)(want < cap ? want : cap);
-    const bool partial = (slots % kWaveSize) != 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool ok = fmt == 8 ? dispatch<8>(scale_fmt, clamp, rowred, partial, (int)spu_max, p, blocks, s)
-                             : dispatch<4>(scale_fmt, clamp, rowred, partial, (int)spu_max, p, blocks, s);
+    const bool ok =
+        fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s)
+                 : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s);
     if (!ok)
         return TK_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess)

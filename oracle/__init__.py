@@ -55,6 +55,12 @@ def _load():
         lib.oracle_cast.restype = c.c_int
         lib.oracle_cast.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_int,
                                     c.c_void_p, c.c_void_p]
+        lib.oracle_cast_bf16.restype = c.c_int
+        lib.oracle_cast_bf16.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_int,
+                                         c.c_void_p, c.c_void_p]
+        lib.oracle_topk_gate.restype = c.c_int
+        lib.oracle_topk_gate.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int64, c.c_int64,
+                                         c.c_int, c.c_void_p, c.c_void_p]
         lib.oracle_swiglu_cast.restype = c.c_int
         lib.oracle_swiglu_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int64,
                                            c.c_float, c.c_int, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p]
@@ -139,6 +145,53 @@ def cast(y: np.ndarray, group_size: int, fmt: int, scale_fmt: int) -> Tuple[np.n
     return codes, scales
 
 
+def cast_bf16(x: np.ndarray, group_size: int, fmt: int, scale_fmt: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The stand-alone cast of bf16 rows (uint16 bit patterns [n, hidden])."""
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint16 and x.ndim == 2
+    n, hidden = x.shape
+    codes, scales = _out(n, hidden, group_size, fmt, scale_fmt)
+    rc = _load().oracle_cast_bf16(x.ctypes.data, n, hidden, group_size, fmt, scale_fmt, codes.ctypes.data,
+                                  scales.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_cast_bf16 failed ({rc})")
+    return codes, scales
+
+
+def scale_layout(scales: np.ndarray, layout: str, fill: int = 0) -> np.ndarray:
+    """Row-major scales [n, G] (fp32 or UE8M0 bytes) re-laid as the scale
+    tensor of the given layout, returned as raw bytes; positions the layout
+    leaves unwritten hold `fill`.  Data movement only:
+      "fp32_colmajor"  fp32  [G][ld], ld = n rounded up to 4, (r, k) at k*ld + r
+      "ue8m0_colmajor" uint8 [G][ld], ld = n rounded up to 16
+      "ue8m0_packed"   uint32 [ceil(G/4)][ld], ld = n rounded up to 4; word (j, r)
+                       holds the bytes of groups 4j..4j+3 of row r, group 4j lowest
+    """
+    n, G = scales.shape
+    if layout == "fp32_colmajor":
+        ld = (n + 3) // 4 * 4
+        out = np.full((G, ld, 4), fill, dtype=np.uint8)
+        for k in range(G):
+            for r in range(n):
+                out[k, r] = np.frombuffer(np.float32(scales[r, k]).tobytes(), dtype=np.uint8)
+        return out.reshape(-1)
+    if layout == "ue8m0_colmajor":
+        ld = (n + 15) // 16 * 16
+        out = np.full((G, ld), fill, dtype=np.uint8)
+        for k in range(G):
+            for r in range(n):
+                out[k, r] = scales[r, k]
+        return out.reshape(-1)
+    if layout == "ue8m0_packed":
+        ld = (n + 3) // 4 * 4
+        out = np.full(((G + 3) // 4, ld, 4), fill, dtype=np.uint8)
+        for k in range(G):
+            for r in range(n):
+                out[k // 4, r, k % 4] = scales[r, k]
+        return out.reshape(-1)
+    raise ValueError(layout)
+
+
 def swiglu_cast(x: np.ndarray, w: Optional[np.ndarray], group_size: int, clamp_limit: Optional[float],
                 fmt: int, scale_fmt: int) -> Tuple[np.ndarray, np.ndarray, int]:
     """The fused step, row by row: (codes, scales, clamped_count)."""
@@ -153,3 +206,18 @@ def swiglu_cast(x: np.ndarray, w: Optional[np.ndarray], group_size: int, clamp_l
     if rc:
         raise ValueError(f"oracle_swiglu_cast failed ({rc})")
     return codes, scales, int(cnt[0])
+
+
+def topk_gate(scores: np.ndarray, k: int, n_group: int = 1, topk_group: int = 1,
+              normalise: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k expert selection per token (oracle.c: oracle_topk_gate):
+    (indices int32 [tokens, k], weights fp32 [tokens, k]), best first."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    tokens, experts = scores.shape
+    idx = np.empty((tokens, k), dtype=np.int32)
+    w = np.empty((tokens, k), dtype=np.float32)
+    rc = _load().oracle_topk_gate(scores.ctypes.data, tokens, experts, k, n_group, topk_group, int(normalise),
+                                  idx.ctypes.data, w.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_topk_gate failed ({rc})")
+    return idx, w

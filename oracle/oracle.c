@@ -297,3 +297,118 @@ int oracle_encode(int fmt, const float* q, int64_t n, uint8_t* out)
         out[i] = fmt == ORACLE_FP8 ? oracle_e4m3(q[i]) : oracle_e2m1(q[i]);
     return 0;
 }
+
+/* The stand-alone cast of bf16 rows ("per_token_cast" in Tutorial ch.1
+ * "透视底层" / "闭环": bf16 in, FP8/FP4 codes and scales out, the same abs-max ->
+ * scale -> cast tail as the fused step).  Each bf16 value is widened exactly to
+ * fp32, then oracle_cast applies. */
+int oracle_cast_bf16(const uint16_t* x, int64_t n, int64_t hidden, int64_t group_size, int fmt,
+                     int scale_fmt, uint8_t* codes, void* scales)
+{
+    if (n < 0 || hidden <= 0)
+        return 1;
+    float* row = (float*)malloc((size_t)hidden * sizeof(float));
+    if (!row)
+        return 2;
+    const int64_t groups = hidden / (group_size ? group_size : hidden);
+    const int64_t code_bytes = fmt == ORACLE_FP8 ? hidden : hidden / 2;
+    const size_t scale_bytes = scale_fmt == ORACLE_SCALE_FP32 ? sizeof(float) : 1;
+    int rc = 0;
+    for (int64_t r = 0; r < n && rc == 0; ++r) {
+        for (int64_t j = 0; j < hidden; ++j)
+            row[j] = bf16_to_float(x[r * hidden + j]);
+        rc = oracle_cast(row, 1, hidden, group_size, fmt, scale_fmt, codes + r * code_bytes,
+                         (uint8_t*)scales + (size_t)(r * groups) * scale_bytes);
+    }
+    free(row);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Top-k expert gating ("TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式"
+ * "1. Gating": pick each token's top-k experts from [num_tokens, num_experts]
+ * scores, equal scores going to the smaller index; "【DeepSeek】TileKernels从入门
+ * 到精通" ch.3 "导诊台的“工号制度”": take the best, label it, take the next; the
+ * group step compares the sums of each group's two best scores, equal sums
+ * going to the smaller group index).
+ *
+ * Readings: "a beats b" means score_a > score_b, or score_a == score_b (as
+ * numbers, so -0 == +0) and a < b.  With n_group > 1 the experts form n_group
+ * consecutive groups; a group's score is RN(best + second best) of its members;
+ * the topk_group best groups (same tie rule on group index) are kept and the k
+ * experts are chosen among their members only.  Output order: best first.
+ * Weights are the chosen scores, or, when normalise is set, each chosen score
+ * divided by the fp32 sum of the chosen scores added best first (a zero sum
+ * leaves the chosen scores as they are).
+ * ------------------------------------------------------------------------- */
+static int beats(float sa, int64_t a, float sb, int64_t b) { return sa > sb || (sa == sb && a < b); }
+
+int oracle_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
+                     int64_t topk_group, int normalise, int32_t* idx_out, float* w_out)
+{
+    if (tokens < 0 || experts <= 0 || k <= 0 || n_group <= 0 || experts % n_group != 0)
+        return 1;
+    const int64_t per = experts / n_group;
+    if (topk_group <= 0 || topk_group > n_group || k > topk_group * per || (n_group > 1 && per < 2))
+        return 1;
+    unsigned char* allowed = (unsigned char*)malloc((size_t)experts);
+    unsigned char* taken = (unsigned char*)malloc((size_t)(experts > n_group ? experts : n_group));
+    float* gscore = (float*)malloc((size_t)n_group * sizeof(float));
+    if (!allowed || !taken || !gscore) {
+        free(allowed); free(taken); free(gscore);
+        return 2;
+    }
+    for (int64_t t = 0; t < tokens; ++t) {
+        const float* s = scores + t * experts;
+        /* groups: best two members' sum, then the topk_group best groups */
+        if (n_group > 1) {
+            for (int64_t g = 0; g < n_group; ++g) {
+                int64_t b1 = -1, b2 = -1;
+                for (int64_t e = g * per; e < (g + 1) * per; ++e) {
+                    if (b1 < 0 || beats(s[e], e, s[b1], b1)) {
+                        b2 = b1;
+                        b1 = e;
+                    } else if (b2 < 0 || beats(s[e], e, s[b2], b2)) {
+                        b2 = e;
+                    }
+                }
+                gscore[g] = s[b1] + s[b2];
+            }
+            memset(taken, 0, (size_t)n_group);
+            memset(allowed, 0, (size_t)experts);
+            for (int64_t j = 0; j < topk_group; ++j) {
+                int64_t best = -1;
+                for (int64_t g = 0; g < n_group; ++g)
+                    if (!taken[g] && (best < 0 || beats(gscore[g], g, gscore[best], best)))
+                        best = g;
+                taken[best] = 1;
+                memset(allowed + best * per, 1, (size_t)per);
+            }
+        } else {
+            memset(allowed, 1, (size_t)experts);
+        }
+        /* experts: the best allowed one, k times */
+        memset(taken, 0, (size_t)experts);
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < experts; ++e)
+                if (allowed[e] && !taken[e] && (best < 0 || beats(s[e], e, s[best], best)))
+                    best = e;
+            taken[best] = 1;
+            idx_out[t * k + j] = (int32_t)best;
+            w_out[t * k + j] = s[best];
+        }
+        if (normalise) {
+            float sum = 0.0f;
+            for (int64_t j = 0; j < k; ++j)
+                sum += w_out[t * k + j];
+            if (sum != 0.0f)
+                for (int64_t j = 0; j < k; ++j)
+                    w_out[t * k + j] = w_out[t * k + j] / sum;
+        }
+    }
+    free(allowed);
+    free(taken);
+    free(gscore);
+    return 0;
+}

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["tk_init", "tk_status_str", "tk_swiglu_cast_fp4", "tk_swiglu_cast_fp8",
-                                         "tk_swiglu_forward"])
+                                         "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -61,7 +61,9 @@ def cast4(**kw):
 @pytest.mark.parametrize("kw", [
     dict(n=-1), dict(n=2 ** 31), dict(hidden=0), dict(hidden=-8), dict(hidden=12), dict(group_size=-8),
     dict(group_size=12), dict(group_size=48), dict(clamp_limit=float("nan")), dict(clamp_limit=0.0),
-    dict(clamp_limit=-1.0), dict(clamp_limit=-INF), dict(scale_fmt=2), dict(x=None), dict(codes=None),
+    dict(clamp_limit=-1.0), dict(clamp_limit=-INF), dict(scale_fmt=7), dict(scale_fmt=-1), dict(x=None),
+    dict(codes=None), dict(scales=S + 4, scale_fmt=tk.TK_SCALE_FP32_COLMAJOR),
+    dict(scales=S + 8, scale_fmt=tk.TK_SCALE_UE8M0_COLMAJOR), dict(scales=S + 4, scale_fmt=tk.TK_SCALE_UE8M0_PACKED),
     dict(scales=None), dict(x=X + 8), dict(codes=C + 4), dict(topk_weight=W + 2), dict(clamped_count=K + 4),
     dict(codes=X), dict(scales=X + 64), dict(codes=W), dict(scales=C + 16), dict(clamped_count=S),
 ], ids=str)
@@ -105,3 +107,29 @@ def test_swiglu_forward_invalid_arguments(kw):
 def test_init_rejects_bad_device():
     # tk_init validates the index against the device count (0 here: no GPU)
     assert tk.tk_init(-1) in (INVALID, tk.TkStatus.TK_ERR_HIP)
+
+
+def cast_only(fn, **kw):
+    a = dict(x=X, in_dtype=tk.TK_DTYPE_BF16, n=4, hidden=1024, group_size=128, scale_fmt=UE8M0, codes=C, scales=S,
+             stream=0)
+    a.update(kw)
+    return fn(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=-1), dict(hidden=12), dict(group_size=12), dict(in_dtype=2), dict(in_dtype=-1), dict(scale_fmt=5),
+    dict(scales=S + 4, scale_fmt=tk.TK_SCALE_UE8M0_PACKED),
+    dict(x=None), dict(codes=None), dict(scales=None), dict(x=X + 8), dict(codes=C + 2),
+    dict(scales=S + 2, scale_fmt=FP32), dict(codes=X), dict(scales=X + 100), dict(codes=S),
+], ids=str)
+def test_cast_invalid_arguments(kw):
+    # every case is invalid for both formats, so no call can reach a launch
+    assert cast_only(tk.tk_cast_fp8, **kw) == INVALID
+    assert cast_only(tk.tk_cast_fp4, **kw) == INVALID
+
+
+def test_cast_unsupported_and_empty():
+    assert cast_only(tk.tk_cast_fp8, hidden=48, group_size=24) == UNSUPPORTED
+    assert cast_only(tk.tk_cast_fp8, hidden=8200, group_size=0) == UNSUPPORTED
+    assert cast_only(tk.tk_cast_fp8, n=0) == OK
+    assert cast_only(tk.tk_cast_fp4, n=0, x=None, codes=None, scales=None) == OK

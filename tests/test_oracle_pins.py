@@ -291,3 +291,75 @@ def test_clamp_count_and_infinite_limit():
     a = oracle.swiglu_cast(x, wt, 0, math.inf, 8, 0)
     b = oracle.swiglu_cast(x, wt, 0, None, 8, 0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] == 0
+
+
+def test_scale_layouts_match_hand_written_fixture():
+    d = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "scale_layouts.json")))
+    s8 = np.array([[10 * r + k for k in range(6)] for r in range(5)], dtype=np.uint8)
+    cm = oracle.scale_layout(s8, "ue8m0_colmajor", 255)
+    assert len(cm) == 6 * d["ue8m0_colmajor_ld"]
+    assert cm[:32].tolist() == d["ue8m0_colmajor_first_two_columns"]
+    pk = oracle.scale_layout(s8, "ue8m0_packed", 255).view("<u4")
+    assert [f"{w:08x}" for w in pk] == d["ue8m0_packed_words_hex"]
+    sf = np.array([[r + k / 8 for k in range(6)] for r in range(5)], dtype=np.float32)
+    fc = oracle.scale_layout(sf, "fp32_colmajor", 0).view(np.float32).reshape(6, d["fp32_colmajor_ld"])
+    assert fc[1, :5].tolist() == d["fp32_colmajor_column_1"]
+
+
+# ---------------------------------------------------------------------------
+# Top-k gating: the oracle's iterative selection against brute force by sorting
+# ---------------------------------------------------------------------------
+def _brute_topk(s, k, n_group, topk_group, normalise):
+    E = len(s)
+    per = E // n_group
+    allowed = set(range(E))
+    if n_group > 1:
+        gsum = []
+        for g in range(n_group):
+            vals = sorted((float(v) for v in s[g * per:(g + 1) * per]), reverse=True)
+            gsum.append(float(np.float32(vals[0]) + np.float32(vals[1])))
+        groups = sorted(range(n_group), key=lambda g: (-gsum[g], g))[:topk_group]
+        allowed = {e for g in groups for e in range(g * per, (g + 1) * per)}
+    order = sorted(allowed, key=lambda e: (-float(s[e]), e))[:k]
+    w = [np.float32(s[e]) for e in order]
+    if normalise:
+        tot = np.float32(0)
+        for v in w:
+            tot = np.float32(tot + v)
+        if tot != 0:
+            w = [np.float32(v / tot) for v in w]
+    return order, [float(v) for v in w]
+
+
+@pytest.mark.parametrize("E,k,ng,tg", [(256, 8, 8, 4), (256, 8, 1, 1), (64, 6, 1, 1), (128, 4, 4, 2), (8, 2, 1, 1),
+                                       (72, 5, 3, 2), (256, 256, 1, 1), (32, 1, 16, 3)])
+@pytest.mark.parametrize("normalise", [False, True])
+def test_topk_gate_matches_brute_force(E, k, ng, tg, normalise):
+    rng = np.random.default_rng(E * 7 + k)
+    T = 40
+    s = np.floor(rng.uniform(0, 1, (T, E)) * 16) / 16  # coarse values: many ties
+    s[::5] = rng.uniform(0, 1, (len(s[::5]), E))
+    s[3, :] = 0.25
+    s[4, ::2] = -0.0
+    s[4, 1::2] = 0.0
+    s = s.astype(np.float32)
+    idx, w = oracle.topk_gate(s, k, ng, tg, normalise)
+    for t in range(T):
+        order, ww = _brute_topk(s[t], k, ng, tg, normalise)
+        assert idx[t].tolist() == order, t
+        assert w[t].tolist() == ww, t
+
+
+def test_topk_gate_invariants():
+    rng = np.random.default_rng(1)
+    s = rng.uniform(-1, 1, (30, 256)).astype(np.float32)
+    idx, w = oracle.topk_gate(s, 8, 8, 4, False)
+    for t in range(30):
+        assert len(set(idx[t].tolist())) == 8                  # distinct experts
+        assert (np.diff(w[t]) <= 0).all()                     # best first
+        groups = {int(e) // 32 for e in idx[t]}
+        assert len(groups) <= 4                               # only the kept groups
+    idx1, _ = oracle.topk_gate(s, 1, 1, 1, False)
+    assert (idx1[:, 0] == np.argmax(s, axis=1)).all()         # k = 1: argmax, first index on ties
+    _, wn = oracle.topk_gate(np.abs(s), 8, 8, 4, True)
+    assert np.allclose(wn.sum(axis=1), 1.0, atol=1e-6)
