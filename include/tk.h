@@ -183,6 +183,37 @@ tk_status tk_cast_fp8(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
 tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
                       tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream);
 
+/*
+ * tk_topk_gate: deterministic top-k expert selection per token -- the Gating
+ * module of "TileLang + TileKernels：DeepSeek 的 GPU 内核开发新范式" ("1. Gating":
+ * top-k of [num_tokens, num_experts] scores, equal scores to the smaller
+ * index) with the grouped step of "【DeepSeek】TileKernels从入门到精通" ch.3
+ * ("导诊台的“工号制度”": groups ranked by the sum of their two best scores,
+ * equal sums to the smaller group index).
+ *
+ *   "a beats b": score_a > score_b, or equal scores (-0 == +0) and a < b.
+ *   n_group > 1: the experts form n_group consecutive groups; a group's score
+ *   is RN(best + second best) of its members; only the topk_group best groups'
+ *   members are candidates.  Then k times: the best remaining candidate.
+ *
+ *  scores       fp32 [tokens, experts], row-major, 4-byte aligned (device).
+ *  tokens       0 <= tokens < 2^31.
+ *  experts      1..256;  k: 1..64 and at most the number of candidates.
+ *  n_group      divides experts (1 = no groups); topk_group in 1..n_group;
+ *               with groups, each group has at least 2 experts.
+ *  normalise    0: weights are the chosen scores; 1: each chosen score divided
+ *               by the fp32 sum of the chosen scores added best first (a zero
+ *               sum leaves the scores as they are).
+ *  topk_idx     int32 [tokens, k] (device), best first.
+ *  topk_weight  fp32 [tokens, k] (device), in the same order.
+ * Returns TK_ERR_INVALID_ARG for violated preconditions, overlapping outputs or
+ * misaligned pointers; TK_ERR_UNSUPPORTED when experts > 256 or k > 64, or when
+ * a group is not a power-of-two number of whole 64-lane slots (experts/n_group
+ * must be a multiple of ceil(experts/64), with a power-of-two quotient).
+ */
+tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
+                       int64_t topk_group, int normalise, int32_t* topk_idx, float* topk_weight, void* stream);
+
 /* tk_status_str: a static, human-readable name for a status code. */
 const char* tk_status_str(tk_status status);
 

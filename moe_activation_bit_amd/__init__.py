@@ -23,7 +23,7 @@ __all__ = [
     "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "TK_SCALE_FP32_COLMAJOR", "TK_SCALE_UE8M0_COLMAJOR",
     "TK_SCALE_UE8M0_PACKED", "TK_DTYPE_BF16", "TK_DTYPE_FP32", "LIB_PATH", "load_library",
     "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4",
-    "tk_status_str",
+    "tk_topk_gate", "tk_status_str",
 ]
 
 TK_SCALE_FP32 = 0
@@ -58,6 +58,8 @@ SIGNATURES = {
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_cast_fp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_topk_gate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -144,6 +146,14 @@ def tk_cast_fp8(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, st
 def tk_cast_fp4(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream=None) -> TkStatus:
     """See tk_cast_fp4 in include/tk.h."""
     return _cast_only("tk_cast_fp4", x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream)
+
+
+def tk_topk_gate(scores, tokens, experts, k, n_group, topk_group, normalise, topk_idx, topk_weight,
+                 stream=None) -> TkStatus:
+    """See tk_topk_gate in include/tk.h."""
+    return TkStatus(load_library().tk_topk_gate(_ptr(scores), int(tokens), int(experts), int(k), int(n_group),
+                                                int(topk_group), int(bool(normalise)), _ptr(topk_idx),
+                                                _ptr(topk_weight), _stream(stream)))
 
 
 def tk_status_str(status: int) -> str:

@@ -34,7 +34,7 @@ def _run(cmd):
 
 
 OBJ_DIR = os.path.join(HERE, "_build")
-TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip"]
+TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip", "tk_topk.hip"]
 
 
 def _hip_object(src):

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["tk_init", "tk_status_str", "tk_swiglu_cast_fp4", "tk_swiglu_cast_fp8",
-                                         "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4"])
+                                         "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4", "tk_topk_gate"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,3 +133,26 @@ def test_cast_unsupported_and_empty():
     assert cast_only(tk.tk_cast_fp8, hidden=8200, group_size=0) == UNSUPPORTED
     assert cast_only(tk.tk_cast_fp8, n=0) == OK
     assert cast_only(tk.tk_cast_fp4, n=0, x=None, codes=None, scales=None) == OK
+
+
+def topk(**kw):
+    a = dict(scores=X, tokens=4, experts=256, k=8, n_group=8, topk_group=4, normalise=0, topk_idx=C, topk_weight=S,
+             stream=0)
+    a.update(kw)
+    return tk.tk_topk_gate(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tokens=-1), dict(experts=0), dict(k=0), dict(n_group=0), dict(topk_group=0), dict(n_group=3),
+    dict(topk_group=9), dict(k=129), dict(experts=8, n_group=8, topk_group=1, k=1), dict(scores=None),
+    dict(topk_idx=None), dict(topk_weight=None), dict(scores=X + 2), dict(topk_idx=X), dict(topk_weight=C + 8),
+], ids=str)
+def test_topk_invalid_arguments(kw):
+    assert topk(**kw) == INVALID
+
+
+def test_topk_unsupported_and_empty():
+    assert topk(experts=512, n_group=8) == UNSUPPORTED
+    assert topk(experts=256, n_group=1, topk_group=1, k=65) == UNSUPPORTED
+    assert topk(experts=72, n_group=3, topk_group=2, k=5) == UNSUPPORTED
+    assert topk(tokens=0) == OK

@@ -1,0 +1,73 @@
+"""GPU parity of the deterministic top-k gating kernel (tk_topk_gate) against
+the oracle: indices and weights bit-exact, including ties and signed zeros."""
+import numpy as np
+import pytest
+import torch
+
+import moe_activation_bit_amd as tk
+import oracle
+from moe_activation_bit_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def run(scores, k, ng, tg, normalise):
+    T, E = scores.shape
+    sd = torch.from_numpy(scores).to(DEV)
+    idx = torch.full((T * k + 64,), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T * k + 64,), -7.0, dtype=torch.float32, device=DEV)
+    rc = tk.tk_topk_gate(sd, T, E, k, ng, tg, normalise, idx.data_ptr() + 128, w.data_ptr() + 128)
+    assert rc == tk.TkStatus.TK_OK, tk.tk_status_str(rc)
+    torch.cuda.synchronize()
+    i, ww = idx.cpu().numpy(), w.cpu().numpy()
+    assert (i[:32] == -7).all() and (i[32 + T * k:] == -7).all(), "index canary"
+    assert (ww[:32] == -7).all() and (ww[32 + T * k:] == -7).all(), "weight canary"
+    return i[32:32 + T * k].reshape(T, k), ww[32:32 + T * k].reshape(T, k)
+
+
+SHAPES = [  # (experts, k, n_group, topk_group)
+    (256, 8, 8, 4), (256, 8, 1, 1), (256, 64, 1, 1), (256, 6, 16, 2), (128, 4, 4, 2), (64, 6, 1, 1), (64, 8, 32, 4),
+    (8, 2, 1, 1), (100, 3, 1, 1), (160, 8, 5, 2), (200, 5, 1, 1),
+]
+
+
+@pytest.mark.parametrize("normalise", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_topk_matches_oracle(shape, normalise):
+    E, k, ng, tg = shape
+    print("[gpu-case] topk", shape, normalise, flush=True)
+    key = wl.stream_key("topk_test", E * 1000 + k, "scores")
+    T = 777
+    u = wl.uniform(key, 0, T * E).reshape(T, E)
+    s = np.where(np.arange(T)[:, None] % 3 == 0, np.floor(u * 8) / 8, u).astype(np.float32)  # ties on 1/3 of rows
+    s[5] = 0.5
+    s[6, ::2] = -0.0
+    s[6, 1::2] = 0.0
+    s[7] = -u[7].astype(np.float32)
+    C = (E + 63) // 64
+    per = E // ng
+    if ng > 1 and (per % C or ((per // C) & (per // C - 1))):
+        sd = torch.from_numpy(s).to(DEV)
+        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        assert tk.tk_topk_gate(sd, T, E, k, ng, tg, normalise, idx, w) == tk.TkStatus.TK_ERR_UNSUPPORTED
+        return
+    gi, gw = run(s, k, ng, tg, normalise)
+    oi, ow = oracle.topk_gate(s, k, ng, tg, bool(normalise))
+    bad = np.argwhere(gi != oi)
+    assert bad.size == 0, f"indices differ at {bad[:4].tolist()}: {gi[bad[0][0]]} vs {oi[bad[0][0]]}"
+    assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), np.argwhere(gw.view(np.uint32) != ow.view(np.uint32))[:4]
+
+
+def test_topk_deepseek_shape_full_size():
+    """16384 tokens x 256 experts, 8 groups keep 4, top-8, normalised."""
+    T, E = 16384, 256
+    print("[gpu-case] topk full size", T, E, flush=True)
+    s = wl.uniform(wl.stream_key("topk_test", 0, "full"), 0, T * E).reshape(T, E).astype(np.float32)
+    gi, gw = run(s, 8, 8, 4, 1)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), np.arange(0, T, 97)]))
+    oi, ow = oracle.topk_gate(s[rows], 8, 8, 4, True)
+    assert np.array_equal(gi[rows], oi) and np.array_equal(gw[rows].view(np.uint32), ow.view(np.uint32))
+    assert ((gi >= 0) & (gi < E)).all()
+    assert np.allclose(gw.sum(axis=1), 1.0, atol=1e-5)
