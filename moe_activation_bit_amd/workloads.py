@@ -1,8 +1,9 @@
-"""Seeded synthetic workloads for the fused SwiGLU + top-k weight + FP8/FP4 cast.
+"""Seeded synthetic workloads for the fused SwiGLU + top-k weight + FP8/FP4
+cast and for the weighted top-k reduce of the experts' output rows.
 
 This module only draws inputs (random streams, bf16 rounding of samples,
-routing-weight normalisation); it holds none of the activation or
-quantisation arithmetic.  The tests, the benchmark and the oracle's harness
+routing-weight normalisation, the position map of a dispatch layout); it
+holds none of the activation, quantisation or reduce arithmetic.  The tests, the benchmark and the oracle's harness
 all draw their inputs here, so both sides of every comparison see the same
 bytes.
 
@@ -192,3 +193,113 @@ def make_w(w: Workload, seed: int) -> np.ndarray:
     else:
         raise ValueError(w.weights)
     return out.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Weighted top-k reduce of the experts' output rows
+# ("【DeepSeek】TileKernels从入门到精通" ch.3 "结算中心的“减法工程”" and
+# "动态寻址": the rows are found through a token/top-k -> position map).
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class ReduceWorkload:
+    """One synthetic reduce workload.  The expanded rows are laid out as an MoE
+    dispatch leaves them: grouped by expert, tokens in order within an expert,
+    so a token's k rows lie far apart."""
+
+    name: str
+    tokens: int
+    k: int
+    experts: int
+    hidden: int
+    sigma: float                  # std-dev of the bf16 expert outputs
+    drop_p: float                 # probability that a (token, slot) was dropped
+    row_scale: bool               # a per-row dequantisation factor is given
+    global_scale: float
+    out_bf16: bool
+    skew: float = 1.0             # expert popularity ~ (rank+1)^-skew
+
+    def out_bytes_per_token(self) -> int:
+        return self.hidden * (2 if self.out_bf16 else 4)
+
+    def algorithmic_bytes(self, pos: np.ndarray) -> int:
+        """Bytes the step must move at least once: the present rows (and their
+        scale), the position map and weights, and the output."""
+        present = int(np.count_nonzero(pos >= 0))
+        per_present = 2 * self.hidden + (4 if self.row_scale else 0)
+        return present * per_present + pos.size * 8 + self.tokens * self.out_bytes_per_token()
+
+
+REDUCE_WORKLOADS = {
+    r.name: r
+    for r in [
+        # small case for the oracle on every element: 64 tokens x top-8 of 256
+        # experts, hidden 7168, 5% dropped slots
+        ReduceWorkload("reduce_t64_k8_h7168_drop5", 64, 8, 256, 7168, 1.0, 0.05, True, 2.5, True),
+        # 4096 tokens x top-8 of 256 experts at hidden 7168: the down-projection
+        # outputs of the 32768 expanded rows of the headline activation step
+        ReduceWorkload("reduce_t4096_k8_h7168", 4096, 8, 256, 7168, 1.0, 0.0, True, 2.5, True),
+    ]
+}
+REDUCE_HEADLINE = "reduce_t4096_k8_h7168"
+
+
+def make_routing(r: ReduceWorkload, seed: int):
+    """(pos int32 [tokens, k], w fp32 [tokens, k], row_scale fp32 [n_rows] or
+    None, n_rows).  Each token picks k distinct experts (popularity skewed by
+    a power law); the present (token, slot) pairs get rows expert-major,
+    tokens in order within an expert; dropped pairs get -1.  w is each
+    token's uniform draws normalised to sum 1 (zero-weight dropped slots
+    keep their draw)."""
+    T, k, E = r.tokens, r.k, r.experts
+    pop = (np.arange(E, dtype=np.float64) + 1.0) ** -r.skew
+    perm = np.argsort(uniform(stream_key(r.name, seed, "expert_perm"), 0, E), kind="stable")
+    pop = pop[np.argsort(perm, kind="stable")]  # popularity not tied to the expert index
+    # k distinct experts per token: the k largest of u^(1/pop) (weighted draw
+    # without replacement)
+    u = uniform(stream_key(r.name, seed, "expert_pick"), 0, T * E).reshape(T, E)
+    keys = np.log(np.maximum(u, 1e-300)) / pop
+    experts = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int64)
+    drop = uniform(stream_key(r.name, seed, "drop"), 0, T * k).reshape(T, k) < r.drop_p
+    t_idx = np.repeat(np.arange(T, dtype=np.int64), k).reshape(T, k)
+    present = ~drop
+    e_p, t_p = experts[present], t_idx[present]
+    order = np.lexsort((t_p, e_p))  # expert-major, then token
+    rows = np.empty(order.size, dtype=np.int64)
+    rows[order] = np.arange(order.size, dtype=np.int64)
+    pos = np.full((T, k), -1, dtype=np.int32)
+    pos[present] = rows.astype(np.int32)
+    n_rows = int(order.size)
+    wu = uniform(stream_key(r.name, seed, "w"), 0, T * k).reshape(T, k)
+    w = (wu / wu.sum(axis=1, keepdims=True)).astype(np.float32)
+    rs = None
+    if r.row_scale:
+        rs = (0.5 + 1.5 * uniform(stream_key(r.name, seed, "row_scale"), 0, n_rows)).astype(np.float32)
+    return pos, w, rs, n_rows
+
+
+def make_expert_rows(r: ReduceWorkload, seed: int, n_rows: int, rows: Optional[Sequence[int]] = None,
+                     out: Optional[np.ndarray] = None) -> np.ndarray:
+    """bf16 bits of the experts' output rows, shape [n_rows, hidden] (or the
+    listed rows only)."""
+    lib = _synth()
+    hidden = r.hidden
+    row_list = list(range(n_rows)) if rows is None else [int(i) for i in rows]
+    x = out if out is not None else np.empty((len(row_list), hidden), dtype=np.uint16)
+    assert x.shape == (len(row_list), hidden) and x.dtype == np.uint16 and x.flags.c_contiguous
+    key = stream_key(r.name, seed, "expert_rows")
+    base = x.ctypes.data
+
+    def fill(span):
+        for i in range(*span):
+            lib.synth_normal_bf16(key, row_list[i] * hidden, hidden, r.sigma, base + i * hidden * 2)
+
+    count = len(row_list)
+    if count:
+        nt = min(_threads(), count)
+        step = (count + nt - 1) // nt
+        spans = [(i, min(count, i + step)) for i in range(0, count, step)]
+        with ThreadPoolExecutor(len(spans)) as ex:
+            list(ex.map(fill, spans))
+    return x

@@ -1,6 +1,6 @@
 """The oracle: a plain CPU statement of the fused SwiGLU + top-k weight +
-FP8/FP4 cast (see oracle.c for the sources it follows and every reading it
-takes).  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+FP8/FP4 cast, the stand-alone cast, the top-k gating and the weighted top-k
+reduce (see oracle.c for the sources it follows and every reading it takes).  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
 benchmark's CPU-baseline leg may use it; the GPU library never does.
 
 numpy in, numpy out.  x is the bf16 bit pattern as uint16 [n, 2*hidden].
@@ -61,6 +61,9 @@ def _load():
         lib.oracle_topk_gate.restype = c.c_int
         lib.oracle_topk_gate.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int64, c.c_int64,
                                          c.c_int, c.c_void_p, c.c_void_p]
+        lib.oracle_moe_reduce.restype = c.c_int
+        lib.oracle_moe_reduce.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_float, c.c_int64,
+                                          c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_void_p]
         lib.oracle_swiglu_cast.restype = c.c_int
         lib.oracle_swiglu_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int64,
                                            c.c_float, c.c_int, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p]
@@ -221,3 +224,28 @@ def topk_gate(scores: np.ndarray, k: int, n_group: int = 1, topk_group: int = 1,
     if rc:
         raise ValueError(f"oracle_topk_gate failed ({rc})")
     return idx, w
+
+
+def moe_reduce(x: np.ndarray, pos: np.ndarray, w: np.ndarray, row_scale: Optional[np.ndarray] = None,
+               global_scale: float = 1.0, out_bf16: bool = True) -> np.ndarray:
+    """Weighted top-k reduce (oracle.c: oracle_moe_reduce).  x: bf16 bits uint16
+    [n_rows, hidden]; pos: int32 [tokens, k] row per (token, slot), entries
+    outside [0, n_rows) dropped; w: fp32 [tokens, k]; row_scale: fp32 [n_rows]
+    or None.  Returns bf16 bits uint16 [tokens, hidden], or fp32."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n_rows, hidden = x.shape
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    tokens, k = pos.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.shape == (tokens, k)
+    rs = None
+    if row_scale is not None:
+        rs = np.ascontiguousarray(row_scale, dtype=np.float32)
+        assert rs.shape == (n_rows,)
+    out = np.empty((tokens, hidden), dtype=np.uint16 if out_bf16 else np.float32)
+    rc = _load().oracle_moe_reduce(x.ctypes.data, None if rs is None else rs.ctypes.data, pos.ctypes.data,
+                                   w.ctypes.data, float(global_scale), tokens, k, hidden, n_rows, int(out_bf16),
+                                   out.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_moe_reduce failed ({rc})")
+    return out

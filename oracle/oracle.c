@@ -5,7 +5,9 @@
  * step of an MoE expert: SwiGLU on a packed [gate | up] bf16 row, optional
  * clamp with a clamp counter, scaling by the token's top-k routing weight,
  * an abs-max per token or per column group, and the cast to FP8 E4M3 or
- * FP4 E2M1 codes with an fp32 or UE8M0 (power-of-two) scale.
+ * FP4 E2M1 codes with an fp32 or UE8M0 (power-of-two) scale; the same cast
+ * on its own; the deterministic top-k gating that produces the routing
+ * weights; and the weighted top-k reduce of the experts' output rows.
  *
  * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  The GPU library never calls it, and the two share no
@@ -410,5 +412,72 @@ int oracle_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64
     free(allowed);
     free(taken);
     free(gscore);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Fused MoE reduce ("【DeepSeek】TileKernels从入门到精通" ch.3 "结算中心的“减法
+ * 工程”": each token's top-k expert outputs are weighted and summed in one pass,
+ * the routing weights, the quantisation scale factors and a global scale
+ * applied on the way; "动态寻址": a token/top-k -> position map says where each
+ * expert output row lies).
+ *
+ * Readings: x holds the experts' output rows (bf16 [n_rows, hidden]); pos[t,j]
+ * is the row of token t's j-th expert output; an entry outside [0, n_rows)
+ * (negative: a dropped slot) contributes nothing.  row_scale (nullable) is a
+ * per-row dequantisation factor.  Per token t and column c, over the present
+ * slots in order j = 0..k-1:
+ *   f = RN(w[t,j] * row_scale[p]) (or w[t,j]),  acc = RN(acc + RN(f * x[p,c]))
+ * from acc = +0; out = RN(acc * global_scale), then rounded to the nearest
+ * bf16 (ties to even) when out_bf16 is set, else kept as fp32.
+ * ------------------------------------------------------------------------- */
+
+/* nearest bf16 to a finite fp32 value, ties to the even code; a value at or
+   past the midpoint between the largest bf16 and 2^128 becomes infinity */
+static uint16_t float_to_bf16_rne(float v)
+{
+    uint32_t b;
+    memcpy(&b, &v, 4);
+    const uint32_t lo_b = b & 0xFFFF0000u; /* v truncated toward zero */
+    float lo;
+    memcpy(&lo, &lo_b, 4);
+    /* the next bf16 away from zero, as an exact double (2^128 past the top) */
+    const double ulp = ldexp(1.0, ((int)((lo_b >> 23) & 0xFFu) > 0 ? (int)((lo_b >> 23) & 0xFFu) - 127 - 7 : -126 - 7));
+    const double dlo = fabs((double)v - (double)lo);
+    const double dhi = ulp - dlo;
+    int up;
+    if (dlo < dhi)
+        up = 0;
+    else if (dhi < dlo)
+        up = 1;
+    else
+        up = (int)((lo_b >> 16) & 1u); /* tie: go to the even code */
+    return (uint16_t)((lo_b >> 16) + (uint32_t)up);
+}
+
+int oracle_moe_reduce(const uint16_t* x, const float* row_scale, const int32_t* pos, const float* w,
+                      float global_scale, int64_t tokens, int64_t k, int64_t hidden, int64_t n_rows,
+                      int out_bf16, void* out)
+{
+    if (tokens < 0 || k <= 0 || hidden <= 0 || n_rows < 0)
+        return 1;
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int64_t c = 0; c < hidden; ++c) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < k; ++j) {
+                const int64_t p = pos[t * k + j];
+                if (p < 0 || p >= n_rows)
+                    continue;
+                const float f = row_scale ? w[t * k + j] * row_scale[p] : w[t * k + j];
+                const float term = f * bf16_to_float(x[p * hidden + c]);
+                acc = acc + term;
+            }
+            const float o = acc * global_scale;
+            if (out_bf16)
+                ((uint16_t*)out)[t * hidden + c] = float_to_bf16_rne(o);
+            else
+                ((float*)out)[t * hidden + c] = o;
+        }
+    }
     return 0;
 }

@@ -172,3 +172,35 @@ def cast_row(y: Sequence[float], group: int, fmt: int, scale_fmt: int):
 
 def pack_fp4(codes: Sequence[int]) -> List[int]:
     return [codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(len(codes) // 2)]
+
+
+def add_f32(a: float, b: float) -> float:
+    """RN(a + b) in fp32; an exact zero sum is +0 unless both addends are -0."""
+    s = Fr(a) + Fr(b)
+    return round_f32(s, neg_zero=(s == 0 and is_neg(a) and is_neg(b)))
+
+
+def round_bf16(v: float) -> int:
+    """bf16 bit pattern nearest to the finite value v, ties to the even code,
+    found by searching the neighbouring codes on exact rationals."""
+    if v == 0:
+        return 0x8000 if is_neg(v) else 0
+    best, best_d = None, None
+    b = struct.unpack("<I", struct.pack("<f", v))[0] >> 16
+    for code in range(max(0, (b & 0x7FFF) - 2), min(0x7F80, (b & 0x7FFF) + 3) + 1):
+        mag = Fr(2) ** 128 if code == 0x7F80 else Fr(bf16_to_float(code))
+        d = abs(abs(Fr(v)) - mag)
+        if best is None or d < best_d or (d == best_d and code % 2 == 0):
+            best, best_d = code, d
+    return best | (b & 0x8000)
+
+
+def reduce_cell(xs: Sequence[int], ws: Sequence[float], scales: Sequence[Optional[float]], gscale: float) -> float:
+    """One output element of the weighted top-k reduce over the present slots,
+    in slot order: f = RN(w*s), acc = RN(acc + RN(f*x)) from +0, then
+    RN(acc*gscale)."""
+    acc = 0.0
+    for xh, w, s in zip(xs, ws, scales):
+        f = w if s is None else mul_f32(w, s)
+        acc = add_f32(acc, mul_f32(f, bf16_to_float(xh)))
+    return mul_f32(acc, gscale)
