@@ -232,6 +232,108 @@ def cpu_baseline(w, seed: int, rows: int):
     }
 
 
+def _timed(torch, stream, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, ev0.elapsed_time(ev1) / 1e3
+
+
+def bench_aux(args, torch, np, tk, wl):
+    """The next-row kernels on their own workloads, one JSON line like the
+    headline's: the stand-alone cast (bf16 [65536, 2048] -> E4M3, groups of
+    128, UE8M0), the top-k gating (16384 tokens x 256 experts, 8 groups,
+    keep 4, top-8, normalised) or the weighted top-k reduce (4096 tokens x
+    top-8, hidden 7168, bf16 rows gathered through the position map)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    assert tk.tk_init(0) == tk.TkStatus.TK_OK
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    sets = max(1, args.sets)
+    if args.kernel == "cast":
+        n, hidden, group = 32768, 2048, 128
+        name = f"cast_bf16_e4m3_g{group}_ue8m0_n{n}_h{hidden}"
+        w = wl.Workload(name, n, hidden, 2.0, "fp8", group, "ue8m0", None, "uniform")
+        xh = wl.make_x(w, args.seed)  # [n, 2*hidden] bf16 N(0,2) samples, read as [2n, hidden] rows
+        assert xh.size == 2 * n * hidden
+        n2 = 2 * n
+        xs = [torch.from_numpy(xh.view(np.int16)).to(dev) for _ in range(sets)]
+        cs = [torch.empty((n2, hidden), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        ss = [torch.empty((n2, hidden // group), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        del xh
+        nbytes = n2 * (2 * hidden + hidden + hidden // group)
+
+        def step(i):
+            k = i % sets
+            rc = tk.tk_cast_fp8(xs[k], tk.TK_DTYPE_BF16, n2, hidden, group, tk.TK_SCALE_UE8M0, cs[k], ss[k], sh)
+            assert rc == tk.TkStatus.TK_OK, rc
+        metric = "stand-alone bf16->FP8 cast HBM GB/s (frac of peak) at 1 MI355X"
+        config = {"workload": f"cast_bf16_e4m3_g{group}_ue8m0_n{n2}_h{hidden}", "rows": n2, "hidden": hidden,
+                  "group_size": group, "format": "e4m3", "scale": "ue8m0", "input": "bf16 [rows, hidden]"}
+        rows = n2
+        kernel = "cast_kernel"
+    elif args.kernel == "reduce":
+        r = wl.REDUCE_WORKLOADS[wl.REDUCE_HEADLINE]
+        pos, wts, rsc, n_rows = wl.make_routing(r, args.seed)
+        xh = wl.make_expert_rows(r, args.seed, n_rows)
+        xs = [torch.from_numpy(xh.view(np.int16)).to(dev) for _ in range(sets)]
+        del xh
+        pd, wd, rd = (torch.from_numpy(pos).to(dev), torch.from_numpy(wts).to(dev), torch.from_numpy(rsc).to(dev))
+        outs = [torch.empty((r.tokens, r.hidden), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        nbytes = r.algorithmic_bytes(pos)
+
+        def step(i):
+            j = i % sets
+            rc = tk.tk_moe_reduce(xs[j], rd, pd, wd, r.global_scale, r.tokens, r.k, r.hidden, n_rows,
+                                  tk.TK_DTYPE_BF16, outs[j], sh)
+            assert rc == tk.TkStatus.TK_OK, rc
+        metric = "weighted top-k MoE reduce HBM GB/s (frac of peak) at 1 MI355X"
+        config = {"workload": r.name, "tokens": r.tokens, "k": r.k, "experts": r.experts, "hidden": r.hidden,
+                  "n_rows": n_rows, "row_scale": r.row_scale, "global_scale": r.global_scale, "out": "bf16",
+                  "layout": "rows grouped by expert, tokens in order within an expert"}
+        rows = r.tokens
+        kernel = "moe_reduce_kernel"
+    else:
+        T, E, k, ng, tg = 16384, 256, 8, 8, 4
+        key = wl.stream_key("topk_gate", args.seed, "scores")
+        sh_ = wl.uniform(key, 0, T * E).reshape(T, E).astype(np.float32)
+        sc = [torch.from_numpy(sh_).to(dev) for _ in range(sets)]
+        idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(sets)]
+        wt = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(sets)]
+        nbytes = T * (4 * E + 8 * k)
+
+        def step(i):
+            j = i % sets
+            rc = tk.tk_topk_gate(sc[j], T, E, k, ng, tg, 1, idx[j], wt[j], sh)
+            assert rc == tk.TkStatus.TK_OK, rc
+        metric = "deterministic top-k gating tokens/s and HBM GB/s at 1 MI355X"
+        config = {"workload": f"topk_gate_t{T}_e{E}_g{ng}_keep{tg}_top{k}", "tokens": T, "experts": E, "k": k,
+                  "n_group": ng, "topk_group": tg, "normalise": True, "scores": "U(0,1) fp32"}
+        rows = T
+        kernel = "topk_kernel"
+    wall, gpu = _timed(torch, stream, step, args.steps, args.warmup)
+    avg = gpu / args.steps
+    achieved = nbytes / avg / 1e9
+    out = {"metric": metric, "value": round(nbytes * args.steps / wall / 1e9, 3), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp32", "data": "synthetic", "config": config,
+           "rows_per_s": round(rows * args.steps / wall, 1),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(avg * 1e6, 3)},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +349,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce"], default="fused",
+                    help="fused (default): the fused SwiGLU + cast; cast: the stand-alone cast; topk: the gating; "
+                         "reduce: the weighted top-k reduce")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -264,6 +369,9 @@ def main():
 
     import moe_activation_bit_amd as tk
     from moe_activation_bit_amd import workloads as wl
+
+    if args.kernel != "fused":
+        return bench_aux(args, torch, np, tk, wl)
 
     name = args.workload or wl.HEADLINE
     w = wl.WORKLOADS[name]

@@ -214,6 +214,47 @@ tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
 tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
                        int64_t topk_group, int normalise, int32_t* topk_idx, float* topk_weight, void* stream);
 
+/*
+ * tk_moe_reduce: the weighted top-k reduce of the experts' output rows -- the
+ * fused reduce of "【DeepSeek】TileKernels从入门到精通" ch.3, sections
+ * "结算中心的“减法工程”" (routing weights, quantisation scale factors and a
+ * global scale applied in one pass: the expert outputs are read once and the
+ * result written once) and "动态寻址" (rows found through a token/top-k ->
+ * position map).
+ *
+ *   Per token t and column c, over the present slots j = 0..k-1 in order
+ *   (slot j is present when 0 <= pos[t,j] < n_rows; any other entry, such as
+ *   -1 for a dropped slot, contributes nothing and its row is never read):
+ *     f   = RN(topk_weight[t,j] * row_scale[p])   (f = topk_weight[t,j] when
+ *                                                  row_scale is NULL)
+ *     acc = RN(acc + RN(f * x[p,c]))              from acc = +0
+ *     out[t,c] = RN(acc * global_scale), then rounded to the nearest bf16
+ *     (ties to even) for TK_DTYPE_BF16, or kept as fp32 for TK_DTYPE_FP32.
+ *   Every operation is one IEEE fp32 operation, round to nearest even.
+ *
+ *  x            bf16 [n_rows, hidden], row-major, 16-byte aligned (device); may
+ *               be NULL when n_rows == 0.
+ *  row_scale    fp32 [n_rows] (device), 4-byte aligned, or NULL.
+ *  pos          int32 [tokens, k] (device), 4-byte aligned: the row of each
+ *               (token, slot).  Entries are range-checked on the device, so a
+ *               bad entry drops its slot instead of reading out of bounds.
+ *  topk_weight  fp32 [tokens, k] (device), 4-byte aligned.
+ *  global_scale a finite fp32 factor applied once to each sum.
+ *  tokens       0 <= tokens < 2^31;  k: 1..32 (k > 32: TK_ERR_UNSUPPORTED).
+ *  hidden       a positive multiple of 8, at most (2^31-1)/8.
+ *  n_rows       0 <= n_rows < 2^31.
+ *  out_dtype    TK_DTYPE_BF16 or TK_DTYPE_FP32.
+ *  out          [tokens, hidden] of out_dtype (device), 16-byte aligned; it must
+ *               not overlap x, row_scale, pos or topk_weight.
+ * The caller owns every buffer; the call keeps no pointer after it returns and
+ * allocates nothing.  Returns TK_ERR_INVALID_ARG for violated preconditions,
+ * overlapping buffers or misaligned pointers (before any HIP call), TK_OK
+ * without a launch when tokens == 0, TK_ERR_HIP if the launch fails.
+ */
+tk_status tk_moe_reduce(const void* x, const float* row_scale, const int32_t* pos, const float* topk_weight,
+                        float global_scale, int64_t tokens, int64_t k, int64_t hidden, int64_t n_rows,
+                        tk_dtype out_dtype, void* out, void* stream);
+
 /* tk_status_str: a static, human-readable name for a status code. */
 const char* tk_status_str(tk_status status);
 

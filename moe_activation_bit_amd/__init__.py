@@ -1,8 +1,9 @@
-"""Python binding of the MI355X fused SwiGLU + top-k weight + FP8/FP4 cast.
+"""Python binding of the MI355X fused SwiGLU + top-k weight + FP8/FP4 cast,
+the stand-alone cast, the top-k gating and the weighted top-k reduce.
 
 Argument marshalling only: every function here forwards to the C ABI in
-``include/tk.h`` (library ``libtk.so`` built from ``csrc/tk_swiglu_cast.hip``)
-under the same name.  All arithmetic runs in the library's HIP kernels; there
+``include/tk.h`` (library ``libtk.so`` built from ``csrc/*.hip``) under the
+same name.  All arithmetic runs in the library's HIP kernels; there
 is no CPU fallback, and importing a function whose library is missing raises.
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed) or raw
@@ -23,7 +24,7 @@ __all__ = [
     "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "TK_SCALE_FP32_COLMAJOR", "TK_SCALE_UE8M0_COLMAJOR",
     "TK_SCALE_UE8M0_PACKED", "TK_DTYPE_BF16", "TK_DTYPE_FP32", "LIB_PATH", "load_library",
     "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4",
-    "tk_topk_gate", "tk_status_str",
+    "tk_topk_gate", "tk_moe_reduce", "tk_status_str",
 ]
 
 TK_SCALE_FP32 = 0
@@ -60,6 +61,9 @@ SIGNATURES = {
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_topk_gate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_moe_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_float, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -154,6 +158,14 @@ def tk_topk_gate(scores, tokens, experts, k, n_group, topk_group, normalise, top
     return TkStatus(load_library().tk_topk_gate(_ptr(scores), int(tokens), int(experts), int(k), int(n_group),
                                                 int(topk_group), int(bool(normalise)), _ptr(topk_idx),
                                                 _ptr(topk_weight), _stream(stream)))
+
+
+def tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens, k, hidden, n_rows, out_dtype, out,
+                  stream=None) -> TkStatus:
+    """See tk_moe_reduce in include/tk.h."""
+    return TkStatus(load_library().tk_moe_reduce(_ptr(x), _ptr(row_scale), _ptr(pos), _ptr(topk_weight),
+                                                 float(global_scale), int(tokens), int(k), int(hidden), int(n_rows),
+                                                 int(out_dtype), _ptr(out), _stream(stream)))
 
 
 def tk_status_str(status: int) -> str:

@@ -34,7 +34,7 @@ def _run(cmd):
 
 
 OBJ_DIR = os.path.join(HERE, "_build")
-TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip", "tk_topk.hip"]
+TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip", "tk_topk.hip", "tk_reduce.hip"]
 
 
 def _hip_object(src):

@@ -27,7 +27,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["tk_init", "tk_status_str", "tk_swiglu_cast_fp4", "tk_swiglu_cast_fp8",
-                                         "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4", "tk_topk_gate"])
+                                         "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4", "tk_topk_gate",
+                                         "tk_moe_reduce"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -156,3 +157,30 @@ def test_topk_unsupported_and_empty():
     assert topk(experts=256, n_group=1, topk_group=1, k=65) == UNSUPPORTED
     assert topk(experts=72, n_group=3, topk_group=2, k=5) == UNSUPPORTED
     assert topk(tokens=0) == OK
+
+
+def reduce(**kw):
+    a = dict(x=X, row_scale=W, pos=C, topk_weight=S, global_scale=2.5, tokens=4, k=8, hidden=7168, n_rows=32,
+             out_dtype=tk.TK_DTYPE_BF16, out=K, stream=0)
+    a.update(kw)
+    return tk.tk_moe_reduce(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tokens=-1), dict(tokens=2 ** 31), dict(k=0), dict(k=-3), dict(hidden=0), dict(hidden=12), dict(hidden=-8),
+    dict(n_rows=-1), dict(n_rows=2 ** 31), dict(out_dtype=2), dict(out_dtype=-1), dict(global_scale=float("nan")),
+    dict(global_scale=INF), dict(pos=None), dict(topk_weight=None), dict(out=None), dict(x=None),
+    dict(x=X + 8), dict(out=K + 8), dict(pos=C + 2), dict(topk_weight=S + 1), dict(row_scale=W + 2),
+    dict(out=X + 64), dict(out=C), dict(out=S + 4), dict(out=W), dict(k=40, out=X),
+], ids=str)
+def test_moe_reduce_invalid_arguments(kw):
+    assert reduce(**kw) == INVALID
+
+
+def test_moe_reduce_unsupported_and_empty():
+    assert reduce(k=33) == UNSUPPORTED
+    assert reduce(k=64) == UNSUPPORTED
+    assert reduce(tokens=0) == OK
+    assert reduce(tokens=0, x=None, pos=None, topk_weight=None, out=None) == OK
+    # n_rows == 0 lets x be NULL (nothing can be read); with no tokens nothing launches
+    assert reduce(tokens=0, n_rows=0, x=None) == OK
