@@ -1,24 +1,25 @@
 """Benchmark of the fused SwiGLU + top-k weight + FP8/FP4 cast on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+python bench.py --kernel cast|topk|reduce   (the next-row kernels, each on its own workload)
 
-One step = one launch of the fused kernel over one whole batch of the
-workload (inputs resident in HBM).  The timed region is exactly K
-back-to-back steps bracketed by device synchronisations and by two HIP
-events on the launch stream (GPU time per launch = event time / K).  Inputs
-and outputs rotate over several buffer sets whose combined footprint is far
-above the 256 MB Infinity Cache, so every launch streams from HBM.
+One step = one launch of the kernel over one whole batch of the workload
+(inputs resident in HBM).  The timed region is exactly K back-to-back steps
+bracketed by device synchronisations and by two HIP events on the launch
+stream (GPU time per launch = event time / K).  Inputs and outputs rotate
+over several buffer sets whose combined footprint is far above the 256 MB
+Infinity Cache, so every launch streams from HBM.
 
 Prints one JSON line on stdout.  The CPU baseline is the oracle, timed on a
 bounded sample of the same workload's rows on the host's cores.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter runs of
-`bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration`, one with
-`--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`; `bench.py --summarize-pmc
-FETCH.csv WRITE.csv` scales the fused kernel's per-dispatch counters by what
-the same counters read for a plain elementwise copy of known size and writes
-profiles/traffic_<workload>.json (tagged with the kernel source digest; a
-stale record is ignored).
+`bench.py [--kernel K] --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration`,
+one with `--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`; `bench.py [--kernel K]
+--summarize-pmc FETCH.csv WRITE.csv` scales that kernel's per-dispatch counters
+by what the same counters read for a plain elementwise copy of known size and
+writes profiles/traffic_<workload>.json (tagged with the kernel source digest;
+a stale record is ignored).
 """
 from __future__ import annotations
 
@@ -34,29 +35,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
-KERNEL_SOURCES = [os.path.join(ROOT, "moe_activation_bit_amd", "csrc", f)
-                  for f in ("tk_swiglu_cast.hip", "tk_quant.h")]
+
+# Each timed kernel: the sources its counters depend on, and how its name
+# reads in a rocprofv3 trace.
+KERNELS = {
+    "fused": (("tk_swiglu_cast.hip", "tk_quant.h"), r"\bswiglu_cast_kernel<"),
+    "cast": (("tk_cast.hip", "tk_quant.h"), r"\bcast_kernel<"),
+    "reduce": (("tk_reduce.hip",), r"\bmoe_reduce_kernel<"),
+    "topk": (("tk_topk.hip",), r"\btopk_kernel<"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kernel: str = "fused") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in KERNELS[kernel][0]:
+        h.update(open(os.path.join(ROOT, "moe_activation_bit_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str, launches_bytes: float):
+def traffic_for(workload: str, kernel: str = "fused"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -79,41 +87,65 @@ def _pmc_rows(path):
     return list(csv.DictReader(open(path)))
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the fused kernel, scaled by
-    the calibration copy's readings; writes profiles/traffic_<workload>.json."""
+def aux_workload(kernel: str, wl, seed: int):
+    """(workload name, algorithmic bytes per launch) of a bench mode, from the
+    host-side description alone."""
+    if kernel == "fused":
+        raise ValueError("the fused kernel's workloads are in workloads.WORKLOADS")
+    if kernel == "cast":
+        n, hidden, group = 2 * CAST_TOKENS, CAST_HIDDEN, CAST_GROUP
+        return (f"cast_bf16_e4m3_g{group}_ue8m0_n{n}_h{hidden}",
+                n * (2 * hidden + hidden + hidden // group))
+    if kernel == "reduce":
+        r = wl.REDUCE_WORKLOADS[wl.REDUCE_HEADLINE]
+        pos, _, _, _ = wl.make_routing(r, seed)
+        return r.name, r.algorithmic_bytes(pos)
+    T, E, k, ng, tg = TOPK_SHAPE
+    return f"topk_gate_t{T}_e{E}_g{ng}_keep{tg}_top{k}", T * (4 * E + 8 * k)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, workload: str, seed: int):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of one kernel, scaled by the
+    calibration copy's readings; writes profiles/traffic_<workload>.json."""
+    import re
+
     from moe_activation_bit_amd import workloads as wl
 
-    w = wl.WORKLOADS[workload]
-    n = wl.num_rows(w, 0)
+    if kernel == "fused":
+        w = wl.WORKLOADS[workload]
+        algo = w.algorithmic_bytes(wl.num_rows(w, seed))
+    else:
+        workload, algo = aux_workload(kernel, wl, seed)
+    pat = re.compile(KERNELS[kernel][1])
 
     def per_dispatch(rows, counter, pick):
         vals = [float(r["Counter_Value"]) for r in rows
                 if r.get("Counter_Name") == counter and pick(r.get("Kernel_Name", ""))]
         return sum(vals) / len(vals) if vals else None, len(vals)
 
-    fused = lambda k: "swiglu_cast_kernel" in k
+    mine = lambda k: bool(pat.search(k))
     copy = lambda k: "MulFunctor" in k  # torch.mul(src, 1.0, out=dst): the calibration copy
     f_rows, w_rows = _pmc_rows(fetch_csv), _pmc_rows(write_csv)
-    f_kib, nf = per_dispatch(f_rows, "FETCH_SIZE", fused)
-    w_kib, nw = per_dispatch(w_rows, "WRITE_SIZE", fused)
+    f_kib, nf = per_dispatch(f_rows, "FETCH_SIZE", mine)
+    w_kib, nw = per_dispatch(w_rows, "WRITE_SIZE", mine)
     cf_kib, ncf = per_dispatch(f_rows, "FETCH_SIZE", copy)
     cw_kib, ncw = per_dispatch(w_rows, "WRITE_SIZE", copy)
     if None in (f_kib, w_kib, cf_kib, cw_kib):
-        raise SystemExit("counter rows missing: fused %s/%s copy %s/%s" % (nf, nw, ncf, ncw))
+        raise SystemExit("counter rows missing: kernel %s/%s copy %s/%s" % (nf, nw, ncf, ncw))
     fetch_scale = (COPY_CAL_BYTES / 1024.0) / cf_kib
     write_scale = (COPY_CAL_BYTES / 1024.0) / cw_kib
     fetch_bytes = f_kib * 1024.0 * fetch_scale
     write_bytes = w_kib * 1024.0 * write_scale
     rec = {
         "workload": workload,
-        "kernel_source_sha256_16": kernel_source_digest(),
+        "kernel": kernel,
+        "kernel_source_sha256_16": kernel_source_digest(kernel),
         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
         "copy_fetch_kib_per_dispatch": cf_kib, "copy_write_kib_per_dispatch": cw_kib,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_bytes_per_launch": round(fetch_bytes + write_bytes),
-        "algorithmic_bytes_per_launch": w.algorithmic_bytes(n),
-        "dispatches": {"fused_fetch": nf, "fused_write": nw, "copy_fetch": ncf, "copy_write": ncw},
+        "algorithmic_bytes_per_launch": algo,
+        "dispatches": {"kernel_fetch": nf, "kernel_write": nw, "copy_fetch": ncf, "copy_write": ncw},
     }
     out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(out, "w") as fh:
@@ -246,6 +278,10 @@ def _timed(torch, stream, fn, steps, warmup):
     return time.perf_counter() - t0, ev0.elapsed_time(ev1) / 1e3
 
 
+CAST_TOKENS, CAST_HIDDEN, CAST_GROUP = 32768, 2048, 128
+TOPK_SHAPE = (16384, 256, 8, 8, 4)  # tokens, experts, k, groups, groups kept
+
+
 def bench_aux(args, torch, np, tk, wl):
     """The next-row kernels on their own workloads, one JSON line like the
     headline's: the stand-alone cast (bf16 [65536, 2048] -> E4M3, groups of
@@ -258,9 +294,11 @@ def bench_aux(args, torch, np, tk, wl):
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
     sets = max(1, args.sets)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    name, nbytes = aux_workload(args.kernel, wl, args.seed)
     if args.kernel == "cast":
-        n, hidden, group = 32768, 2048, 128
-        name = f"cast_bf16_e4m3_g{group}_ue8m0_n{n}_h{hidden}"
+        n, hidden, group = CAST_TOKENS, CAST_HIDDEN, CAST_GROUP
         w = wl.Workload(name, n, hidden, 2.0, "fp8", group, "ue8m0", None, "uniform")
         xh = wl.make_x(w, args.seed)  # [n, 2*hidden] bf16 N(0,2) samples, read as [2n, hidden] rows
         assert xh.size == 2 * n * hidden
@@ -269,17 +307,15 @@ def bench_aux(args, torch, np, tk, wl):
         cs = [torch.empty((n2, hidden), dtype=torch.uint8, device=dev) for _ in range(sets)]
         ss = [torch.empty((n2, hidden // group), dtype=torch.uint8, device=dev) for _ in range(sets)]
         del xh
-        nbytes = n2 * (2 * hidden + hidden + hidden // group)
 
         def step(i):
             k = i % sets
             rc = tk.tk_cast_fp8(xs[k], tk.TK_DTYPE_BF16, n2, hidden, group, tk.TK_SCALE_UE8M0, cs[k], ss[k], sh)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "stand-alone bf16->FP8 cast HBM GB/s (frac of peak) at 1 MI355X"
-        config = {"workload": f"cast_bf16_e4m3_g{group}_ue8m0_n{n2}_h{hidden}", "rows": n2, "hidden": hidden,
-                  "group_size": group, "format": "e4m3", "scale": "ue8m0", "input": "bf16 [rows, hidden]"}
+        config = {"workload": name, "rows": n2, "hidden": hidden, "group_size": group, "format": "e4m3",
+                  "scale": "ue8m0", "input": "bf16 [rows, hidden]"}
         rows = n2
-        kernel = "cast_kernel"
     elif args.kernel == "reduce":
         r = wl.REDUCE_WORKLOADS[wl.REDUCE_HEADLINE]
         pos, wts, rsc, n_rows = wl.make_routing(r, args.seed)
@@ -288,7 +324,6 @@ def bench_aux(args, torch, np, tk, wl):
         del xh
         pd, wd, rd = (torch.from_numpy(pos).to(dev), torch.from_numpy(wts).to(dev), torch.from_numpy(rsc).to(dev))
         outs = [torch.empty((r.tokens, r.hidden), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
-        nbytes = r.algorithmic_bytes(pos)
 
         def step(i):
             j = i % sets
@@ -296,29 +331,27 @@ def bench_aux(args, torch, np, tk, wl):
                                   tk.TK_DTYPE_BF16, outs[j], sh)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "weighted top-k MoE reduce HBM GB/s (frac of peak) at 1 MI355X"
-        config = {"workload": r.name, "tokens": r.tokens, "k": r.k, "experts": r.experts, "hidden": r.hidden,
+        config = {"workload": name, "tokens": r.tokens, "k": r.k, "experts": r.experts, "hidden": r.hidden,
                   "n_rows": n_rows, "row_scale": r.row_scale, "global_scale": r.global_scale, "out": "bf16",
                   "layout": "rows grouped by expert, tokens in order within an expert"}
         rows = r.tokens
-        kernel = "moe_reduce_kernel"
     else:
-        T, E, k, ng, tg = 16384, 256, 8, 8, 4
+        T, E, k, ng, tg = TOPK_SHAPE
         key = wl.stream_key("topk_gate", args.seed, "scores")
         sh_ = wl.uniform(key, 0, T * E).reshape(T, E).astype(np.float32)
         sc = [torch.from_numpy(sh_).to(dev) for _ in range(sets)]
         idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(sets)]
         wt = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(sets)]
-        nbytes = T * (4 * E + 8 * k)
 
         def step(i):
             j = i % sets
             rc = tk.tk_topk_gate(sc[j], T, E, k, ng, tg, 1, idx[j], wt[j], sh)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "deterministic top-k gating tokens/s and HBM GB/s at 1 MI355X"
-        config = {"workload": f"topk_gate_t{T}_e{E}_g{ng}_keep{tg}_top{k}", "tokens": T, "experts": E, "k": k,
-                  "n_group": ng, "topk_group": tg, "normalise": True, "scores": "U(0,1) fp32"}
+        config = {"workload": name, "tokens": T, "experts": E, "k": k, "n_group": ng, "topk_group": tg,
+                  "normalise": True, "scores": "U(0,1) fp32"}
         rows = T
-        kernel = "topk_kernel"
+    kernel = KERNELS[args.kernel][1].replace("\\b", "").rstrip("<")
     wall, gpu = _timed(torch, stream, step, args.steps, args.warmup)
     avg = gpu / args.steps
     achieved = nbytes / avg / 1e9
@@ -328,8 +361,9 @@ def bench_aux(args, torch, np, tk, wl):
            "dtype": "fp32", "data": "synthetic", "config": config,
            "rows_per_s": round(rows * args.steps / wall, 1),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
-                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(avg * 1e6, 3)},
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(name, args.kernel),
+                        "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
+                        "avg_launch_us": round(avg * 1e6, 3)},
            "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
@@ -356,7 +390,8 @@ def main():
 
     if args.summarize_pmc:
         from moe_activation_bit_amd import workloads as wl
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload or wl.HEADLINE)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel, args.workload or wl.HEADLINE,
+                      args.seed)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -434,7 +469,7 @@ def main():
     value = bytes_per_step * args.steps / elapsed / 1e9
     avg_launch_s = gpu_s / args.steps
     achieved = bytes_per_step / avg_launch_s / 1e9
-    traffic = traffic_for(name, bytes_per_step)
+    traffic = traffic_for(name, "fused")
 
     out = {
         "metric": "fused SwiGLU+quant HBM GB/s (frac of peak) and rows/s at 1 MI355X",
