@@ -11,12 +11,19 @@
 //
 // gfx950 design: one 64-lane wave per token (the pages use a 32-lane warp);
 // lane l holds experts l*C .. l*C+C-1 (C = ceil(experts/64) <= 4), so a group
-// of experts is a block of consecutive lanes.  Group top-2 sums come from an
-// xor-butterfly over the group's lanes; group ranks from wave-uniform reads of
-// every group's sum.  Each of the k picks is a wave-wide max of a 64-bit key
-// (order-preserving score bits above the complemented expert index), so the
-// larger score wins and equal scores go to the smaller index; -0 and +0
-// compare equal.  The winner's own score is read back from its lane.
+// of experts is a block of consecutive lanes and lane order is index order.
+//   1. Each lane sorts its C candidates once, best first, by the key (score
+//      in an order-preserving uint32 map, -0 == +0; then smaller index).
+//   2. Groups: each lane's two best, merged over the group's lanes by an
+//      xor-butterfly; group ranks from wave-uniform reads of every group sum;
+//      lanes of dropped groups empty their lists.
+//   3. k rounds of a tournament between the lanes' list heads: a DPP max of
+//      the head keys (quad_perm, row_half_mirror, row_mirror, then four
+//      v_readlane), the first lane whose head equals it (ballot + s_ff1: the
+//      smallest index among equal scores), the winner's index by v_readlane,
+//      and the winner pops its head.  The running sum takes each pick's value
+//      from its key; the output weights re-read the picks' own scores.
+// Each round is a few dozen VALU/SALU instructions with no LDS traffic.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -35,16 +42,41 @@ __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(u
 __device__ __forceinline__ float ffrom(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // Order-preserving map of a (non-NaN) float to uint32; -0 and +0 map alike.
+// Every non-NaN value maps above 0, which therefore marks "no candidate".
 __device__ __forceinline__ uint32_t ordered(float f)
 {
     const uint32_t b = fbits(f + 0.0f); // -0 + +0 = +0
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The value of a key (a zero comes back as +0).
+__device__ __forceinline__ float unordered(uint32_t h)
+{
+    return ffrom((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+}
+
 // "a beats b": larger score, or equal score and smaller index
 __device__ __forceinline__ bool beats(float sa, uint32_t a, float sb, uint32_t b)
 {
     return sa > sb || (sa == sb && a < b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+// maximum over all 64 lanes (every lane active), as a wave-uniform value
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
+{
+    v = dpp_umax<0xB1>(v);  // quad_perm [1,0,3,2]
+    v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]
+    v = dpp_umax<0x141>(v); // row_half_mirror
+    v = dpp_umax<0x140>(v); // row_mirror: every lane holds its 16-lane row's max
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 
 template <int C>
@@ -59,30 +91,34 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         return;
     const float* s_row = scores + (size_t)t * experts;
 
-    float s[C];
-    bool allowed[C];
+    // ---- 1. this lane's candidates, sorted best first
+    uint32_t key[C], idx[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) {
         const uint32_t e = lane * C + j;
-        allowed[j] = e < experts;
-        s[j] = allowed[j] ? s_row[e] : 0.0f;
+        key[j] = e < experts ? ordered(s_row[e]) : 0u;
+        idx[j] = e;
+    }
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            // (key desc, idx asc): a strict total order, so the sort is exact
+            const bool swap = key[j] > key[j - 1] || (key[j] == key[j - 1] && idx[j] < idx[j - 1]);
+            const uint32_t k0 = key[j - 1], i0 = idx[j - 1];
+            key[j - 1] = swap ? key[j] : k0;
+            idx[j - 1] = swap ? idx[j] : i0;
+            key[j] = swap ? k0 : key[j];
+            idx[j] = swap ? i0 : idx[j];
+        }
     }
 
+    // ---- 2. group selection
     if (n_group > 1) {
-        // the two best values of this lane's experts, then of the group's lanes
-        float a1 = -INFINITY, a2 = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-            if (allowed[j]) {
-                const float v = s[j];
-                if (v > a1) {
-                    a2 = a1;
-                    a1 = v;
-                } else if (v > a2) {
-                    a2 = v;
-                }
-            }
-        }
+        // the group's two best values (a lane's two best are its list head;
+        // the sign of a zero does not matter to the sums' comparisons)
+        float a1 = key[0] ? unordered(key[0]) : -INFINITY;
+        float a2 = (C > 1 && key[C > 1 ? 1 : 0]) ? unordered(key[C > 1 ? 1 : 0]) : -INFINITY;
         for (uint32_t m = 1; m < (1u << gl_log2); m <<= 1) {
             const float b1 = __shfl_xor(a1, (int)m), b2 = __shfl_xor(a2, (int)m);
             const float hi = fmaxf(a1, b1);
@@ -93,61 +129,38 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         const uint32_t my_g = lane >> gl_log2;
         uint32_t rank = 0;
         for (uint32_t h = 0; h < n_group; ++h) {
-            const float gh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(fbits(gsum), h << gl_log2));
+            const float gh = ffrom(__builtin_amdgcn_readlane(fbits(gsum), h << gl_log2));
             rank += beats(gh, h, gsum, my_g) ? 1u : 0u;
         }
-        const bool keep = rank < topk_group;
-#pragma unroll
-        for (int j = 0; j < C; ++j)
-            allowed[j] = allowed[j] && keep;
-    }
-
-    bool taken[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-        taken[j] = false;
-    int32_t my_idx = 0;
-    float my_w = 0.0f, sum = 0.0f;
-    for (uint32_t it = 0; it < k; ++it) {
-        uint32_t hi = 0, lo = 0; // best key of this lane
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-            if (allowed[j] && !taken[j]) {
-                const uint32_t h = ordered(s[j]), l = 0xFFFFFFFFu - (lane * C + j);
-                if (h > hi || (h == hi && l > lo)) {
-                    hi = h;
-                    lo = l;
-                }
-            }
-        }
-        for (int m = 1; m < kWave; m <<= 1) {
-            const uint32_t oh = (uint32_t)__shfl_xor((int)hi, m), ol = (uint32_t)__shfl_xor((int)lo, m);
-            if (oh > hi || (oh == hi && ol > lo)) {
-                hi = oh;
-                lo = ol;
-            }
-        }
-        const uint32_t e = __builtin_amdgcn_readfirstlane(0xFFFFFFFFu - lo);
-        const uint32_t owner = e / C, slot = e - owner * C;
-        uint32_t mine = 0;
-#pragma unroll
-        for (int j = 0; j < C; ++j)
-            if ((uint32_t)j == slot)
-                mine = fbits(s[j]);
-        const float score = ffrom(__builtin_amdgcn_readlane(mine, owner)); // the winner's own value (keeps -0)
-        if (lane == owner) {
+        if (rank >= topk_group) {
 #pragma unroll
             for (int j = 0; j < C; ++j)
-                if ((uint32_t)j == slot)
-                    taken[j] = true;
+                key[j] = 0u;
         }
-        if (lane == it) {
+    }
+
+    // ---- 3. k rounds between the list heads
+    int32_t my_idx = 0;
+    float sum = 0.0f;
+    for (uint32_t it = 0; it < k; ++it) {
+        const uint32_t best = wave_umax(key[0]);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == best);
+        const uint32_t owner = (uint32_t)__builtin_ctzll(hit); // lowest lane = smallest index
+        const uint32_t e = __builtin_amdgcn_readlane(idx[0], owner);
+        if (lane == owner) {
+#pragma unroll
+            for (int j = 0; j + 1 < C; ++j) {
+                key[j] = key[j + 1];
+                idx[j] = idx[j + 1];
+            }
+            key[C - 1] = 0u;
+        }
+        if (lane == it)
             my_idx = (int32_t)e;
-            my_w = score;
-        }
-        sum += score; // best first, as the weights are normalised
+        sum += unordered(best); // best first, as the weights are normalised (+0 for a -0 is the same sum)
     }
     if (lane < k) {
+        const float my_w = s_row[my_idx]; // the pick's own value (keeps -0)
         idx_out[(size_t)t * k + lane] = my_idx;
         w_out[(size_t)t * k + lane] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
     }
