@@ -15,7 +15,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the wrapper at another build of oracle.c (the mutation
+# test loads copies with planted mistakes this way).
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 SOURCE = os.path.join(_HERE, "oracle.c")
 
 FP8 = 8
@@ -27,8 +29,8 @@ FMT_MAX = {FP8: 448.0, FP4: 6.0}
 _lib = None
 
 
-def build_command(out: str = LIB_PATH) -> list:
-    return ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-o", out, SOURCE,
+def build_command(out: str = os.path.join(_HERE, "liboracle.so"), source: str = SOURCE) -> list:
+    return ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-o", out, source,
             "-lquadmath", "-lm"]
 
 

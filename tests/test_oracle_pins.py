@@ -363,3 +363,24 @@ def test_topk_gate_invariants():
     assert (idx1[:, 0] == np.argmax(s, axis=1)).all()         # k = 1: argmax, first index on ties
     _, wn = oracle.topk_gate(np.abs(s), 8, 8, 4, True)
     assert np.allclose(wn.sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_scale_inverse_is_rn_of_fmt_max_over_amax():
+    """Reading r6: codes come from q = RN(y * RN(fmt_max/amax)), not from the
+    reciprocal of the rounded scale.  For amax = 0x1.852eb2p+6 the two
+    inverses differ by one ulp, and y = 0x1.d89422p-3 makes
+    RN(y * RN(448/amax)) exactly 1.0625, the E4M3 midpoint between 1.0 (0x38)
+    and 1.125 (0x39), which goes to the even code 0x38; the other inverse
+    lands one ulp above the midpoint and would give 0x39."""
+    amax = float.fromhex("0x1.852eb2p+6")
+    y = float.fromhex("0x1.d89422p-3")
+    inv = E.div_f32(448.0, amax)
+    assert E.mul_f32(y, inv) == 1.0625
+    assert E.mul_f32(y, E.div_f32(1.0, E.div_f32(amax, 448.0))) > 1.0625
+    row = np.zeros((1, 16), dtype=np.float32)
+    row[0, 0], row[0, 1], row[0, 2] = amax, y, -y
+    codes, scales = oracle.cast(row, 0, 8, 0)
+    want_codes, want_scales = E.cast_row([float(v) for v in row[0]], 0, 8, 0)
+    assert codes[0].tolist() == want_codes
+    assert codes[0, 0] == 0x7E and codes[0, 1] == 0x38 and codes[0, 2] == 0xB8
+    assert scales[0, 0] == np.float32(want_scales[0])
