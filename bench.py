@@ -233,8 +233,9 @@ def stream_ceiling(torch, dev, in_bytes: int, reps: int = 30):
     return res
 
 
-def cpu_baseline(w, seed: int, rows: int):
-    """The oracle on `rows` rows of the workload, split over host threads."""
+def cpu_baseline(w, seed: int, rows: int, single_rows: int = 1024):
+    """The oracle on `rows` rows of the workload, split over host threads (the
+    reported value), and on `single_rows` of them on one thread."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
@@ -247,20 +248,29 @@ def cpu_baseline(w, seed: int, rows: int):
     wt = wl.make_w(w, seed)[:rows]
     fmt = 8 if w.fmt == "fp8" else 4
     sfmt = 0 if w.scale_fmt == "fp32" else 1
+
+    def run(a, b):
+        oracle.swiglu_cast(x[a:b], wt[a:b], w.group_size, w.clamp_limit, fmt, sfmt)
+
     threads = max(1, min(16, os.cpu_count() or 1, rows))
-    spans = np.array_split(np.arange(rows), threads)
+    spans = [s for s in np.array_split(np.arange(rows), threads) if len(s)]
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda s: oracle.swiglu_cast(x[s[0]:s[-1] + 1], wt[s[0]:s[-1] + 1], w.group_size,
-                                                 w.clamp_limit, fmt, sfmt), [s for s in spans if len(s)]))
+    with ThreadPoolExecutor(threads) as ex:  # ctypes calls release the GIL
+        list(ex.map(lambda s: run(int(s[0]), int(s[-1]) + 1), spans))
     dt = time.perf_counter() - t0
+    r1 = min(single_rows, rows)
+    t1 = time.perf_counter()
+    run(0, r1)
+    dt1 = time.perf_counter() - t1
     return {
         "value": round(w.algorithmic_bytes(rows) / dt / 1e9, 6),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {rows} of {n} rows of {w.name} (seed {seed}); {dt:.2f} s wall, "
-                  f"{rows / dt:.1f} rows/s",
+        "sample": f"first {rows} of {n} rows of {w.name} (seed {seed}); {dt:.2f} s wall on {threads} threads "
+                  f"({dt * threads:.1f} thread-s), {rows / dt:.1f} rows/s",
+        "single_thread": {"value": round(w.algorithmic_bytes(r1) / dt1 / 1e9, 6), "unit": "GB/s",
+                          "rows": r1, "seconds": round(dt1, 3)},
     }
 
 
@@ -376,7 +386,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling measurement")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused two-kernel comparison")

@@ -193,17 +193,18 @@ def test_ragged_decode_every_seed():
         assert (wt == 0).any() or n < 5
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["fp8_g128_ue8m0_n32768_h2048", "fp8_per_token_clamp10_n131072_h2048",
                                   "fp4_g32_ue8m0_n65536_h4096"])
-def test_workload_full_size_sampled(name):
+def test_workload_full_size_sampled(name, seed):
     """Full size, launched as the benchmark launches it; the oracle checks a
     sample of rows, properties are checked on every row."""
     w = wl.WORKLOADS[name]
-    n = wl.num_rows(w, 0)
-    say(name, "full size", n)
-    x, wt = wl.make_x(w, 0), wl.make_w(w, 0)
+    n = wl.num_rows(w, seed)
+    say(name, "full size", n, "seed", seed)
+    x, wt = wl.make_x(w, seed), wl.make_w(w, seed)
     got = run_cast(x, wt, w.hidden, w.group_size, w.clamp_limit, fmt_of(w), sfmt_of(w))
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(5 + seed)
     rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n), rng.choice(n, 24, replace=False)]))
     want = oracle_cast(x[rows], wt[rows], w)
     assert_same((got[0][rows], got[1][rows], 0), (want[0], want[1], 0), name)
