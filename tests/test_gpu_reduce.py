@@ -172,3 +172,15 @@ def test_bf16_output_reads_as_torch_bf16():
     assert rc == OK
     want = oracle.moe_reduce(x, pos, w, rs, r.global_scale, True)
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("hidden", [16392, 32768, 65528])
+def test_long_rows_and_one_token(hidden):
+    """Rows longer than any model's hidden size (ragged and not), and a
+    single-token call, against the oracle."""
+    say("reduce long rows", hidden)
+    x, pos, w, rs = random_case(hidden, 9, 8, hidden, 40)
+    got = run_reduce(x, pos, w, rs, 2.5, True)
+    same(got, oracle.moe_reduce(x, pos, w, rs, 2.5, True), f"hidden={hidden}")
+    got = run_reduce(x, pos[:1], w[:1], rs, 2.5, False)
+    same(got, oracle.moe_reduce(x, pos[:1], w[:1], rs, 2.5, False), f"hidden={hidden} one token")

@@ -71,3 +71,31 @@ def test_topk_deepseek_shape_full_size():
     assert np.array_equal(gi[rows], oi) and np.array_equal(gw[rows].view(np.uint32), ow.view(np.uint32))
     assert ((gi >= 0) & (gi < E)).all()
     assert np.allclose(gw.sum(axis=1), 1.0, atol=1e-5)
+
+
+def test_topk_special_values_and_extremes():
+    """-inf and huge negative scores, subnormals, an all-zero row under
+    normalisation (weights stay zero), k equal to the candidate count, one
+    expert, one token."""
+    print("[gpu-case] topk special values", flush=True)
+    E, T = 256, 64
+    u = wl.uniform(wl.stream_key("topk_test", 1, "special"), 0, T * E).reshape(T, E)
+    s = (u - 0.5).astype(np.float32)
+    s[0] = -np.inf
+    s[1, :128] = -np.inf
+    s[2] = np.float32(1e-40) * np.arange(E, dtype=np.float32)  # subnormal scores
+    s[3] = 0.0
+    s[4] = -3.0e38
+    s[5, ::7] = np.inf
+    for ng, tg, k in ((1, 1, 8), (8, 4, 8), (8, 2, 64), (1, 1, 64)):
+        for normalise in (0, 1):
+            if normalise and ng == 1 and k == 64:
+                continue  # sums over infinite scores are not finite; not a gating case
+            gi, gw = run(s, k, ng, tg, normalise)
+            oi, ow = oracle.topk_gate(s, k, ng, tg, bool(normalise))
+            assert np.array_equal(gi, oi), (ng, tg, k, normalise, np.argwhere(gi != oi)[:4])
+            same = (gw.view(np.uint32) == ow.view(np.uint32)) | (np.isnan(gw) & np.isnan(ow))
+            assert same.all(), (ng, tg, k, normalise, np.argwhere(~same)[:4])
+    one = np.array([[0.25]], dtype=np.float32)
+    gi, gw = run(one, 1, 1, 1, 1)
+    assert gi[0, 0] == 0 and gw[0, 0] == 1.0
