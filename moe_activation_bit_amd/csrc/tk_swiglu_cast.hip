@@ -40,6 +40,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "tk.h"
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_forward_kernel(const uint4* _
 constexpr int kMaxDevices = 64;
 struct DeviceState {
     std::mutex mu;
-    bool ready = false;
+    std::atomic<bool> ready{false}; // set last, after cus and the table; read without the lock
     int cus = 0;
 };
 DeviceState g_dev[kMaxDevices];
@@ -329,7 +330,7 @@ tk_status init_device(int dev)
         return TK_ERR_INVALID_ARG;
     DeviceState& st = g_dev[dev];
     std::lock_guard<std::mutex> lock(st.mu);
-    if (st.ready)
+    if (st.ready.load(std::memory_order_acquire))
         return TK_OK;
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess)
@@ -347,7 +348,7 @@ tk_status init_device(int dev)
     }
     if (rc == TK_OK) {
         st.cus = cus;
-        st.ready = true;
+        st.ready.store(true, std::memory_order_release);
     }
     if (prev != dev)
         (void)hipSetDevice(prev);
@@ -487,7 +488,7 @@ tk_status ensure_device(int& dev)
 {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return TK_ERR_HIP;
-    if (!g_dev[dev].ready)
+    if (!g_dev[dev].ready.load(std::memory_order_acquire))
         return init_device(dev);
     return TK_OK;
 }
