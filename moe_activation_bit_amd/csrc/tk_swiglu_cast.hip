@@ -229,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
     LutT* lut = reinterpret_cast<LutT*>(lut_raw);
-    load_lut_to_lds(lut);
 
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t waves_per_block = kThreads / kWaveSize;
@@ -237,6 +236,24 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     // unit bookkeeping (row, step, addresses) in scalar registers
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
+
+    // The table's global loads go out first and the first unit's loads right
+    // behind them; loads return in order, so the table reaches LDS without
+    // waiting for the unit, and the unit's latency overlaps the table fill
+    // (what a launch of a few hundred rows spends most of its time on).
+    constexpr int kLutPerThread = kLutLdsBytes / 16 / kThreads;
+    static_assert(kLutPerThread * 16 * kThreads == kLutLdsBytes, "table split");
+    uint4 lut_part[kLutPerThread];
+#pragma unroll
+    for (int i = 0; i < kLutPerThread; ++i)
+        lut_part[i] = reinterpret_cast<const uint4*>(g_sigma_lut)[i * kThreads + threadIdx.x];
+    Unit<SPU> first;
+    if (wave < p.units)
+        load_unit<SPU, ROWRED, PARTIAL>(p, wave, lane, first);
+#pragma unroll
+    for (int i = 0; i < kLutPerThread; ++i)
+        reinterpret_cast<uint4*>(lut_raw)[i * kThreads + threadIdx.x] = lut_part[i];
+    __syncthreads();
 
     float limit = 0.0f, a_limit = 0.0f;
     if constexpr (CLAMP) {
@@ -246,7 +263,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     }
     unsigned long long clamped = 0;
 
-    for (uint32_t u = wave; u < p.units; u += nwaves) {
+    if (wave < p.units)
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, first, limit, a_limit, clamped);
+    for (uint32_t u = wave + nwaves; u < p.units; u += nwaves) {
         Unit<SPU> d;
         load_unit<SPU, ROWRED, PARTIAL>(p, u, lane, d);
         process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, d, limit, a_limit, clamped);
