@@ -1,0 +1,270 @@
+/*
+ * abi_check.c -- a plain C99 consumer of the library's C ABI (include/tk.h).
+ * Test code: it links the product library, the seeded input generator and the
+ * oracle, and uses nothing else (no Python, no torch).
+ *
+ *   abi_check        argument checks only: every entry point rejects bad
+ *                    arguments before any HIP call (runs without a GPU)
+ *   abi_check gpu    also runs the fused step, the reduce and the gating on
+ *                    device buffers allocated through the HIP C API, and
+ *                    compares every output byte with the oracle
+ *
+ * Exit status 0 when everything matches; each failure is printed.
+ */
+#include <hip/hip_runtime_api.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "tk.h"
+
+/* the seeded generator (moe_activation_bit_amd/csrc/synth.c) */
+uint64_t synth_key(const char* name);
+void synth_uniform(uint64_t key, int64_t first, int64_t count, double* out);
+void synth_normal_bf16(uint64_t key, int64_t first, int64_t count, double sigma, uint16_t* out);
+
+/* the oracle (oracle/oracle.c) */
+int oracle_swiglu_cast(const uint16_t* x, const float* w, int64_t n, int64_t hidden, int64_t group_size,
+                       float clamp_limit, int fmt, int scale_fmt, uint8_t* codes, void* scales,
+                       int64_t* clamped_count);
+int oracle_moe_reduce(const uint16_t* x, const float* row_scale, const int32_t* pos, const float* w,
+                      float global_scale, int64_t tokens, int64_t k, int64_t hidden, int64_t n_rows, int out_bf16,
+                      void* out);
+int oracle_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
+                     int64_t topk_group, int normalise, int32_t* idx_out, float* w_out);
+
+static int failures = 0;
+
+#define EXPECT(cond, ...)                                  \
+    do {                                                   \
+        if (!(cond)) {                                     \
+            ++failures;                                    \
+            printf("FAIL %s:%d: ", __FILE__, __LINE__);    \
+            printf(__VA_ARGS__);                           \
+            printf("\n");                                  \
+        }                                                  \
+    } while (0)
+
+#define HIP_OK(call)                                                                   \
+    do {                                                                               \
+        hipError_t e_ = (call);                                                        \
+        if (e_ != hipSuccess) {                                                        \
+            printf("FAIL %s:%d: %s -> %s\n", __FILE__, __LINE__, #call, hipGetErrorString(e_)); \
+            exit(2);                                                                   \
+        }                                                                              \
+    } while (0)
+
+/* fake device addresses: aligned, far apart, never dereferenced */
+#define FAKE(i) ((void*)(uintptr_t)(0x700000000000ull + (uint64_t)(i) * 0x10000000000ull))
+
+static void check_validation(void)
+{
+    const float inf = INFINITY;
+    /* status strings */
+    EXPECT(strcmp(tk_status_str(TK_OK), "TK_OK") == 0, "status string of TK_OK");
+    EXPECT(strcmp(tk_status_str(TK_ERR_INVALID_ARG), "TK_ERR_INVALID_ARG") == 0, "status string");
+    EXPECT(strcmp(tk_status_str((tk_status)99), "TK_UNKNOWN_STATUS") == 0, "unknown status string");
+
+    /* fused step */
+    EXPECT(tk_swiglu_cast_fp8(FAKE(0), FAKE(1), -1, 1024, 0, inf, TK_SCALE_FP32, FAKE(2), FAKE(3), NULL, NULL) ==
+               TK_ERR_INVALID_ARG, "negative n");
+    EXPECT(tk_swiglu_cast_fp8(FAKE(0), FAKE(1), 4, 12, 0, inf, TK_SCALE_FP32, FAKE(2), FAKE(3), NULL, NULL) ==
+               TK_ERR_INVALID_ARG, "hidden not a multiple of 8");
+    EXPECT(tk_swiglu_cast_fp8(FAKE(0), FAKE(1), 4, 1024, 0, NAN, TK_SCALE_FP32, FAKE(2), FAKE(3), NULL, NULL) ==
+               TK_ERR_INVALID_ARG, "NaN clamp limit");
+    EXPECT(tk_swiglu_cast_fp8(NULL, FAKE(1), 4, 1024, 0, inf, TK_SCALE_FP32, FAKE(2), FAKE(3), NULL, NULL) ==
+               TK_ERR_INVALID_ARG, "null x");
+    EXPECT(tk_swiglu_cast_fp8(FAKE(0), FAKE(1), 4, 1024, 0, inf, TK_SCALE_FP32, FAKE(0), FAKE(3), NULL, NULL) ==
+               TK_ERR_INVALID_ARG, "codes alias x");
+    EXPECT(tk_swiglu_cast_fp4(FAKE(0), FAKE(1), 4, 1024, 32, inf, TK_SCALE_UE8M0, (char*)FAKE(2) + 2, FAKE(3), NULL,
+                              NULL) == TK_ERR_INVALID_ARG, "misaligned FP4 codes");
+    EXPECT(tk_swiglu_cast_fp8(FAKE(0), FAKE(1), 0, 1024, 0, inf, TK_SCALE_FP32, NULL, NULL, NULL, NULL) == TK_OK,
+           "n = 0 is a no-op");
+    EXPECT(tk_swiglu_forward(FAKE(0), NULL, 4, 1024, inf, (float*)FAKE(0), NULL, NULL) == TK_ERR_INVALID_ARG,
+           "swiglu_forward output aliases x");
+
+    /* stand-alone cast */
+    EXPECT(tk_cast_fp8(FAKE(0), (tk_dtype)2, 4, 1024, 128, TK_SCALE_UE8M0, FAKE(2), FAKE(3), NULL) ==
+               TK_ERR_INVALID_ARG, "bad input dtype");
+    EXPECT(tk_cast_fp8(FAKE(0), TK_DTYPE_BF16, 4, 48, 24, TK_SCALE_UE8M0, FAKE(2), FAKE(3), NULL) ==
+               TK_ERR_UNSUPPORTED, "group of 3 lane slots");
+
+    /* gating */
+    EXPECT(tk_topk_gate((const float*)FAKE(0), 4, 256, 8, 3, 1, 0, (int32_t*)FAKE(1), (float*)FAKE(2), NULL) ==
+               TK_ERR_INVALID_ARG, "groups do not divide experts");
+    EXPECT(tk_topk_gate((const float*)FAKE(0), 4, 512, 8, 8, 4, 0, (int32_t*)FAKE(1), (float*)FAKE(2), NULL) ==
+               TK_ERR_UNSUPPORTED, "more than 256 experts");
+
+    /* reduce */
+    EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), 1.0f, 4, 8, 7168, 32,
+                         TK_DTYPE_BF16, FAKE(0), NULL) == TK_ERR_INVALID_ARG, "reduce output aliases x");
+    EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), INFINITY, 4, 8, 7168, 32,
+                         TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_INVALID_ARG, "infinite global scale");
+    EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), 1.0f, 4, 33, 7168, 32,
+                         TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_UNSUPPORTED, "k above 32");
+}
+
+static void* dev_copy(const void* host, size_t bytes)
+{
+    void* d = NULL;
+    HIP_OK(hipMalloc(&d, bytes ? bytes : 1));
+    if (host && bytes)
+        HIP_OK(hipMemcpy(d, host, bytes, hipMemcpyHostToDevice));
+    return d;
+}
+
+static void from_dev(void* host, const void* dev, size_t bytes)
+{
+    HIP_OK(hipMemcpy(host, dev, bytes, hipMemcpyDeviceToHost));
+}
+
+static void check_fused(int fmt, int64_t n, int64_t hidden, int64_t group, tk_scale_fmt sfmt, float clamp,
+                        double sigma, const char* tag)
+{
+    const int64_t groups = hidden / (group ? group : hidden);
+    const size_t xn = (size_t)(n * 2 * hidden);
+    const size_t cbytes = (size_t)(n * (fmt == 8 ? hidden : hidden / 2));
+    const size_t sbytes = (size_t)(n * groups) * (sfmt == TK_SCALE_FP32 ? 4u : 1u);
+    uint16_t* x = malloc(xn * 2);
+    float* w = malloc((size_t)n * 4);
+    double* u = malloc((size_t)n * 8);
+    uint8_t *c_gpu = malloc(cbytes), *c_ref = malloc(cbytes), *s_gpu = malloc(sbytes), *s_ref = malloc(sbytes);
+    char key[64];
+    snprintf(key, sizeof key, "c_abi/%s/x", tag);
+    synth_normal_bf16(synth_key(key), 0, (int64_t)xn, sigma, x);
+    snprintf(key, sizeof key, "c_abi/%s/w", tag);
+    synth_uniform(synth_key(key), 0, n, u);
+    for (int64_t i = 0; i < n; ++i)
+        w[i] = (float)u[i];
+
+    void* dx = dev_copy(x, xn * 2);
+    void* dw = dev_copy(w, (size_t)n * 4);
+    void* dc = dev_copy(NULL, cbytes);
+    void* ds = dev_copy(NULL, sbytes);
+    int64_t zero = 0, cnt_gpu = 0, cnt_ref = 0;
+    void* dk = dev_copy(&zero, 8);
+    tk_status st = fmt == 8 ? tk_swiglu_cast_fp8(dx, dw, n, hidden, group, clamp, sfmt, dc, ds, dk, NULL)
+                            : tk_swiglu_cast_fp4(dx, dw, n, hidden, group, clamp, sfmt, dc, ds, dk, NULL);
+    EXPECT(st == TK_OK, "%s: status %s", tag, tk_status_str(st));
+    HIP_OK(hipDeviceSynchronize());
+    from_dev(c_gpu, dc, cbytes);
+    from_dev(s_gpu, ds, sbytes);
+    from_dev(&cnt_gpu, dk, 8);
+    EXPECT(oracle_swiglu_cast(x, w, n, hidden, group, clamp, fmt, sfmt == TK_SCALE_FP32 ? 0 : 1, c_ref, s_ref,
+                              &cnt_ref) == 0, "%s: oracle failed", tag);
+    EXPECT(memcmp(c_gpu, c_ref, cbytes) == 0, "%s: codes differ", tag);
+    EXPECT(memcmp(s_gpu, s_ref, sbytes) == 0, "%s: scales differ", tag);
+    EXPECT(cnt_gpu == cnt_ref, "%s: clamp count %lld vs %lld", tag, (long long)cnt_gpu, (long long)cnt_ref);
+    HIP_OK(hipFree(dx));
+    HIP_OK(hipFree(dw));
+    HIP_OK(hipFree(dc));
+    HIP_OK(hipFree(ds));
+    HIP_OK(hipFree(dk));
+    free(x);
+    free(w);
+    free(u);
+    free(c_gpu);
+    free(c_ref);
+    free(s_gpu);
+    free(s_ref);
+}
+
+static void check_reduce(void)
+{
+    const int64_t tokens = 50, k = 8, hidden = 1000, n_rows = 300;
+    uint16_t* x = malloc((size_t)(n_rows * hidden) * 2);
+    int32_t* pos = malloc((size_t)(tokens * k) * 4);
+    float* w = malloc((size_t)(tokens * k) * 4);
+    float* rs = malloc((size_t)n_rows * 4);
+    double* u = malloc((size_t)(tokens * k) * 8);
+    uint16_t *o_gpu = malloc((size_t)(tokens * hidden) * 2), *o_ref = malloc((size_t)(tokens * hidden) * 2);
+    synth_normal_bf16(synth_key("c_abi/reduce/x"), 0, n_rows * hidden, 1.0, x);
+    synth_uniform(synth_key("c_abi/reduce/pos"), 0, tokens * k, u);
+    for (int64_t i = 0; i < tokens * k; ++i) /* about 6% dropped (-1), 4% out of range */
+        pos[i] = u[i] < 0.06 ? -1 : u[i] < 0.10 ? (int32_t)(n_rows + 3) : (int32_t)(u[i] * (double)n_rows);
+    synth_uniform(synth_key("c_abi/reduce/w"), 0, tokens * k, u);
+    for (int64_t i = 0; i < tokens * k; ++i)
+        w[i] = (float)(u[i] - 0.25);
+    synth_uniform(synth_key("c_abi/reduce/rs"), 0, n_rows, u);
+    for (int64_t i = 0; i < n_rows; ++i)
+        rs[i] = (float)(0.5 + 1.5 * u[i]);
+
+    void* dx = dev_copy(x, (size_t)(n_rows * hidden) * 2);
+    void* dp = dev_copy(pos, (size_t)(tokens * k) * 4);
+    void* dw = dev_copy(w, (size_t)(tokens * k) * 4);
+    void* dr = dev_copy(rs, (size_t)n_rows * 4);
+    void* dout = dev_copy(NULL, (size_t)(tokens * hidden) * 2);
+    tk_status st = tk_moe_reduce(dx, (const float*)dr, (const int32_t*)dp, (const float*)dw, -1.5f, tokens, k,
+                                 hidden, n_rows, TK_DTYPE_BF16, dout, NULL);
+    EXPECT(st == TK_OK, "reduce: status %s", tk_status_str(st));
+    HIP_OK(hipDeviceSynchronize());
+    from_dev(o_gpu, dout, (size_t)(tokens * hidden) * 2);
+    EXPECT(oracle_moe_reduce(x, rs, pos, w, -1.5f, tokens, k, hidden, n_rows, 1, o_ref) == 0, "reduce: oracle");
+    EXPECT(memcmp(o_gpu, o_ref, (size_t)(tokens * hidden) * 2) == 0, "reduce: outputs differ");
+    HIP_OK(hipFree(dx));
+    HIP_OK(hipFree(dp));
+    HIP_OK(hipFree(dw));
+    HIP_OK(hipFree(dr));
+    HIP_OK(hipFree(dout));
+    free(x);
+    free(pos);
+    free(w);
+    free(rs);
+    free(u);
+    free(o_gpu);
+    free(o_ref);
+}
+
+static void check_topk(void)
+{
+    const int64_t tokens = 100, experts = 256, k = 8;
+    float* s = malloc((size_t)(tokens * experts) * 4);
+    double* u = malloc((size_t)(tokens * experts) * 8);
+    int32_t *i_gpu = malloc((size_t)(tokens * k) * 4), *i_ref = malloc((size_t)(tokens * k) * 4);
+    float *w_gpu = malloc((size_t)(tokens * k) * 4), *w_ref = malloc((size_t)(tokens * k) * 4);
+    synth_uniform(synth_key("c_abi/topk/scores"), 0, tokens * experts, u);
+    for (int64_t i = 0; i < tokens * experts; ++i) /* coarse values: many ties */
+        s[i] = (float)(floor(u[i] * 16.0) / 16.0);
+    void* ds = dev_copy(s, (size_t)(tokens * experts) * 4);
+    void* di = dev_copy(NULL, (size_t)(tokens * k) * 4);
+    void* dw = dev_copy(NULL, (size_t)(tokens * k) * 4);
+    tk_status st = tk_topk_gate((const float*)ds, tokens, experts, k, 8, 4, 1, (int32_t*)di, (float*)dw, NULL);
+    EXPECT(st == TK_OK, "topk: status %s", tk_status_str(st));
+    HIP_OK(hipDeviceSynchronize());
+    from_dev(i_gpu, di, (size_t)(tokens * k) * 4);
+    from_dev(w_gpu, dw, (size_t)(tokens * k) * 4);
+    EXPECT(oracle_topk_gate(s, tokens, experts, k, 8, 4, 1, i_ref, w_ref) == 0, "topk: oracle");
+    EXPECT(memcmp(i_gpu, i_ref, (size_t)(tokens * k) * 4) == 0, "topk: indices differ");
+    EXPECT(memcmp(w_gpu, w_ref, (size_t)(tokens * k) * 4) == 0, "topk: weights differ");
+    HIP_OK(hipFree(ds));
+    HIP_OK(hipFree(di));
+    HIP_OK(hipFree(dw));
+    free(s);
+    free(u);
+    free(i_gpu);
+    free(i_ref);
+    free(w_gpu);
+    free(w_ref);
+}
+
+int main(int argc, char** argv)
+{
+    check_validation();
+    printf("validation checks done (%d failures)\n", failures);
+    if (argc > 1 && strcmp(argv[1], "gpu") == 0) {
+        tk_status st = tk_init(0);
+        EXPECT(st == TK_OK, "tk_init: %s", tk_status_str(st));
+        check_fused(8, 96, 2048, 128, TK_SCALE_UE8M0, INFINITY, 2.0, "fp8_g128_ue8m0");
+        check_fused(4, 33, 4096, 0, TK_SCALE_FP32, 3.0f, 1.5, "fp4_per_token_clamp3");
+        check_fused(8, 7, 1000, 8, TK_SCALE_FP32, INFINITY, 1.0, "fp8_ragged_g8");
+        check_reduce();
+        check_topk();
+        printf("gpu checks done (%d failures)\n", failures);
+    }
+    if (failures == 0)
+        printf("c-abi: ok\n");
+    return failures == 0 ? 0 : 1;
+}
