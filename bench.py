@@ -274,6 +274,36 @@ def cpu_baseline(w, seed: int, rows: int, single_rows: int = 1024):
     }
 
 
+def graph_replay(torch, step, steps: int, nbytes: int):
+    """The same K launches captured once in a HIP graph (torch.cuda.graph) and
+    replayed: GPU time per launch without host launch overhead, which is what
+    bounds the small, latency-bound workloads."""
+    here = lambda: int(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            step(i, here())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = here()  # the capture stream
+        for i in range(steps):
+            step(i, cap)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) / 1e3 / steps
+    return {"launches_per_graph": steps, "us_per_launch": round(per * 1e6, 3),
+            "GBs": round(nbytes / per / 1e9, 3)}
+
+
 def _timed(torch, stream, fn, steps, warmup):
     for i in range(warmup):
         fn(i)
@@ -393,6 +423,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the K launches captured in one HIP graph (reported as graph_replay)")
     ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce"], default="fused",
                     help="fused (default): the fused SwiGLU + cast; cast: the stand-alone cast; topk: the gating; "
                          "reduce: the weighted top-k reduce")
@@ -447,10 +479,10 @@ def main():
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
 
-    def step(i):
+    def step(i, stream_handle=sh):
         s = sets[i % len(sets)]
         rc = fn(s["x"], s["w"], n, w.hidden, w.group_size, clamp, sfmt, s["codes"], s["scales"],
-                s["count"] if w.clamp_limit is not None else None, sh)
+                s["count"] if w.clamp_limit is not None else None, stream_handle)
         if rc != tk.TkStatus.TK_OK:
             raise RuntimeError(tk.tk_status_str(rc))
 
@@ -512,6 +544,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.graph:
+        log("[bench] graph replay ...")
+        out["graph_replay"] = graph_replay(torch, step, args.steps, bytes_per_step)
     if not args.no_unfused:
         log("[bench] unfused two-kernel path ...")
         out["unfused"] = unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, args.steps // 4 or 1, stream,
