@@ -274,6 +274,32 @@ def cpu_baseline(w, seed: int, rows: int, single_rows: int = 1024):
     }
 
 
+def flushed_reps(torch, step, nbytes: int, reps: int = 30, warm: int = 3):
+    """3 warm-up launches, then `reps` launches each preceded by a 1 GiB write
+    and read of a scratch buffer (the 256 MB Infinity Cache holds none of the
+    inputs afterwards) and bracketed by two events; median, min and max."""
+    import statistics
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for i in range(warm):
+        step(i)
+    times = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        flush.max()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / 1e3)
+    del flush
+    med = statistics.median(times)
+    return {"reps": reps, "median_us": round(med * 1e6, 3), "min_us": round(min(times) * 1e6, 3),
+            "max_us": round(max(times) * 1e6, 3), "GBs_median": round(nbytes / med / 1e9, 3),
+            "frac_median": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def graph_replay(torch, step, steps: int, nbytes: int):
     """The same K launches captured once in a HIP graph (torch.cuda.graph) and
     replayed: GPU time per launch without host launch overhead, which is what
@@ -423,6 +449,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--no-flushed", action="store_true",
+                    help="skip the 30 single launches after a 1 GiB cache flush each (protocol_flush30)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the K launches captured in one HIP graph (reported as graph_replay)")
     ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce"], default="fused",
@@ -544,6 +572,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_flushed:
+        log("[bench] 30 flushed reps ...")
+        out["protocol_flush30"] = flushed_reps(torch, step, bytes_per_step)
     if args.graph:
         log("[bench] graph replay ...")
         out["graph_replay"] = graph_replay(torch, step, args.steps, bytes_per_step)
