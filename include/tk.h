@@ -126,8 +126,11 @@ tk_status tk_init(int device);
  * clamp_limit is NaN or <= 0; scale_fmt is unknown; n > 0 and x, codes or
  * scales is NULL; a pointer breaks its alignment; an output overlaps an input.
  * Returns TK_ERR_UNSUPPORTED when the group (in units of 8 columns) is not a
- * power of two up to 64 and not a multiple of 64, or when one group spans more
- * than 8192 columns.
+ * power of two up to 64 and not a multiple of 64; when one group spans more
+ * than 32768 columns; or when a row holds several groups longer than 8192
+ * columns whose number of 512-column steps is odd (groups up to 16384
+ * columns) or not a multiple of 4 (longer groups).  A group longer than 8192
+ * columns is shared by 2 or 4 waves of one workgroup.
  */
 tk_status tk_swiglu_cast_fp8(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
                              int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt,

@@ -25,8 +25,67 @@ namespace {
 
 using namespace tk_detail;
 
+constexpr uint32_t kMaxCastBlocks = 1u << 20; // 2^28 threads: far more than the chip holds
+constexpr uint32_t kMaxCastXwBlocks = 2048;    // multi-wave groups: 8 workgroups per CU
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_float(w & 0xFFFF0000u); }
+
+// Load unit u (SPU steps of one row, 16 or 32 bytes per lane per step),
+// widen it to fp32 and take the lane-local abs-max of every step.
+template <bool F32IN, int SPU, bool ROWRED, bool PARTIAL>
+__device__ __forceinline__ void cast_load_unit(const Params& p, uint32_t u, uint32_t lane, uint32_t& row,
+                                               uint32_t& unit_in_row, uint32_t& step0, uint32_t& nst,
+                                               float (&y)[SPU][8], uint32_t (&mbits)[SPU])
+{
+    constexpr uint32_t kSlotBytes = F32IN ? 32u : 16u;
+    row = u / p.upr;
+    unit_in_row = u - row * p.upr;
+    step0 = unit_in_row * p.spu;
+    nst = ROWRED ? min(p.spu, p.steps_row - step0) : (uint32_t)SPU;
+    const char* xr = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * kSlotBytes);
+    const uint32_t lane_off = (step0 * kWaveSize + lane) * kSlotBytes;
+
+    uint4 raw[SPU][F32IN ? 2 : 1];
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        if (!ROWRED || s < (int)nst) {
+            uint32_t off = lane_off + (uint32_t)s * (kWaveSize * kSlotBytes);
+            if (PARTIAL) // lanes past the row end re-read its last slot
+                off = min(off, (p.slots - 1u) * kSlotBytes);
+            raw[s][0] = load16(reinterpret_cast<const uint4*>(xr + off));
+            if constexpr (F32IN)
+                raw[s][F32IN ? 1 : 0] = load16(reinterpret_cast<const uint4*>(xr + off + 16u));
+        }
+    }
+
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        if (!ROWRED || s < (int)nst) {
+            if constexpr (F32IN) {
+                const uint4 a = raw[s][0], b = raw[s][F32IN ? 1 : 0];
+                const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    y[s][j] = as_float(w[j]);
+            } else {
+                const uint32_t w[4] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    y[s][2 * k] = bf16_lo(w[k]);
+                    y[s][2 * k + 1] = bf16_hi(w[k]);
+                }
+            }
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j += 2)
+                m = fmaxf(m, fmaxf(fabsf(y[s][j]), fabsf(y[s][j + 1])));
+            if (PARTIAL && (step0 + s) * kWaveSize + lane >= p.slots)
+                m = 0.0f;
+            mbits[s] = as_uint(m);
+        }
+    }
+}
 
 template <int FMT, int SFMT, bool F32IN, int SPU, bool ROWRED, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) void cast_kernel(Params p)
@@ -35,58 +94,56 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(Params p)
     const uint32_t waves_per_block = kThreads / kWaveSize;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
-    constexpr uint32_t kSlotBytes = F32IN ? 32u : 16u;
 
     for (uint32_t u = wave; u < p.units; u += nwaves) {
-        const uint32_t row = u / p.upr;
-        const uint32_t unit_in_row = u - row * p.upr;
-        const uint32_t step0 = unit_in_row * p.spu;
-        const uint32_t nst = ROWRED ? min(p.spu, p.steps_row - step0) : (uint32_t)SPU;
-        const char* xr = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * kSlotBytes);
-        const uint32_t lane_off = (step0 * kWaveSize + lane) * kSlotBytes;
-
-        uint4 raw[SPU][F32IN ? 2 : 1];
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            if (!ROWRED || s < (int)nst) {
-                uint32_t off = lane_off + (uint32_t)s * (kWaveSize * kSlotBytes);
-                if (PARTIAL) // lanes past the row end re-read its last slot
-                    off = min(off, (p.slots - 1u) * kSlotBytes);
-                raw[s][0] = load16(reinterpret_cast<const uint4*>(xr + off));
-                if constexpr (F32IN)
-                    raw[s][F32IN ? 1 : 0] = load16(reinterpret_cast<const uint4*>(xr + off + 16u));
-            }
-        }
-
+        uint32_t row, unit_in_row, step0, nst;
         float y[SPU][8];
         uint32_t mbits[SPU];
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            if (!ROWRED || s < (int)nst) {
-                if constexpr (F32IN) {
-                    const uint4 a = raw[s][0], b = raw[s][F32IN ? 1 : 0];
-                    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        y[s][j] = as_float(w[j]);
-                } else {
-                    const uint32_t w[4] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        y[s][2 * k] = bf16_lo(w[k]);
-                        y[s][2 * k + 1] = bf16_hi(w[k]);
-                    }
-                }
-                float m = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 8; j += 2)
-                    m = fmaxf(m, fmaxf(fabsf(y[s][j]), fabsf(y[s][j + 1])));
-                if (PARTIAL && (step0 + s) * kWaveSize + lane >= p.slots)
-                    m = 0.0f;
-                mbits[s] = as_uint(m);
-            }
-        }
+        cast_load_unit<F32IN, SPU, ROWRED, PARTIAL>(p, u, lane, row, unit_in_row, step0, nst, y, mbits);
         quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mbits);
+    }
+}
+
+// Row-reduced groups longer than one wave holds: W waves of a workgroup share
+// one group (each ceil(k/W) of its k steps), their abs-maxes meet in LDS, and
+// every wave quantises its own steps; the group's first wave stores the scale.
+// A workgroup takes passes of 4/W groups, grid-strided over a capped grid (the
+// maxes double-buffered, one barrier per pass; every wave runs the same
+// passes, so all of them reach it).
+template <int FMT, int SFMT, bool F32IN, int SPU, bool PARTIAL, int W>
+__global__ __launch_bounds__(kThreads) void cast_xw_kernel(Params p)
+{
+    constexpr uint32_t kWaves = kThreads / kWaveSize;
+    constexpr uint32_t kGroupsPerPass = kWaves / W;
+    static_assert(kWaves % W == 0, "waves per group must divide the workgroup");
+    __shared__ uint32_t part_max[2][kWaves];
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t slot_in_pass = wib / W, part = wib % W;
+    const uint32_t groups = p.units / W;
+    const uint32_t passes = (groups + kGroupsPerPass - 1) / kGroupsPerPass;
+    uint32_t parity = 0;
+    for (uint32_t it = blockIdx.x; it < passes; it += gridDim.x, parity ^= 1u) {
+        const uint32_t g = it * kGroupsPerPass + slot_in_pass;
+        const bool valid = g < groups; // wave-uniform
+        uint32_t row = 0, unit_in_row = 0, step0 = 0, nst = 0, mb = 0;
+        float y[SPU][8];
+        uint32_t mbits[SPU];
+        if (valid) {
+            cast_load_unit<F32IN, SPU, true, PARTIAL>(p, g * W + part, lane, row, unit_in_row, step0, nst, y,
+                                                       mbits);
+            mb = wave_umax(lane_max<SPU>(mbits, nst));
+        }
+        if (lane == 0)
+            part_max[parity][wib] = mb;
+        __syncthreads();
+        uint32_t gm = 0;
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+            gm = max(gm, part_max[parity][slot_in_pass * W + j]);
+        if (valid)
+            quantize_rowred<FMT, SFMT, SPU, PARTIAL>(p, lane, row, unit_in_row / W, step0, nst, y, gm,
+                                                     part == 0 && lane == 0);
     }
 }
 
@@ -133,9 +190,37 @@ bool dispatch_cast2(const UnitPlan& plan, const Params& p, int blocks, hipStream
                         : launch_cast<FMT, SFMT, F32IN, false, false>(spu, p, blocks, s);
 }
 
+template <int FMT, int SFMT, bool F32IN>
+bool launch_cast_xw(const UnitPlan& plan, const Params& p, hipStream_t s)
+{
+    constexpr int SPU = kMaxStepsPerUnit;
+    // one pass per workgroup up to 2048 workgroups (8 per CU), passes beyond
+    uint32_t blocks = (p.units + (kThreads / kWaveSize) - 1) / (kThreads / kWaveSize);
+    if (blocks > kMaxCastXwBlocks)
+        blocks = kMaxCastXwBlocks;
+#define TK_CAST_XW(PA, WW)                                                                               \
+    if (plan.partial == PA && plan.xwaves == WW) {                                                        \
+        hipLaunchKernelGGL((cast_xw_kernel<FMT, SFMT, F32IN, SPU, PA, WW>), dim3(blocks), dim3(kThreads), 0, s, p); \
+        return true;                                                                                      \
+    }
+    TK_CAST_XW(false, 2u)
+    TK_CAST_XW(false, 4u)
+    TK_CAST_XW(true, 2u)
+    TK_CAST_XW(true, 4u)
+#undef TK_CAST_XW
+    return false;
+}
+
 template <int FMT>
 bool dispatch_cast(int sfmt, bool f32in, const UnitPlan& plan, const Params& p, int blocks, hipStream_t s)
 {
+    if (plan.xwaves > 1) {
+        if (sfmt == TK_SCALE_FP32)
+            return f32in ? launch_cast_xw<FMT, TK_SCALE_FP32, true>(plan, p, s)
+                         : launch_cast_xw<FMT, TK_SCALE_FP32, false>(plan, p, s);
+        return f32in ? launch_cast_xw<FMT, TK_SCALE_UE8M0, true>(plan, p, s)
+                     : launch_cast_xw<FMT, TK_SCALE_UE8M0, false>(plan, p, s);
+    }
     if (sfmt == TK_SCALE_FP32)
         return f32in ? dispatch_cast2<FMT, TK_SCALE_FP32, true>(plan, p, blocks, s)
                      : dispatch_cast2<FMT, TK_SCALE_FP32, false>(plan, p, blocks, s);
@@ -186,7 +271,10 @@ tk_status cast(int fmt, const void* x, int in_dtype, int64_t n, int64_t hidden, 
     p.scale_ld = sp.ld;
 
     const uint32_t waves_per_block = kThreads / kWaveSize;
-    const int blocks = (int)((p.units + waves_per_block - 1) / waves_per_block); // one unit per wave
+    // one unit per wave; a grid past kMaxCastBlocks loops (a launch holds at
+    // most 2^32 work-items)
+    const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
+    const int blocks = (int)(want < kMaxCastBlocks ? want : kMaxCastBlocks);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f32in = in_dtype == TK_DTYPE_FP32;
     const bool ok = fmt == 8 ? dispatch_cast<8>(sp.kind, f32in, plan, p, blocks, s)

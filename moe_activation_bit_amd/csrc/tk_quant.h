@@ -19,7 +19,8 @@ namespace tk_detail {
 
 constexpr int kWaveSize = 64;
 constexpr int kSlotCols = 8;                     // columns per lane per step (16 B of bf16)
-constexpr int kMaxStepsPerUnit = 16;             // largest row-reduced group: 8192 columns
+constexpr int kMaxStepsPerUnit = 16;             // steps one wave holds: 8192 columns
+constexpr int kMaxWavesPerGroup = 4;             // a row-reduced group split over up to 4 waves: 32768 columns
 
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -171,6 +172,42 @@ __device__ __forceinline__ uint4 load16(const uint4* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Lane-local abs-max (bit pattern) over the first nst steps of a unit.
+template <int SPU>
+__device__ __forceinline__ uint32_t lane_max(const uint32_t (&mbits)[SPU], uint32_t nst)
+{
+    uint32_t mb = 0;
+#pragma unroll
+    for (int s = 0; s < SPU; ++s)
+        if (s < (int)nst)
+            mb = max(mb, mbits[s]);
+    return mb;
+}
+
+// Quantise the lane's steps step0 .. step0+nst-1 of one row-reduced group
+// (per-token, or a 512k-column group) whose abs-max bit pattern is mb; the lane
+// given store_scale_here writes the group's scale.
+template <int FMT, int SFMT, int SPU, bool PARTIAL>
+__device__ __forceinline__ void quantize_rowred(const Params& p, uint32_t lane, uint32_t row, uint32_t group,
+                                                uint32_t step0, uint32_t nst, const float (&y)[SPU][8], uint32_t mb,
+                                                bool store_scale_here)
+{
+    uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+    float s32 = 0.0f;
+    uint32_t s8 = 0;
+    const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        if (s < (int)nst) {
+            const uint32_t slot = (step0 + s) * kWaveSize + lane;
+            if (!PARTIAL || slot < p.slots)
+                quantize_store<FMT>(row_codes, slot, y[s], inv);
+        }
+    }
+    if (store_scale_here)
+        store_scale<SFMT>(p, row, group, s32, s8);
+}
+
 // The data of one unit held in registers between its load and its use.
 
 // The quantisation tail of one unit: y[s][j] are the unit's fp32 values (step
@@ -186,25 +223,8 @@ __device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, ui
 {
     uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
     if constexpr (ROWRED) {
-        uint32_t mb = 0;
-#pragma unroll
-        for (int s = 0; s < SPU; ++s)
-            if (s < (int)nst)
-                mb = max(mb, mbits[s]);
-        mb = wave_umax(mb);
-        float s32 = 0.0f;
-        uint32_t s8 = 0;
-        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            if (s < (int)nst) {
-                const uint32_t slot = (step0 + s) * kWaveSize + lane;
-                if (!PARTIAL || slot < p.slots)
-                    quantize_store<FMT>(row_codes, slot, y[s], inv);
-            }
-        }
-        if (lane == 0)
-            store_scale<SFMT>(p, row, unit_in_row, s32, s8);
+        const uint32_t mb = wave_umax(lane_max<SPU>(mbits, nst));
+        quantize_rowred<FMT, SFMT, SPU, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mb, lane == 0);
     } else {
 #pragma unroll
         for (int s = 0; s < SPU; ++s) {
@@ -285,7 +305,8 @@ inline bool scale_spec(int scale_fmt, int64_t n, int64_t groups, ScaleSpec& sp)
 }
 
 // How a [n, hidden] row set is cut into units for a group size G (0 = the
-// whole row).  Fills p.spu, p.upr, p.gl_log2, p.slots, p.steps_row, p.units,
+// whole row).  A row-reduced group longer than kMaxStepsPerUnit steps becomes
+// plan.xwaves consecutive units (one per wave of a workgroup).  Fills p.spu, p.upr, p.gl_log2, p.slots, p.steps_row, p.units,
 // p.groups_row.  Returns TK_ERR_UNSUPPORTED for groups the kernels do not
 // cover.  spu_pref: preferred steps per unit for per-block groups (a power of
 // two up to 4; reduced until it divides the row's steps).
@@ -293,7 +314,26 @@ struct UnitPlan {
     bool rowred = false;
     bool partial = false;
     uint32_t spu_max = 1; // the kernel's compile-time steps per unit
+    uint32_t xwaves = 1;  // row-reduced groups: waves of one workgroup per group (1, 2 or 4)
 };
+
+// A row-reduced group of k steps: one wave up to kMaxStepsPerUnit steps, else
+// split over 2 or 4 waves of one workgroup, each holding ceil(k / waves)
+// steps.  Several such groups in one row need k % waves == 0, so that every
+// part starts at a multiple of its step count.
+inline bool rowred_split(uint32_t k, uint32_t groups_row, uint32_t& waves, uint32_t& spw)
+{
+    if (k <= (uint32_t)kMaxStepsPerUnit) {
+        waves = 1;
+        spw = k;
+        return true;
+    }
+    if (k > (uint32_t)(kMaxStepsPerUnit * kMaxWavesPerGroup))
+        return false;
+    waves = k <= 2u * kMaxStepsPerUnit ? 2u : 4u;
+    spw = (k + waves - 1) / waves;
+    return groups_row == 1 || k % waves == 0;
+}
 
 inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint32_t spu_pref, Params& p,
                             UnitPlan& plan)
@@ -303,12 +343,14 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
     const uint32_t steps_row = (slots + kWaveSize - 1) / kWaveSize;
     const uint32_t gslots = (uint32_t)(G / kSlotCols);
     if (G == hidden) {
-        if (steps_row > (uint32_t)kMaxStepsPerUnit)
+        uint32_t waves = 1, spw = 1;
+        if (!rowred_split(steps_row, 1, waves, spw))
             return TK_ERR_UNSUPPORTED;
         plan.rowred = true;
-        p.spu = steps_row;
-        p.upr = 1;
-        plan.spu_max = pow2_at_least(steps_row);
+        plan.xwaves = waves;
+        p.spu = spw;
+        p.upr = waves;
+        plan.spu_max = pow2_at_least(spw);
     } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
         plan.rowred = false;
         p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
@@ -320,12 +362,15 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
         p.upr = steps_row / spu;
     } else if (gslots % kWaveSize == 0) {
         const uint32_t k = gslots / kWaveSize;
-        if (k > (uint32_t)kMaxStepsPerUnit)
+        const uint32_t groups = (uint32_t)(hidden / G);
+        uint32_t waves = 1, spw = 1;
+        if (!rowred_split(k, groups, waves, spw))
             return TK_ERR_UNSUPPORTED;
         plan.rowred = true;
-        p.spu = k;
-        p.upr = (uint32_t)(hidden / G);
-        plan.spu_max = pow2_at_least(k);
+        plan.xwaves = waves;
+        p.spu = spw;
+        p.upr = groups * waves;
+        plan.spu_max = pow2_at_least(spw);
     } else {
         return TK_ERR_UNSUPPORTED;
     }

@@ -197,6 +197,26 @@ __device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t 
     d.w = p.w ? p.w[d.row] : 1.0f;
 }
 
+// One 8-column step of a loaded unit: ys = w * silu(gate) * up for the lane's
+// columns; returns the lane's abs-max bits (0 for a lane past the row end).
+template <bool CLAMP, bool PARTIAL>
+__device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4 u, float w, bool valid, float limit,
+                                                 float a_limit, unsigned long long& clamped, float (&ys)[8])
+{
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        ys[2 * k] = swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
+        ys[2 * k + 1] = swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
+        m = fmaxf(m, fmaxf(fabsf(ys[2 * k]), fabsf(ys[2 * k + 1])));
+    }
+    if (PARTIAL && !valid)
+        m = 0.0f;
+    return as_uint(m);
+}
+
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
                                              float limit, float a_limit, unsigned long long& clamped)
@@ -204,23 +224,11 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
     float y[SPU][8];
     uint32_t mbits[SPU];
 #pragma unroll
-    for (int s = 0; s < SPU; ++s) {
-        if (!ROWRED || s < (int)d.nst) {
-            const uint32_t gw[4] = {d.g[s].x, d.g[s].y, d.g[s].z, d.g[s].w};
-            const uint32_t uw[4] = {d.u[s].x, d.u[s].y, d.u[s].z, d.u[s].w};
-            const bool valid = !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots;
-            float m = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                y[s][2 * k] = swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], d.w, limit, a_limit, clamped, valid);
-                y[s][2 * k + 1] = swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], d.w, limit, a_limit, clamped, valid);
-                m = fmaxf(m, fmaxf(fabsf(y[s][2 * k]), fabsf(y[s][2 * k + 1])));
-            }
-            if (!valid)
-                m = 0.0f;
-            mbits[s] = as_uint(m);
-        }
-    }
+    for (int s = 0; s < SPU; ++s)
+        if (!ROWRED || s < (int)d.nst)
+            mbits[s] = compute_step<CLAMP, PARTIAL>(lut, d.g[s], d.u[s], d.w,
+                                                    !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots, limit,
+                                                    a_limit, clamped, y[s]);
     quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
 }
 
@@ -279,6 +287,79 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
         process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, d, limit, a_limit, clamped);
     }
 
+    if constexpr (CLAMP) {
+        if (p.count && lane == 0 && clamped)
+            atomicAdd(p.count, clamped);
+    }
+}
+
+// Row-reduced groups longer than one wave holds (per-token rows or 512k-column
+// groups beyond 8192 columns): W waves of a workgroup share one group, each
+// loading and computing ceil(k/W) of its k steps; the waves' abs-maxes meet in
+// LDS (double-buffered, one barrier per pass), then every wave quantises its
+// own steps and the group's first wave stores the scale.  Persistent over
+// passes of 4/W groups per workgroup; every wave runs the same passes, so the
+// barrier is reached by all of them.
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool PARTIAL, int W>
+__global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
+{
+    constexpr uint32_t kWaves = kThreads / kWaveSize;
+    constexpr uint32_t kGroupsPerPass = kWaves / W;
+    static_assert(kWaves % W == 0, "waves per group must divide the workgroup");
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    __shared__ uint32_t part_max[2][kWaves];
+    LutT* lut = reinterpret_cast<LutT*>(lut_raw);
+    load_lut_to_lds(lut);
+
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    uint32_t block = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
+        block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const uint32_t slot_in_pass = wib / W, part = wib % W;
+    const uint32_t groups = p.units / W;
+    const uint32_t passes = (groups + kGroupsPerPass - 1) / kGroupsPerPass;
+
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = p.clamp;
+        a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
+    }
+    unsigned long long clamped = 0;
+    uint32_t parity = 0;
+    for (uint32_t it = block; it < passes; it += gridDim.x, parity ^= 1u) {
+        const uint32_t g = it * kGroupsPerPass + slot_in_pass;
+        const bool valid = g < groups; // wave-uniform
+        float y[SPU][8];
+        uint32_t row = 0, unit_in_row = 0, step0 = 0, nst = 0, mb = 0;
+        if (valid) {
+            Unit<SPU> d; // its raw loads are dead once y is computed
+            uint32_t mbits[SPU];
+            load_unit<SPU, true, PARTIAL>(p, g * W + part, lane, d);
+#pragma unroll
+            for (int s = 0; s < SPU; ++s)
+                if (s < (int)d.nst)
+                    mbits[s] = compute_step<CLAMP, PARTIAL>(lut, d.g[s], d.u[s], d.w,
+                                                            !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots,
+                                                            limit, a_limit, clamped, y[s]);
+            mb = wave_umax(lane_max<SPU>(mbits, d.nst));
+            row = d.row;
+            unit_in_row = d.unit_in_row;
+            step0 = d.step0;
+            nst = d.nst;
+        }
+        if (lane == 0)
+            part_max[parity][wib] = mb;
+        __syncthreads();
+        uint32_t gm = 0;
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+            gm = max(gm, part_max[parity][slot_in_pass * W + j]);
+        if (valid)
+            quantize_rowred<FMT, SFMT, SPU, PARTIAL>(p, lane, row, unit_in_row / W, step0, nst, y, gm,
+                                                     part == 0 && lane == 0);
+    }
     if constexpr (CLAMP) {
         if (p.count && lane == 0 && clamped)
             atomicAdd(p.count, clamped);
@@ -408,6 +489,34 @@ bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
     }
 }
 
+template <int FMT, int SFMT, bool CLAMP>
+bool launch_xw(bool partial, uint32_t waves, const Params& p, int blocks, hipStream_t s)
+{
+    constexpr int SPU = kMaxStepsPerUnit; // ceil(k / W) is 9..16 steps
+#define TK_XW(PA, WW)                                                                                  \
+    if (partial == PA && waves == WW) {                                                                 \
+        hipLaunchKernelGGL((swiglu_cast_xw_kernel<FMT, SFMT, CLAMP, SPU, PA, WW>), dim3(blocks), dim3(kThreads), \
+                           0, s, p);                                                                    \
+        return true;                                                                                    \
+    }
+    TK_XW(false, 2u)
+    TK_XW(false, 4u)
+    TK_XW(true, 2u)
+    TK_XW(true, 4u)
+#undef TK_XW
+    return false;
+}
+
+template <int FMT>
+bool dispatch_xw(int sfmt, bool clamp, bool partial, uint32_t waves, const Params& p, int blocks, hipStream_t s)
+{
+    if (sfmt == TK_SCALE_FP32)
+        return clamp ? launch_xw<FMT, TK_SCALE_FP32, true>(partial, waves, p, blocks, s)
+                     : launch_xw<FMT, TK_SCALE_FP32, false>(partial, waves, p, blocks, s);
+    return clamp ? launch_xw<FMT, TK_SCALE_UE8M0, true>(partial, waves, p, blocks, s)
+                 : launch_xw<FMT, TK_SCALE_UE8M0, false>(partial, waves, p, blocks, s);
+}
+
 template <int FMT>
 bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, const Params& p, int blocks,
               hipStream_t s)
@@ -503,6 +612,7 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     p.clamp = clamp_limit;
 
     const uint32_t waves_per_block = kThreads / kWaveSize;
+    // one unit per wave (a group of xwaves units per xwaves waves) when the grid is not capped
     const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
     const uint32_t cus = (uint32_t)g_dev[dev].cus;
     const uint32_t per_cu = (uint64_t)p.units <= (uint64_t)cus * kSmallUnitsPerCU ? kBlocksPerCUSmall : kBlocksPerCU;
@@ -510,9 +620,13 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     const int blocks = (int)(want < cap ? want : cap);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool ok =
-        fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s)
-                 : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s);
+    bool ok;
+    if (plan.xwaves > 1)
+        ok = fmt == 8 ? dispatch_xw<8>(sp.kind, clamp, plan.partial, plan.xwaves, p, blocks, s)
+                      : dispatch_xw<4>(sp.kind, clamp, plan.partial, plan.xwaves, p, blocks, s);
+    else
+        ok = fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s)
+                      : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s);
     if (!ok)
         return TK_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess)

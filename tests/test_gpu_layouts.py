@@ -19,6 +19,7 @@ LAYOUTS = {tk.TK_SCALE_FP32_COLMAJOR: ("fp32_colmajor", 0), tk.TK_SCALE_UE8M0_CO
 CASES = [  # (rows, hidden, group, fmt, clamp)
     (37, 2048, 128, 8, None), (21, 4096, 32, 4, None), (13, 2048, 0, 8, 10.0), (70, 7168, 128, 8, None),
     (9, 1024, 512, 4, 2.0), (50, 1000, 8, 8, None),
+    (5, 32768, 16384, 8, None), (6, 10000, 0, 4, 10.0),  # groups shared by several waves
 ]
 
 
