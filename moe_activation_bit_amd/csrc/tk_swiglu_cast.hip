@@ -122,12 +122,21 @@ __global__ void sigma_lut_init_kernel()
 // Kernel
 // ---------------------------------------------------------------------------
 typedef float2 LutT;
+// The whole table into LDS by a workgroup of kThreads threads: every thread's
+// loads go out together, then the stores, then one barrier.
 __device__ __forceinline__ void load_lut_to_lds(float2* lut)
 {
+    constexpr int kPer = kLutSize / 2 / kThreads; // 16-byte pieces per thread
+    static_assert(kPer * kThreads * 2 == kLutSize, "table split");
     const uint4* src = reinterpret_cast<const uint4*>(g_sigma_lut);
     uint4* dst = reinterpret_cast<uint4*>(lut);
-    for (int i = threadIdx.x; i < kLutSize / 2; i += blockDim.x)
-        dst[i] = src[i];
+    uint4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        v[i] = src[i * kThreads + threadIdx.x];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        dst[i * kThreads + threadIdx.x] = v[i];
     __syncthreads();
 }
 // sigma(g) for a gate whose bf16 bits sit in bits [POS, POS+16) of `word`;
@@ -217,6 +226,60 @@ __device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4
     return as_uint(m);
 }
 
+// Row-reduced units of kStreamMinSteps steps or more: the loads run kStreamDepth
+// steps ahead of the arithmetic instead of all being issued up front, so a
+// wave computes while its next steps are in flight and holds the raw data of
+// only kStreamDepth steps (the unit's y stays in registers for the quantise
+// pass).  Fills y and mbits of steps 0 .. nst-1 of unit u.
+constexpr int kStreamMinSteps = 8;
+constexpr int kStreamDepth = 4;
+
+template <bool CLAMP, int SPU, bool PARTIAL>
+__device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, uint32_t lane, uint32_t u, float limit,
+                                            float a_limit, unsigned long long& clamped, uint32_t& row,
+                                            uint32_t& unit_in_row, uint32_t& step0, uint32_t& nst, float (&y)[SPU][8],
+                                            uint32_t (&mbits)[SPU])
+{
+    constexpr int D = kStreamDepth;
+    row = u / p.upr;
+    unit_in_row = u - row * p.upr;
+    step0 = unit_in_row * p.spu;
+    nst = min(p.spu, p.steps_row - step0);
+    const char* xg = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * 32u);
+    const char* xu = xg + p.slots * 16u;
+    const uint32_t lane_off = (step0 * kWaveSize + lane) * 16u;
+    const float w = p.w ? p.w[row] : 1.0f;
+    // Every load is issued unconditionally (a step past the unit's end
+    // re-reads the unit's last step, already in cache) so that no load sits
+    // under a branch: the wait before each step then counts only the loads
+    // still ahead of it.
+    const uint32_t last = nst - 1u;
+    const uint32_t row_end = (p.slots - 1u) * 16u;
+    auto step_off = [&](int s) {
+        uint32_t off = lane_off + min((uint32_t)s, last) * (kWaveSize * 16u);
+        if (PARTIAL) // lanes past the row end re-read its last slot
+            off = min(off, row_end);
+        return off;
+    };
+    uint4 gq[D], uq[D];
+#pragma unroll
+    for (int s = 0; s < D && s < SPU; ++s) {
+        gq[s] = load16(reinterpret_cast<const uint4*>(xg + step_off(s)));
+        uq[s] = load16(reinterpret_cast<const uint4*>(xu + step_off(s)));
+    }
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        const uint4 g = gq[s % D], uu = uq[s % D];
+        if (s + D < SPU) {
+            gq[s % D] = load16(reinterpret_cast<const uint4*>(xg + step_off(s + D)));
+            uq[s % D] = load16(reinterpret_cast<const uint4*>(xu + step_off(s + D)));
+        }
+        if (s < (int)nst)
+            mbits[s] = compute_step<CLAMP, PARTIAL>(lut, g, uu, w, !PARTIAL || (step0 + s) * kWaveSize + lane < p.slots,
+                                                    limit, a_limit, clamped, y[s]);
+    }
+}
+
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
                                              float limit, float a_limit, unsigned long long& clamped)
@@ -230,6 +293,32 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
                                                     !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots, limit,
                                                     a_limit, clamped, y[s]);
     quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
+}
+
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool PARTIAL>
+__device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut, uint32_t lane, uint32_t wave,
+                                                     uint32_t nwaves)
+{
+    load_lut_to_lds(lut);
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = p.clamp;
+        a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
+    }
+    unsigned long long clamped = 0;
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        float y[SPU][8];
+        uint32_t mbits[SPU];
+        uint32_t row, unit_in_row, step0, nst;
+        stream_unit<CLAMP, SPU, PARTIAL>(p, lut, lane, u, limit, a_limit, clamped, row, unit_in_row, step0, nst, y,
+                                         mbits);
+        quantize_unit<FMT, SFMT, SPU, true, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mbits);
+    }
+    if constexpr (CLAMP) {
+        if (p.count && lane == 0 && clamped)
+            atomicAdd(p.count, clamped);
+    }
 }
 
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
@@ -252,6 +341,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     // unit bookkeeping (row, step, addresses) in scalar registers
     const uint32_t wave = __builtin_amdgcn_readfirstlane(block * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
+    if constexpr (ROWRED && SPU >= kStreamMinSteps) {
+        streamed_rowred_loop<FMT, SFMT, CLAMP, SPU, PARTIAL>(p, lut, lane, wave, nwaves);
+        return;
+    }
 
     // The table's global loads go out first and the first unit's loads right
     // behind them; loads return in order, so the table reaches LDS without
@@ -334,20 +427,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
         float y[SPU][8];
         uint32_t row = 0, unit_in_row = 0, step0 = 0, nst = 0, mb = 0;
         if (valid) {
-            Unit<SPU> d; // its raw loads are dead once y is computed
             uint32_t mbits[SPU];
-            load_unit<SPU, true, PARTIAL>(p, g * W + part, lane, d);
-#pragma unroll
-            for (int s = 0; s < SPU; ++s)
-                if (s < (int)d.nst)
-                    mbits[s] = compute_step<CLAMP, PARTIAL>(lut, d.g[s], d.u[s], d.w,
-                                                            !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots,
-                                                            limit, a_limit, clamped, y[s]);
-            mb = wave_umax(lane_max<SPU>(mbits, d.nst));
-            row = d.row;
-            unit_in_row = d.unit_in_row;
-            step0 = d.step0;
-            nst = d.nst;
+            stream_unit<CLAMP, SPU, PARTIAL>(p, lut, lane, g * W + part, limit, a_limit, clamped, row, unit_in_row,
+                                             step0, nst, y, mbits);
+            mb = wave_umax(lane_max<SPU>(mbits, nst));
         }
         if (lane == 0)
             part_max[parity][wib] = mb;

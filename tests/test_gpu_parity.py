@@ -224,16 +224,34 @@ SHAPES = [  # (hidden, group, fmt, scale_fmt, clamp, weighted)
     (2048, 256, 8, 0, None, True), (2048, 512, 4, 1, None, True), (2048, 1024, 8, 1, 3.0, True),
     (3072, 1536, 8, 0, None, True), (8192, 0, 8, 0, 5.0, True), (8192, 0, 4, 1, None, False), (7168, 128, 4, 0, None, True),
     (512, 0, 4, 0, None, True), (1536, 0, 8, 1, None, True), (64, 32, 8, 0, None, True),
+    # row-reduced units of 8..16 steps (loads streamed a few steps ahead)
+    (4096, 0, 8, 1, 10.0, True), (7168, 0, 8, 0, None, True), (5000, 0, 4, 0, 3.0, True), (2600, 0, 8, 1, None, True),
+    (16384, 8192, 8, 0, None, True), (12288, 4096, 4, 1, 2.0, True),
 ]
+
+
+def planned(hidden, group):
+    """Whether the library covers (hidden, group): groups of 2^j <= 64 lane
+    slots, or of k whole 512-column steps with k <= 64 (k > 16 split over 2 or
+    4 waves, several groups in a row only when k divides evenly)."""
+    slots, G = hidden // 8, group or hidden
+    gslots = G // 8
+    if group and (gslots & (gslots - 1)) == 0 and gslots <= 64:
+        return True
+    if group == 0:
+        k = (slots + 63) // 64
+        return k <= 64
+    if gslots % 64:
+        return False
+    k = gslots // 64
+    waves = 1 if k <= 16 else 2 if k <= 32 else 4
+    return k <= 64 and (hidden == G or k % waves == 0)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=str)
 def test_shapes_groups_and_formats(shape):
     hidden, group, fmt, sfmt, clamp, weighted = shape
-    slots = hidden // 8
-    gslots = (group or hidden) // 8
-    supported = group == 0 and slots <= 16 * 64 or (group and ((gslots & (gslots - 1)) == 0 and gslots <= 64
-                                                              or gslots % 64 == 0 and gslots // 64 <= 16))
+    supported = planned(hidden, group)
     base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
     rows = 67
     say("shape", shape)
