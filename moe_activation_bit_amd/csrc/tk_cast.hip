@@ -166,6 +166,13 @@ bool launch_cast(int spu_max, const Params& p, int blocks, hipStream_t s)
             return true;
         }
         return false;
+    case 12:
+        if constexpr (ROWRED) {
+            hipLaunchKernelGGL((cast_kernel<FMT, SFMT, F32IN, 12, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads),
+                               0, s, p);
+            return true;
+        }
+        return false;
     case 16:
         if constexpr (ROWRED) {
             hipLaunchKernelGGL((cast_kernel<FMT, SFMT, F32IN, 16, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads),
@@ -193,20 +200,24 @@ bool dispatch_cast2(const UnitPlan& plan, const Params& p, int blocks, hipStream
 template <int FMT, int SFMT, bool F32IN>
 bool launch_cast_xw(const UnitPlan& plan, const Params& p, hipStream_t s)
 {
-    constexpr int SPU = kMaxStepsPerUnit;
     // one pass per workgroup up to 2048 workgroups (8 per CU), passes beyond
     uint32_t blocks = (p.units + (kThreads / kWaveSize) - 1) / (kThreads / kWaveSize);
     if (blocks > kMaxCastXwBlocks)
         blocks = kMaxCastXwBlocks;
-#define TK_CAST_XW(PA, WW)                                                                               \
-    if (plan.partial == PA && plan.xwaves == WW) {                                                        \
-        hipLaunchKernelGGL((cast_xw_kernel<FMT, SFMT, F32IN, SPU, PA, WW>), dim3(blocks), dim3(kThreads), 0, s, p); \
+#define TK_CAST_XW(SP, PA, WW)                                                                           \
+    if (plan.spu_max == SP && plan.partial == PA && plan.xwaves == WW) {                                  \
+        hipLaunchKernelGGL((cast_xw_kernel<FMT, SFMT, F32IN, SP, PA, WW>), dim3(blocks), dim3(kThreads), 0, s, p); \
         return true;                                                                                      \
     }
-    TK_CAST_XW(false, 2u)
-    TK_CAST_XW(false, 4u)
-    TK_CAST_XW(true, 2u)
-    TK_CAST_XW(true, 4u)
+    // a wave's share, ceil(k / W), is 9..16 steps
+    TK_CAST_XW(12u, false, 2u)
+    TK_CAST_XW(12u, false, 4u)
+    TK_CAST_XW(12u, true, 2u)
+    TK_CAST_XW(12u, true, 4u)
+    TK_CAST_XW(16u, false, 2u)
+    TK_CAST_XW(16u, false, 4u)
+    TK_CAST_XW(16u, true, 2u)
+    TK_CAST_XW(16u, true, 4u)
 #undef TK_CAST_XW
     return false;
 }

@@ -255,12 +255,13 @@ inline bool overlaps(const void* a, size_t an, const void* b, size_t bn)
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-inline uint32_t pow2_at_least(uint32_t v)
+// The compile-time step count a row-reduced unit of k <= 16 steps runs in: the
+// smallest of 1, 2, 4, 8, 12, 16 that holds it (steps past k are not computed).
+inline uint32_t template_steps(uint32_t k)
 {
-    uint32_t p = 1;
-    while (p < v)
-        p <<= 1;
-    return p;
+    if (k <= 2)
+        return k;
+    return k <= 4 ? 4u : k <= 8 ? 8u : k <= 12 ? 12u : 16u;
 }
 
 // A tk_scale_fmt value split into the value kind (TK_SCALE_FP32 or
@@ -313,7 +314,7 @@ inline bool scale_spec(int scale_fmt, int64_t n, int64_t groups, ScaleSpec& sp)
 struct UnitPlan {
     bool rowred = false;
     bool partial = false;
-    uint32_t spu_max = 1; // the kernel's compile-time steps per unit
+    uint32_t spu_max = 1; // the kernel's compile-time steps per unit (per wave for split groups)
     uint32_t xwaves = 1;  // row-reduced groups: waves of one workgroup per group (1, 2 or 4)
 };
 
@@ -350,7 +351,7 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
         plan.xwaves = waves;
         p.spu = spw;
         p.upr = waves;
-        plan.spu_max = pow2_at_least(spw);
+        plan.spu_max = template_steps(spw);
     } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
         plan.rowred = false;
         p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
@@ -370,7 +371,7 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
         plan.xwaves = waves;
         p.spu = spw;
         p.upr = groups * waves;
-        plan.spu_max = pow2_at_least(spw);
+        plan.spu_max = template_steps(spw);
     } else {
         return TK_ERR_UNSUPPORTED;
     }

@@ -565,6 +565,9 @@ bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
     case 8:
         if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 8, ROWRED, PARTIAL>(p, blocks, stream); return true; }
         return false;
+    case 12:
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 12, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        return false;
     case 16:
         if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 16, ROWRED, PARTIAL>(p, blocks, stream); return true; }
         return false;
@@ -573,31 +576,36 @@ bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
 }
 
 template <int FMT, int SFMT, bool CLAMP>
-bool launch_xw(bool partial, uint32_t waves, const Params& p, int blocks, hipStream_t s)
+bool launch_xw(bool partial, uint32_t waves, uint32_t spu_max, const Params& p, int blocks, hipStream_t s)
 {
-    constexpr int SPU = kMaxStepsPerUnit; // ceil(k / W) is 9..16 steps
-#define TK_XW(PA, WW)                                                                                  \
-    if (partial == PA && waves == WW) {                                                                 \
-        hipLaunchKernelGGL((swiglu_cast_xw_kernel<FMT, SFMT, CLAMP, SPU, PA, WW>), dim3(blocks), dim3(kThreads), \
+#define TK_XW(SP, PA, WW)                                                                              \
+    if (spu_max == SP && partial == PA && waves == WW) {                                                \
+        hipLaunchKernelGGL((swiglu_cast_xw_kernel<FMT, SFMT, CLAMP, SP, PA, WW>), dim3(blocks), dim3(kThreads), \
                            0, s, p);                                                                    \
         return true;                                                                                    \
     }
-    TK_XW(false, 2u)
-    TK_XW(false, 4u)
-    TK_XW(true, 2u)
-    TK_XW(true, 4u)
+    // a wave's share, ceil(k / W), is 9..16 steps
+    TK_XW(12u, false, 2u)
+    TK_XW(12u, false, 4u)
+    TK_XW(12u, true, 2u)
+    TK_XW(12u, true, 4u)
+    TK_XW(16u, false, 2u)
+    TK_XW(16u, false, 4u)
+    TK_XW(16u, true, 2u)
+    TK_XW(16u, true, 4u)
 #undef TK_XW
     return false;
 }
 
 template <int FMT>
-bool dispatch_xw(int sfmt, bool clamp, bool partial, uint32_t waves, const Params& p, int blocks, hipStream_t s)
+bool dispatch_xw(int sfmt, bool clamp, bool partial, uint32_t waves, uint32_t spu_max, const Params& p, int blocks,
+                 hipStream_t s)
 {
     if (sfmt == TK_SCALE_FP32)
-        return clamp ? launch_xw<FMT, TK_SCALE_FP32, true>(partial, waves, p, blocks, s)
-                     : launch_xw<FMT, TK_SCALE_FP32, false>(partial, waves, p, blocks, s);
-    return clamp ? launch_xw<FMT, TK_SCALE_UE8M0, true>(partial, waves, p, blocks, s)
-                 : launch_xw<FMT, TK_SCALE_UE8M0, false>(partial, waves, p, blocks, s);
+        return clamp ? launch_xw<FMT, TK_SCALE_FP32, true>(partial, waves, spu_max, p, blocks, s)
+                     : launch_xw<FMT, TK_SCALE_FP32, false>(partial, waves, spu_max, p, blocks, s);
+    return clamp ? launch_xw<FMT, TK_SCALE_UE8M0, true>(partial, waves, spu_max, p, blocks, s)
+                 : launch_xw<FMT, TK_SCALE_UE8M0, false>(partial, waves, spu_max, p, blocks, s);
 }
 
 template <int FMT>
@@ -705,8 +713,8 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool ok;
     if (plan.xwaves > 1)
-        ok = fmt == 8 ? dispatch_xw<8>(sp.kind, clamp, plan.partial, plan.xwaves, p, blocks, s)
-                      : dispatch_xw<4>(sp.kind, clamp, plan.partial, plan.xwaves, p, blocks, s);
+        ok = fmt == 8 ? dispatch_xw<8>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s)
+                      : dispatch_xw<4>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s);
     else
         ok = fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s)
                       : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s);

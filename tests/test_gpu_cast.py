@@ -51,7 +51,7 @@ def same(got, want, what):
 
 CASES = [  # (hidden, group, fmt, scale_fmt)
     (2048, 128, 8, 1), (2048, 0, 8, 0), (4096, 32, 4, 1), (7168, 128, 8, 0), (1000, 8, 4, 0), (1000, 0, 8, 1),
-    (2048, 1024, 4, 1), (64, 32, 8, 0), (8192, 0, 4, 0),
+    (2048, 1024, 4, 1), (64, 32, 8, 0), (8192, 0, 4, 0), (6144, 0, 8, 1), (5000, 0, 4, 0),
 ]
 
 

@@ -226,7 +226,8 @@ SHAPES = [  # (hidden, group, fmt, scale_fmt, clamp, weighted)
     (512, 0, 4, 0, None, True), (1536, 0, 8, 1, None, True), (64, 32, 8, 0, None, True),
     # row-reduced units of 8..16 steps (loads streamed a few steps ahead)
     (4096, 0, 8, 1, 10.0, True), (7168, 0, 8, 0, None, True), (5000, 0, 4, 0, 3.0, True), (2600, 0, 8, 1, None, True),
-    (16384, 8192, 8, 0, None, True), (12288, 4096, 4, 1, 2.0, True),
+    (16384, 8192, 8, 0, None, True), (12288, 4096, 4, 1, 2.0, True), (6144, 0, 8, 1, 10.0, False),
+    (4608, 0, 4, 0, None, True),
 ]
 
 
