@@ -249,10 +249,14 @@ __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, ui
     const char* xu = xg + p.slots * 16u;
     const uint32_t lane_off = (step0 * kWaveSize + lane) * 16u;
     const float w = p.w ? p.w[row] : 1.0f;
-    // Every load is issued unconditionally (a step past the unit's end
-    // re-reads the unit's last step, already in cache) so that no load sits
-    // under a branch: the wait before each step then counts only the loads
-    // still ahead of it.
+    // Every load is issued unconditionally so that no load sits under a
+    // branch: the wait before each step then counts only the loads still
+    // ahead of it.  A step past the unit's end reads the first KiB of the
+    // sigmoid table in global memory (hot in cache: every workgroup reads it),
+    // except in the variants where that address would push the kernel past
+    // 256 VGPRs (one workgroup per CU instead of two): the clamp variants and
+    // 16-step units of ragged rows re-read the unit's last step instead.
+    constexpr bool kSpareRead = !CLAMP && !(PARTIAL && SPU > 12);
     const uint32_t last = nst - 1u;
     const uint32_t row_end = (p.slots - 1u) * 16u;
     auto step_off = [&](int s) {
@@ -261,18 +265,25 @@ __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, ui
             off = min(off, row_end);
         return off;
     };
+    const char* spare = reinterpret_cast<const char*>(g_sigma_lut) + lane * 16u;
+    auto addr = [&](const char* half, int s) {
+        if constexpr (!kSpareRead)
+            return reinterpret_cast<const uint4*>(half + step_off(s));
+        else
+            return reinterpret_cast<const uint4*>(s < (int)nst ? half + step_off(s) : spare);
+    };
     uint4 gq[D], uq[D];
 #pragma unroll
     for (int s = 0; s < D && s < SPU; ++s) {
-        gq[s] = load16(reinterpret_cast<const uint4*>(xg + step_off(s)));
-        uq[s] = load16(reinterpret_cast<const uint4*>(xu + step_off(s)));
+        gq[s] = load16(addr(xg, s));
+        uq[s] = load16(addr(xu, s));
     }
 #pragma unroll
     for (int s = 0; s < SPU; ++s) {
         const uint4 g = gq[s % D], uu = uq[s % D];
         if (s + D < SPU) {
-            gq[s % D] = load16(reinterpret_cast<const uint4*>(xg + step_off(s + D)));
-            uq[s % D] = load16(reinterpret_cast<const uint4*>(xu + step_off(s + D)));
+            gq[s % D] = load16(addr(xg, s + D));
+            uq[s % D] = load16(addr(xu, s + D));
         }
         if (s < (int)nst)
             mbits[s] = compute_step<CLAMP, PARTIAL>(lut, g, uu, w, !PARTIAL || (step0 + s) * kWaveSize + lane < p.slots,
