@@ -3,8 +3,10 @@ the stand-alone cast, the top-k gating and the weighted top-k reduce.
 
 Argument marshalling only: every function here forwards to the C ABI in
 ``include/tk.h`` (library ``libtk.so`` built from ``csrc/*.hip``) under the
-same name.  All arithmetic runs in the library's HIP kernels; there
-is no CPU fallback, and importing a function whose library is missing raises.
+same name, through the small CPython extension ``_tkpy`` (``csrc/tk_py.c``,
+a fraction of a microsecond per call where ctypes took a few).  All
+arithmetic runs in the library's HIP kernels; there is no CPU fallback, and
+calling a function whose library or extension is missing raises.
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed) or raw
 device addresses as ints; ``None`` is a null pointer.  ``stream`` defaults to
@@ -22,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libtk.so")
 
 __all__ = [
     "TkStatus", "TK_SCALE_FP32", "TK_SCALE_UE8M0", "TK_SCALE_FP32_COLMAJOR", "TK_SCALE_UE8M0_COLMAJOR",
-    "TK_SCALE_UE8M0_PACKED", "TK_DTYPE_BF16", "TK_DTYPE_FP32", "LIB_PATH", "load_library",
+    "TK_SCALE_UE8M0_PACKED", "TK_DTYPE_BF16", "TK_DTYPE_FP32", "LIB_PATH", "load_library", "load_extension",
     "tk_init", "tk_swiglu_cast_fp8", "tk_swiglu_cast_fp4", "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4",
     "tk_topk_gate", "tk_moe_reduce", "tk_status_str",
 ]
@@ -84,89 +86,86 @@ def load_library() -> ctypes.CDLL:
     return _lib
 
 
-def _ptr(t: Any) -> Optional[int]:
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    return int(t.data_ptr())
+EXT_NAME = "_tkpy"  # the CPython extension that marshals arguments to libtk.so (csrc/tk_py.c)
+_ext = None
+_STATUS = tuple(TkStatus(i) for i in range(len(TkStatus)))
 
 
-def _stream(stream: Any) -> Optional[int]:
-    if stream is None:
-        import torch
-        return int(torch.cuda.current_stream().cuda_stream)
-    if isinstance(stream, int):
-        return stream
-    return int(stream.cuda_stream)
+def _current_stream() -> int:
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def load_extension():
+    """Import the argument-marshalling extension (fails loudly when it has not
+    been built); its default stream is torch's current stream."""
+    global _ext
+    if _ext is None:
+        load_library()
+        import importlib
+        try:
+            mod = importlib.import_module(f"{__name__}.{EXT_NAME}")
+        except ImportError as e:
+            raise RuntimeError(f"{EXT_NAME} is missing: build the package first (__graft_entry__.build())") from e
+        mod._set_stream_getter(_current_stream)
+        _ext = mod
+    return _ext
+
+
+# Pointer arguments: a torch tensor (its data_ptr()), an int address or None.
+# stream: None (torch's current stream), an int handle or a torch stream.
 
 
 def tk_init(device: int) -> TkStatus:
-    return TkStatus(load_library().tk_init(int(device)))
-
-
-def _cast(fn_name: str, x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
-          clamped_count, stream) -> TkStatus:
-    lib = load_library()
-    fn = getattr(lib, fn_name)
-    rc = fn(_ptr(x), _ptr(topk_weight), int(n), int(hidden), int(group_size), float(clamp_limit),
-            int(scale_fmt), _ptr(codes), _ptr(scales), _ptr(clamped_count), _stream(stream))
-    return TkStatus(rc)
+    return _STATUS[(_ext or load_extension()).tk_init(int(device))]
 
 
 def tk_swiglu_cast_fp8(x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
                        clamped_count=None, stream=None) -> TkStatus:
     """See tk_swiglu_cast_fp8 in include/tk.h."""
-    return _cast("tk_swiglu_cast_fp8", x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt,
-                 codes, scales, clamped_count, stream)
+    return _STATUS[(_ext or load_extension()).tk_swiglu_cast_fp8(
+        x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales, clamped_count, stream)]
 
 
 def tk_swiglu_cast_fp4(x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales,
                        clamped_count=None, stream=None) -> TkStatus:
     """See tk_swiglu_cast_fp4 in include/tk.h."""
-    return _cast("tk_swiglu_cast_fp4", x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt,
-                 codes, scales, clamped_count, stream)
+    return _STATUS[(_ext or load_extension()).tk_swiglu_cast_fp4(
+        x, topk_weight, n, hidden, group_size, clamp_limit, scale_fmt, codes, scales, clamped_count, stream)]
 
 
 def tk_swiglu_forward(x, topk_weight, n, hidden, clamp_limit, y, clamped_count=None,
                       stream=None) -> TkStatus:
     """See tk_swiglu_forward in include/tk.h."""
-    rc = load_library().tk_swiglu_forward(_ptr(x), _ptr(topk_weight), int(n), int(hidden), float(clamp_limit),
-                                          _ptr(y), _ptr(clamped_count), _stream(stream))
-    return TkStatus(rc)
-
-
-def _cast_only(fn_name, x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream) -> TkStatus:
-    fn = getattr(load_library(), fn_name)
-    return TkStatus(fn(_ptr(x), int(in_dtype), int(n), int(hidden), int(group_size), int(scale_fmt), _ptr(codes),
-                       _ptr(scales), _stream(stream)))
+    return _STATUS[(_ext or load_extension()).tk_swiglu_forward(x, topk_weight, n, hidden, clamp_limit, y,
+                                                                  clamped_count, stream)]
 
 
 def tk_cast_fp8(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream=None) -> TkStatus:
     """See tk_cast_fp8 in include/tk.h."""
-    return _cast_only("tk_cast_fp8", x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream)
+    return _STATUS[(_ext or load_extension()).tk_cast_fp8(x, in_dtype, n, hidden, group_size, scale_fmt, codes,
+                                                            scales, stream)]
 
 
 def tk_cast_fp4(x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream=None) -> TkStatus:
     """See tk_cast_fp4 in include/tk.h."""
-    return _cast_only("tk_cast_fp4", x, in_dtype, n, hidden, group_size, scale_fmt, codes, scales, stream)
+    return _STATUS[(_ext or load_extension()).tk_cast_fp4(x, in_dtype, n, hidden, group_size, scale_fmt, codes,
+                                                            scales, stream)]
 
 
 def tk_topk_gate(scores, tokens, experts, k, n_group, topk_group, normalise, topk_idx, topk_weight,
                  stream=None) -> TkStatus:
     """See tk_topk_gate in include/tk.h."""
-    return TkStatus(load_library().tk_topk_gate(_ptr(scores), int(tokens), int(experts), int(k), int(n_group),
-                                                int(topk_group), int(bool(normalise)), _ptr(topk_idx),
-                                                _ptr(topk_weight), _stream(stream)))
+    return _STATUS[(_ext or load_extension()).tk_topk_gate(scores, tokens, experts, k, n_group, topk_group,
+                                                             normalise, topk_idx, topk_weight, stream)]
 
 
 def tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens, k, hidden, n_rows, out_dtype, out,
                   stream=None) -> TkStatus:
     """See tk_moe_reduce in include/tk.h."""
-    return TkStatus(load_library().tk_moe_reduce(_ptr(x), _ptr(row_scale), _ptr(pos), _ptr(topk_weight),
-                                                 float(global_scale), int(tokens), int(k), int(hidden), int(n_rows),
-                                                 int(out_dtype), _ptr(out), _stream(stream)))
+    return _STATUS[(_ext or load_extension()).tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens,
+                                                              k, hidden, n_rows, out_dtype, out, stream)]
 
 
 def tk_status_str(status: int) -> str:
-    return load_library().tk_status_str(int(status)).decode()
+    return (_ext or load_extension()).tk_status_str(int(status))

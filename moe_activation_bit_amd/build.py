@@ -3,6 +3,7 @@
 libtk.so    -- the HIP kernels and C ABI (hipcc, gfx950; one object per source)
 libsynth.so -- the seeded input generator (plain C)
 libstreamceil.so -- plain streaming kernels that measure the HBM ceiling
+_tkpy            -- the CPython extension behind the Python binding (gcc)
 """
 from __future__ import annotations
 
@@ -51,8 +52,18 @@ def build_commands():
          "-lm"],
     ]
     stage2 = [[HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", os.path.join(HERE, "libtk.so")]
-              + [o for o, _ in objs]]
+              + [o for o, _ in objs], extension_command()]
     return stage1, stage2
+
+
+def extension_command():
+    """gcc line for the CPython extension _tkpy (argument marshalling to
+    libtk.so, found next to it at run time)."""
+    import sysconfig
+    out = os.path.join(HERE, "_tkpy" + sysconfig.get_config_var("EXT_SUFFIX"))
+    return ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra", "-Werror",
+            "-I" + sysconfig.get_paths()["include"], "-I" + os.path.join(ROOT, "include"),
+            os.path.join(CSRC, "tk_py.c"), "-o", out, "-L" + HERE, "-ltk", "-Wl,-rpath,$ORIGIN"]
 
 
 def build(extra=None):
