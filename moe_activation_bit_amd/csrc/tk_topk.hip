@@ -14,16 +14,18 @@
 // of experts is a block of consecutive lanes and lane order is index order.
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
-//   2. Groups: each lane's two best, merged over the group's lanes by an
-//      xor-butterfly; group ranks from wave-uniform reads of every group sum;
-//      lanes of dropped groups empty their lists.
+//   2. Groups: each lane's two best, merged over the group's lanes (DPP
+//      quad_perm / half-row and row mirrors, lane shuffles past 16 lanes);
+//      group ranks from wave-uniform reads of every group sum; lanes of
+//      dropped groups empty their lists.
 //   3. k rounds of a tournament between the lanes' list heads: a DPP max of
 //      the head keys (quad_perm, row_half_mirror, row_mirror, then four
 //      v_readlane), the first lane whose head equals it (ballot + s_ff1: the
 //      smallest index among equal scores), the winner's index by v_readlane,
-//      and the winner pops its head.  The running sum takes each pick's value
-//      from its key; the output weights re-read the picks' own scores.
-// Each round is a few dozen VALU/SALU instructions with no LDS traffic.
+//      and the winner pops its head; lane `round` keeps the pick's index.
+//      Output lane j then re-reads pick j's own score, and the
+//      normalising sum adds those k values in pick order after the rounds.
+// Each round is about three dozen VALU/SALU instructions with no LDS traffic.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -46,7 +48,8 @@ __device__ __forceinline__ float ffrom(uint32_t u) { return __builtin_bit_cast(f
 __device__ __forceinline__ uint32_t ordered(float f)
 {
     const uint32_t b = fbits(f + 0.0f); // -0 + +0 = +0
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    // negative: all bits flipped; otherwise only the sign bit set
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
 // The value of a key (a zero comes back as +0).
@@ -74,9 +77,28 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v)
     v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]
     v = dpp_umax<0x141>(v); // row_half_mirror
     v = dpp_umax<0x140>(v); // row_mirror: every lane holds its 16-lane row's max
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
+    // row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3:
+    // lane 63 ends with the wave's max
+    // (rows left out read 0, the identity of the unsigned max)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// (a1, a2) <- the two largest of (a1, a2) and (b1, b2), each pair ordered
+__device__ __forceinline__ void merge_top2_from(float& a1, float& a2, float b1, float b2)
+{
+    const float hi = fmaxf(a1, b1);
+    a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+    a1 = hi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void merge_top2(float& a1, float& a2)
+{
+    const float b1 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a1), CTRL, 0xF, 0xF, false));
+    const float b2 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a2), CTRL, 0xF, 0xF, false));
+    merge_top2_from(a1, a2, b1, b2);
 }
 
 template <int C>
@@ -92,19 +114,26 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const float* s_row = scores + (size_t)t * experts;
 
     // ---- 1. this lane's candidates, sorted best first
+    // every load is issued (a slot past the last expert re-reads the last
+    // one and is then emptied), so all C are in flight together
     uint32_t key[C], idx[C];
+    float v[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        v[j] = s_row[min(lane * C + j, experts - 1u)];
 #pragma unroll
     for (int j = 0; j < C; ++j) {
         const uint32_t e = lane * C + j;
-        key[j] = e < experts ? ordered(s_row[e]) : 0u;
+        key[j] = e < experts ? ordered(v[j]) : 0u;
         idx[j] = e;
     }
 #pragma unroll
     for (int i = 1; i < C; ++i) {
 #pragma unroll
         for (int j = i; j > 0; --j) {
-            // (key desc, idx asc): a strict total order, so the sort is exact
-            const bool swap = key[j] > key[j - 1] || (key[j] == key[j - 1] && idx[j] < idx[j - 1]);
+            // insertion by strict comparison is stable and the indices start
+            // ascending, so equal keys stay smallest index first
+            const bool swap = key[j] > key[j - 1];
             const uint32_t k0 = key[j - 1], i0 = idx[j - 1];
             key[j - 1] = swap ? key[j] : k0;
             idx[j - 1] = swap ? idx[j] : i0;
@@ -119,12 +148,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         // the sign of a zero does not matter to the sums' comparisons)
         float a1 = key[0] ? unordered(key[0]) : -INFINITY;
         float a2 = (C > 1 && key[C > 1 ? 1 : 0]) ? unordered(key[C > 1 ? 1 : 0]) : -INFINITY;
-        for (uint32_t m = 1; m < (1u << gl_log2); m <<= 1) {
-            const float b1 = __shfl_xor(a1, (int)m), b2 = __shfl_xor(a2, (int)m);
-            const float hi = fmaxf(a1, b1);
-            a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
-            a1 = hi;
-        }
+        // Merge the pairs over the group's 2^gl_log2 lanes: DPP within 16-lane
+        // rows (after each step a block of lanes holds one merged pair, so the
+        // mirror partner always brings the other block's), lane shuffles above.
+        if (gl_log2 >= 1)
+            merge_top2<0xB1>(a1, a2); // quad_perm [1,0,3,2]
+        if (gl_log2 >= 2)
+            merge_top2<0x4E>(a1, a2); // quad_perm [2,3,0,1]
+        if (gl_log2 >= 3)
+            merge_top2<0x141>(a1, a2); // row_half_mirror
+        if (gl_log2 >= 4)
+            merge_top2<0x140>(a1, a2); // row_mirror
+        for (uint32_t m = 16; m < (1u << gl_log2); m <<= 1)
+            merge_top2_from(a1, a2, __shfl_xor(a1, (int)m), __shfl_xor(a2, (int)m));
         const float gsum = a1 + a2;
         const uint32_t my_g = lane >> gl_log2;
         uint32_t rank = 0;
@@ -139,9 +175,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         }
     }
 
-    // ---- 3. k rounds between the list heads
+    // ---- 3. k rounds between the list heads; pick it goes to lane it
     int32_t my_idx = 0;
-    float sum = 0.0f;
     for (uint32_t it = 0; it < k; ++it) {
         const uint32_t best = wave_umax(key[0]);
         const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == best);
@@ -155,12 +190,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
             }
             key[C - 1] = 0u;
         }
-        if (lane == it)
-            my_idx = (int32_t)e;
-        sum += unordered(best); // best first, as the weights are normalised (+0 for a -0 is the same sum)
+        my_idx = lane == it ? (int32_t)e : my_idx;
+    }
+    // each pick's own value (keeps -0), summed in pick order for the normalisation
+    const float my_w = lane < k ? s_row[my_idx] : 0.0f;
+    float sum = 0.0f;
+    if (normalise) {
+        for (uint32_t it = 0; it < k; ++it)
+            sum += ffrom(__builtin_amdgcn_readlane(fbits(my_w), it));
     }
     if (lane < k) {
-        const float my_w = s_row[my_idx]; // the pick's own value (keeps -0)
         idx_out[(size_t)t * k + lane] = my_idx;
         w_out[(size_t)t * k + lane] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
     }
