@@ -205,3 +205,42 @@ def test_moe_reduce_unsupported_and_empty():
     assert reduce(tokens=0, x=None, pos=None, topk_weight=None, out=None) == OK
     # n_rows == 0 lets x be NULL (nothing can be read); with no tokens nothing launches
     assert reduce(tokens=0, n_rows=0, x=None) == OK
+
+
+class _FakeTensor:
+    """Stands in for a torch tensor: the binding takes its data_ptr()."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_extension_marshals_like_the_c_abi():
+    # the binding goes through the _tkpy extension; its conversions must reach
+    # the C ABI unchanged: objects with data_ptr(), ints and None for pointers,
+    # numpy integers and floats for sizes, and the status comes back as TkStatus
+    import numpy as np
+
+    ext = tk.load_extension()
+    assert os.path.dirname(ext.__file__) == os.path.dirname(tk.LIB_PATH)
+    rc = tk.tk_swiglu_cast_fp8(_FakeTensor(X), _FakeTensor(W), np.int64(0), np.int32(1024), 0, np.float32(INF),
+                               FP32, _FakeTensor(C), S, None, 0)
+    assert rc is OK
+    # a misaligned address passed as an object is rejected by the library itself
+    assert tk.tk_swiglu_cast_fp8(_FakeTensor(X + 4), W, 4, 1024, 0, INF, FP32, C, S, None, 0) is INVALID
+    assert tk.tk_cast_fp8(X, tk.TK_DTYPE_BF16, 0, 1024, 128, UE8M0, C, S, 0) is OK
+    assert tk.tk_topk_gate(X, 0, 256, 8, 8, 4, True, C, S, 0) is OK
+    assert tk.tk_moe_reduce(X, None, C, W, 1.0, 0, 8, 7168, 0, tk.TK_DTYPE_BF16, S, 0) is OK
+    assert tk.tk_swiglu_forward(X, None, 0, 1024, INF, C, None, 0) is OK
+
+
+@pytest.mark.parametrize("bad", [dict(x="not a pointer"), dict(n="4"), dict(clamp_limit="inf"), dict(scale_fmt=0.5),
+                                 dict(stream="stream")], ids=str)
+def test_extension_rejects_wrong_argument_types(bad):
+    a = dict(x=X, topk_weight=W, n=4, hidden=1024, group_size=0, clamp_limit=INF, scale_fmt=FP32, codes=C,
+             scales=S, clamped_count=None, stream=0)
+    a.update(bad)
+    with pytest.raises((TypeError, AttributeError)):
+        tk.tk_swiglu_cast_fp8(**a)

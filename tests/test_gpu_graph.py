@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture: they allocate nothing, record no
 memset and query nothing that capture forbids, so a caller can capture them
 once and replay.  One graph holds a fused FP8 launch (with the clamp counter),
-an FP4 launch, a stand-alone cast, the gating and the reduce; it is replayed
+an FP4 launch, a stand-alone cast, the gating, the reduce and three launches
+of long rows (groups shared by two waves, and 16 streamed steps); it is replayed
 several times with eager work between the replays (outputs poisoned, the
 counter zeroed by torch outside the graph), and every replay must equal the
 eager results bit for bit."""
@@ -35,6 +36,11 @@ def test_capture_and_replay_matches_eager():
     pd, rwd, rsd = torch.from_numpy(pos).to(DEV), torch.from_numpy(rw).to(DEV), torch.from_numpy(rs).to(DEV)
     scores = torch.from_numpy(wl.uniform(wl.stream_key("graph_test", 0, "scores"), 0, 300 * 256)
                               .reshape(300, 256).astype(np.float32)).to(DEV)
+    # long rows: per-token groups of 16384 columns (two waves per group, loads
+    # streamed) and 8192 columns (one wave, 16 streamed steps)
+    nl, hl = 40, 16384
+    xl_h = wl.make_x(wc, 1, rows=range(nl))
+    xl = torch.from_numpy(np.ascontiguousarray(np.tile(xl_h, (1, 2 * hl // xl_h.shape[1]))).view(np.int16)).to(DEV)
 
     outs = dict(
         codes=torch.empty((n, 2048), dtype=torch.uint8, device=DEV),
@@ -47,6 +53,12 @@ def test_capture_and_replay_matches_eager():
         idx=torch.empty((300, 8), dtype=torch.int32, device=DEV),
         gw=torch.empty((300, 8), dtype=torch.float32, device=DEV),
         red=torch.empty((r.tokens, r.hidden), dtype=torch.bfloat16, device=DEV),
+        lcodes=torch.empty((nl, hl), dtype=torch.uint8, device=DEV),
+        lscales=torch.empty((nl, 1), dtype=torch.float32, device=DEV),
+        lcodes4=torch.empty((nl, hl // 4), dtype=torch.uint8, device=DEV),
+        lscales4=torch.empty((nl, 1), dtype=torch.uint8, device=DEV),
+        lccodes=torch.empty((nl, hl), dtype=torch.uint8, device=DEV),
+        lcscales=torch.empty((nl, 1), dtype=torch.float32, device=DEV),
     )
 
     def work():
@@ -60,6 +72,12 @@ def test_capture_and_replay_matches_eager():
         assert tk.tk_topk_gate(scores, 300, 256, 8, 8, 4, 1, outs["idx"], outs["gw"], s) == OK
         assert tk.tk_moe_reduce(xr, rsd, pd, rwd, r.global_scale, r.tokens, r.k, r.hidden, n_rows,
                                 tk.TK_DTYPE_BF16, outs["red"], s) == OK
+        assert tk.tk_swiglu_cast_fp8(xl, None, nl, hl, 0, math.inf, tk.TK_SCALE_FP32, outs["lcodes"],
+                                     outs["lscales"], None, s) == OK
+        assert tk.tk_swiglu_cast_fp4(xl, None, nl, hl // 2, 0, math.inf, tk.TK_SCALE_UE8M0, outs["lcodes4"],
+                                     outs["lscales4"], None, s) == OK
+        assert tk.tk_cast_fp8(xl, tk.TK_DTYPE_BF16, nl, hl, 0, tk.TK_SCALE_FP32, outs["lccodes"], outs["lcscales"],
+                              s) == OK
 
     def poison():
         for k, t in outs.items():
