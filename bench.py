@@ -112,7 +112,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, workload: str, se
     from moe_activation_bit_amd import workloads as wl
 
     if kernel == "fused":
-        w = wl.WORKLOADS[workload]
+        w = wl.workload(workload)
         algo = w.algorithmic_bytes(wl.num_rows(w, seed))
     else:
         workload, algo = aux_workload(kernel, wl, seed)
@@ -483,7 +483,7 @@ def main():
         return bench_aux(args, torch, np, tk, wl)
 
     name = args.workload or wl.HEADLINE
-    w = wl.WORKLOADS[name]
+    w = wl.workload(name)
     n = wl.num_rows(w, args.seed)
     fmt = 8 if w.fmt == "fp8" else 4
     sfmt = tk.TK_SCALE_FP32 if w.scale_fmt == "fp32" else tk.TK_SCALE_UE8M0

@@ -85,6 +85,24 @@ WORKLOADS = {
 # The benchmark's headline workload: the per-block FP8 case.
 HEADLINE = "fp8_g128_ue8m0_n32768_h2048"
 
+# Per-token rows longer than the workloads above use, 512 MiB of x each: one
+# wave of 16 streamed 512-column steps per row; two waves of 16; four waves of
+# 9 (a 12-step template).  Timed by `bench.py --workload NAME`, never by
+# default.
+LONG_ROW_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fp8_per_token_n16384_h8192", 16384, 8192, 3.0, "fp8", 0, "fp32", None, "uniform"),
+        Workload("fp8_per_token_n8192_h16384", 8192, 16384, 3.0, "fp8", 0, "fp32", None, "uniform"),
+        Workload("fp8_per_token_n7281_h18432", 7281, 18432, 3.0, "fp8", 0, "fp32", None, "uniform"),
+    ]
+}
+
+
+def workload(name: str) -> Workload:
+    """A fused-step workload by name, from either table."""
+    return WORKLOADS[name] if name in WORKLOADS else LONG_ROW_WORKLOADS[name]
+
 
 _lib = None
 

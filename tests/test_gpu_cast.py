@@ -147,3 +147,16 @@ def test_unfused_two_kernel_path_equals_fused(name):
     fused_scales = fused_scales.view(np.float32) if sfmt == 0 else fused_scales
     same(unfused, (codes.cpu().numpy(), fused_scales), name)
     assert int(c1.item()) == int(c2.item())
+
+
+def test_benchmark_workload_full_size_every_row():
+    """The stand-alone cast exactly as the benchmark times it: bf16 rows
+    [65536, 2048] (the N(0,2) samples of a [32768, 4096] draw), groups of 128,
+    UE8M0 scales; every code and scale against the oracle."""
+    n, hidden, group = 32768, 2048, 128
+    w = wl.Workload("cast_bf16_e4m3_g128_ue8m0_n65536_h2048", n, hidden, 2.0, "fp8", group, "ue8m0", None, "uniform")
+    say("cast benchmark workload, full size")
+    x = wl.make_x(w, 0).reshape(2 * n, hidden)
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+    got = run_cast(xd, tk.TK_DTYPE_BF16, 2 * n, hidden, group, 8, tk.TK_SCALE_UE8M0)
+    same(got, oracle.cast_bf16(x, group, 8, tk.TK_SCALE_UE8M0), "cast benchmark workload")
