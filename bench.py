@@ -50,10 +50,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text with comments removed and whitespace collapsed, so that a
+    comment edit leaves the digest (and the counters tied to it) unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(kernel: str = "fused") -> str:
     h = hashlib.sha256()
     for f in KERNELS[kernel][0]:
-        h.update(open(os.path.join(ROOT, "moe_activation_bit_amd", "csrc", f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "moe_activation_bit_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -31,6 +31,10 @@
 //  - A persistent grid of two 256-thread workgroups per CU for large launches
 //    and four for small ones (measured best on MI355X); every wave strides
 //    over units, so the LDS table is filled once per workgroup.
+//  - Row-reduced units of 8 to 16 steps (per-token rows beyond 2048 columns,
+//    512k-column groups) stream their loads four steps ahead of the
+//    arithmetic; groups of more than 16 steps are split over 2 or 4 waves of
+//    a workgroup, which meet in LDS for the group's abs-max.
 //  - The clamp counter is reduced per wave with ballots and added to the
 //    int64 counter with one vector atomic per wave.
 #include <hip/hip_runtime.h>
@@ -306,6 +310,8 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
     quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
 }
 
+// The persistent loop for row-reduced units of kStreamMinSteps steps or more:
+// the table first, then every unit of the wave streamed (stream_unit).
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool PARTIAL>
 __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut, uint32_t lane, uint32_t wave,
                                                      uint32_t nwaves)
