@@ -478,7 +478,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(rows are independent; see the sharding notes). Run with --gpus 1.")
         sys.exit(2)
 
