@@ -85,19 +85,19 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// (a1, a2) <- the two largest of (a1, a2) and (b1, b2), each pair ordered
-__device__ __forceinline__ void merge_top2_from(float& a1, float& a2, float b1, float b2)
+// (a1, a2) <- the two largest keys of (a1, a2) and (b1, b2), each pair ordered
+__device__ __forceinline__ void merge_top2_from(uint32_t& a1, uint32_t& a2, uint32_t b1, uint32_t b2)
 {
-    const float hi = fmaxf(a1, b1);
-    a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+    const uint32_t hi = max(a1, b1);
+    a2 = max(min(a1, b1), max(a2, b2));
     a1 = hi;
 }
 
 template <int CTRL>
-__device__ __forceinline__ void merge_top2(float& a1, float& a2)
+__device__ __forceinline__ void merge_top2(uint32_t& a1, uint32_t& a2)
 {
-    const float b1 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a1), CTRL, 0xF, 0xF, false));
-    const float b2 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a2), CTRL, 0xF, 0xF, false));
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a1, CTRL, 0xF, 0xF, false);
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a2, CTRL, 0xF, 0xF, false);
     merge_top2_from(a1, a2, b1, b2);
 }
 
@@ -144,13 +144,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
     // ---- 2. group selection
     if (n_group > 1) {
-        // the group's two best values (a lane's two best are its list head;
-        // the sign of a zero does not matter to the sums' comparisons)
-        float a1 = key[0] ? unordered(key[0]) : -INFINITY;
-        float a2 = (C > 1 && key[C > 1 ? 1 : 0]) ? unordered(key[C > 1 ? 1 : 0]) : -INFINITY;
-        // Merge the pairs over the group's 2^gl_log2 lanes: DPP within 16-lane
-        // rows (after each step a block of lanes holds one merged pair, so the
-        // mirror partner always brings the other block's), lane shuffles above.
+        // the group's two best keys (a lane's two best are its list head; 0 =
+        // none), merged as order-preserving integers and turned back into
+        // values for the sum (the sign of a zero does not matter to the sums'
+        // comparisons).  Merge over the group's 2^gl_log2 lanes: DPP within
+        // 16-lane rows (after each step a block of lanes holds one merged
+        // pair, so the mirror partner always brings the other block's), lane
+        // shuffles above.
+        uint32_t a1 = key[0], a2 = C > 1 ? key[C > 1 ? 1 : 0] : 0u;
         if (gl_log2 >= 1)
             merge_top2<0xB1>(a1, a2); // quad_perm [1,0,3,2]
         if (gl_log2 >= 2)
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         if (gl_log2 >= 4)
             merge_top2<0x140>(a1, a2); // row_mirror
         for (uint32_t m = 16; m < (1u << gl_log2); m <<= 1)
-            merge_top2_from(a1, a2, __shfl_xor(a1, (int)m), __shfl_xor(a2, (int)m));
-        const float gsum = a1 + a2;
+            merge_top2_from(a1, a2, (uint32_t)__shfl_xor((int)a1, (int)m), (uint32_t)__shfl_xor((int)a2, (int)m));
+        const float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
         const uint32_t my_g = lane >> gl_log2;
         uint32_t rank = 0;
         for (uint32_t h = 0; h < n_group; ++h) {
