@@ -201,7 +201,7 @@ tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
  *
  *  scores       fp32 [tokens, experts], row-major, 4-byte aligned (device).
  *  tokens       0 <= tokens < 2^31.
- *  experts      1..256;  k: 1..64 and at most the number of candidates.
+ *  experts      1..512;  k: 1..64 and at most the number of candidates.
  *  n_group      divides experts (1 = no groups); topk_group in 1..n_group;
  *               with groups, each group has at least 2 experts.
  *  normalise    0: weights are the chosen scores; 1: each chosen score divided
@@ -210,7 +210,7 @@ tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
  *  topk_idx     int32 [tokens, k] (device), best first.
  *  topk_weight  fp32 [tokens, k] (device), in the same order.
  * Returns TK_ERR_INVALID_ARG for violated preconditions, overlapping outputs or
- * misaligned pointers; TK_ERR_UNSUPPORTED when experts > 256 or k > 64, or when
+ * misaligned pointers; TK_ERR_UNSUPPORTED when experts > 512 or k > 64, or when
  * a group is not a power-of-two number of whole 64-lane slots (experts/n_group
  * must be a multiple of ceil(experts/64), with a power-of-two quotient).
  */

@@ -10,7 +10,7 @@
 // pick the next).
 //
 // gfx950 design: one 64-lane wave per token (the pages use a 32-lane warp);
-// lane l holds experts l*C .. l*C+C-1 (C = ceil(experts/64) <= 4), so a group
+// lane l holds experts l*C .. l*C+C-1 (C = ceil(experts/64) <= 8), so a group
 // of experts is a block of consecutive lanes and lane order is index order.
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;
-constexpr int kMaxExperts = 256;
+constexpr int kMaxExperts = 512;
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float ffrom(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -260,7 +260,11 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
     case 1: TK_TOPK(1); break;
     case 2: TK_TOPK(2); break;
     case 3: TK_TOPK(3); break;
-    default: TK_TOPK(4); break;
+    case 4: TK_TOPK(4); break;
+    case 5: TK_TOPK(5); break;
+    case 6: TK_TOPK(6); break;
+    case 7: TK_TOPK(7); break;
+    default: TK_TOPK(8); break;
     }
 #undef TK_TOPK
     return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;

@@ -174,7 +174,9 @@ def test_topk_invalid_arguments(kw):
 
 
 def test_topk_unsupported_and_empty():
-    assert topk(experts=512, n_group=8) == UNSUPPORTED
+    assert topk(experts=576, n_group=8) == UNSUPPORTED     # more than 8 experts per lane
+    assert topk(tokens=0, experts=512, n_group=8) == OK     # 8 per lane, groups of 8 lanes
+    assert topk(tokens=0, experts=384, n_group=1, topk_group=1) == OK
     assert topk(experts=256, n_group=1, topk_group=1, k=65) == UNSUPPORTED
     assert topk(experts=72, n_group=3, topk_group=2, k=5) == UNSUPPORTED
     assert topk(tokens=0) == OK

@@ -29,6 +29,9 @@ def run(scores, k, ng, tg, normalise):
 SHAPES = [  # (experts, k, n_group, topk_group)
     (256, 8, 8, 4), (256, 8, 1, 1), (256, 64, 1, 1), (256, 6, 16, 2), (128, 4, 4, 2), (64, 6, 1, 1), (64, 8, 32, 4),
     (8, 2, 1, 1), (100, 3, 1, 1), (160, 8, 5, 2), (200, 5, 1, 1),
+    # 5 to 8 experts per lane
+    (320, 6, 1, 1), (384, 8, 1, 1), (384, 8, 12, 4), (448, 8, 1, 1), (512, 8, 8, 4), (512, 16, 16, 4),
+    (512, 64, 1, 1), (500, 7, 1, 1),
 ]
 
 
