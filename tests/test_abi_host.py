@@ -16,7 +16,9 @@ OK, INVALID, UNSUPPORTED = tk.TkStatus.TK_OK, tk.TkStatus.TK_ERR_INVALID_ARG, tk
 FP32, UE8M0 = tk.TK_SCALE_FP32, tk.TK_SCALE_UE8M0
 INF = math.inf
 
-# fake device addresses: aligned, far apart, never dereferenced
+# fake device addresses: aligned, far apart, never dereferenced.  Every call
+# given them is rejected before any HIP call or has no rows to process, so no
+# kernel is ever launched on them (a supported shape is checked with n = 0).
 X, W, C, S, K = 0x7000_0000_0000, 0x7100_0000_0000, 0x7200_0000_0000, 0x7300_0000_0000, 0x7400_0000_0000
 
 
