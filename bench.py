@@ -280,7 +280,23 @@ def cpu_baseline(w, seed: int, rows: int, single_rows: int = 1024):
                   f"({dt * threads:.1f} thread-s), {rows / dt:.1f} rows/s",
         "single_thread": {"value": round(w.algorithmic_bytes(r1) / dt1 / 1e9, 6), "unit": "GB/s",
                           "rows": r1, "seconds": round(dt1, 3)},
+        "rows_per_s": round(rows / dt, 1),
+        "host": host_cpu(),
     }
+
+
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"logical_cpus": os.cpu_count(), "cpu_model": model}
 
 
 def flushed_reps(torch, step, nbytes: int, reps: int = 30, warm: int = 3):
