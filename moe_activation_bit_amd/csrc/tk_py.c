@@ -68,6 +68,15 @@ static int as_stream(PyObject* o, void* out)
 
 static PyObject* status(tk_status rc) { return PyLong_FromLong((long)rc); }
 
+/* Run one library call without the GIL (the library never calls back into
+ * Python; other threads can issue their own launches meanwhile, as they could
+ * through ctypes). */
+#define TK_CALL(rc, expr)              \
+    do {                               \
+        Py_BEGIN_ALLOW_THREADS rc = (expr); \
+        Py_END_ALLOW_THREADS           \
+    } while (0)
+
 static PyObject* py_set_stream_getter(PyObject* self, PyObject* fn)
 {
     (void)self;
@@ -87,7 +96,9 @@ static PyObject* py_tk_init(PyObject* self, PyObject* args)
     int device;
     if (!PyArg_ParseTuple(args, "i", &device))
         return NULL;
-    return status(tk_init(device));
+    tk_status rc;
+    TK_CALL(rc, tk_init(device));
+    return status(rc);
 }
 
 static PyObject* py_tk_status_str(PyObject* self, PyObject* args)
@@ -114,8 +125,10 @@ static PyObject* swiglu_cast(swiglu_cast_fn fn, PyObject* args)
         return NULL;
     if (!as_stream(so, &stream))
         return NULL;
-    return status(fn(x, (const float*)w, n, hidden, group, clamp, (tk_scale_fmt)sfmt, codes, scales, (int64_t*)count,
-                     stream));
+    tk_status rc;
+    TK_CALL(rc, fn(x, (const float*)w, n, hidden, group, clamp, (tk_scale_fmt)sfmt, codes, scales, (int64_t*)count,
+                   stream));
+    return status(rc);
 }
 
 static PyObject* py_tk_swiglu_cast_fp8(PyObject* self, PyObject* args)
@@ -142,7 +155,9 @@ static PyObject* py_tk_swiglu_forward(PyObject* self, PyObject* args)
         return NULL;
     if (!as_stream(so, &stream))
         return NULL;
-    return status(tk_swiglu_forward(x, (const float*)w, n, hidden, clamp, (float*)y, (int64_t*)count, stream));
+    tk_status rc;
+    TK_CALL(rc, tk_swiglu_forward(x, (const float*)w, n, hidden, clamp, (float*)y, (int64_t*)count, stream));
+    return status(rc);
 }
 
 typedef tk_status (*cast_fn)(const void*, tk_dtype, int64_t, int64_t, int64_t, tk_scale_fmt, void*, void*, void*);
@@ -158,7 +173,9 @@ static PyObject* cast(cast_fn fn, PyObject* args)
         return NULL;
     if (!as_stream(so, &stream))
         return NULL;
-    return status(fn(x, (tk_dtype)in_dtype, n, hidden, group, (tk_scale_fmt)sfmt, codes, scales, stream));
+    tk_status rc;
+    TK_CALL(rc, fn(x, (tk_dtype)in_dtype, n, hidden, group, (tk_scale_fmt)sfmt, codes, scales, stream));
+    return status(rc);
 }
 
 static PyObject* py_tk_cast_fp8(PyObject* self, PyObject* args)
@@ -185,8 +202,10 @@ static PyObject* py_tk_topk_gate(PyObject* self, PyObject* args)
         return NULL;
     if (!as_stream(so, &stream))
         return NULL;
-    return status(tk_topk_gate((const float*)scores, tokens, experts, k, n_group, topk_group, normalise,
-                               (int32_t*)idx, (float*)w, stream));
+    tk_status rc;
+    TK_CALL(rc, tk_topk_gate((const float*)scores, tokens, experts, k, n_group, topk_group, normalise, (int32_t*)idx,
+                             (float*)w, stream));
+    return status(rc);
 }
 
 static PyObject* py_tk_moe_reduce(PyObject* self, PyObject* args)
@@ -202,8 +221,10 @@ static PyObject* py_tk_moe_reduce(PyObject* self, PyObject* args)
         return NULL;
     if (!as_stream(so, &stream))
         return NULL;
-    return status(tk_moe_reduce(x, (const float*)row_scale, (const int32_t*)pos, (const float*)w, global_scale,
-                                tokens, k, hidden, n_rows, (tk_dtype)out_dtype, out, stream));
+    tk_status rc;
+    TK_CALL(rc, tk_moe_reduce(x, (const float*)row_scale, (const int32_t*)pos, (const float*)w, global_scale, tokens,
+                              k, hidden, n_rows, (tk_dtype)out_dtype, out, stream));
+    return status(rc);
 }
 
 static PyMethodDef kMethods[] = {
