@@ -19,7 +19,10 @@ one with `--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`; `bench.py [--kernel K]
 --summarize-pmc FETCH.csv WRITE.csv` scales that kernel's per-dispatch counters
 by what the same counters read for a plain elementwise copy of known size and
 writes profiles/traffic_<workload>.json (tagged with the kernel source digest;
-a stale record is ignored).
+a stale record is ignored).  The gating's line also carries valu_issue: VALU
+instructions per launch from a `--pmc SQ_INSTS_VALU SQ_WAVES ...` run, recorded
+by `bench.py --kernel topk --summarize-valu PMC.csv` in
+profiles/valu_<workload>.json, against the chip's VALU issue rate.
 """
 from __future__ import annotations
 
@@ -160,6 +163,48 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, workload: str, se
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+
+
+# VALU issue peak of the chip: 256 CUs x 4 SIMDs, one wave64 VALU instruction
+# per SIMD every 4 cycles, 2.4 GHz
+VALU_PEAK_INSTS_PER_S = 256 * 4 * 2.4e9 / 4
+
+
+def summarize_valu(csv_path: str, kernel: str, seed: int):
+    """Per-dispatch SQ_INSTS_VALU / SQ_WAVES of one kernel from a rocprofv3
+    counter run; writes profiles/valu_<workload>.json (tagged with the kernel
+    source digest, like the traffic records)."""
+    import re
+
+    from moe_activation_bit_amd import workloads as wl
+
+    workload, _ = aux_workload(kernel, wl, seed)
+    pat = re.compile(KERNELS[kernel][1])
+    vals = {}
+    for r in _pmc_rows(csv_path):
+        if pat.search(r.get("Kernel_Name", "")) and r.get("Counter_Name") in ("SQ_INSTS_VALU", "SQ_WAVES"):
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if set(vals) != {"SQ_INSTS_VALU", "SQ_WAVES"}:
+        raise SystemExit("counter rows missing: need SQ_INSTS_VALU and SQ_WAVES")
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_sha256_16": kernel_source_digest(kernel),
+           "valu_insts_per_dispatch": sum(vals["SQ_INSTS_VALU"]) / len(vals["SQ_INSTS_VALU"]),
+           "waves_per_dispatch": sum(vals["SQ_WAVES"]) / len(vals["SQ_WAVES"]),
+           "dispatches": len(vals["SQ_INSTS_VALU"])}
+    with open(os.path.join(ROOT, "profiles", f"valu_{workload}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def valu_for(workload: str, kernel: str):
+    """VALU instructions per launch from the committed counter record, if it
+    was taken on the current kernel code; else None."""
+    path = os.path.join(ROOT, "profiles", f"valu_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest(kernel):
+        return None
+    return rec.get("valu_insts_per_dispatch")
 
 
 def unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, reps, stream, fused_s):
@@ -456,6 +501,13 @@ def bench_aux(args, torch, np, tk, wl):
                         "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
                         "avg_launch_us": round(avg * 1e6, 3)},
            "cpu_baseline": None}
+    if args.kernel == "topk":
+        # the gating is bound by VALU issue, not by its bytes: VALU instructions
+        # per launch (counter record) against the chip's issue rate
+        v = valu_for(name, "topk")
+        out["valu_issue"] = None if v is None else {
+            "insts_per_launch": round(v), "achieved": round(v / avg / 1e9, 2), "peak": VALU_PEAK_INSTS_PER_S / 1e9,
+            "unit": "G wave64 VALU instructions/s", "frac": round(v / avg / VALU_PEAK_INSTS_PER_S, 4)}
     print(json.dumps(out), flush=True)
 
 
@@ -478,6 +530,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-valu", metavar="PMC_CSV",
+                    help="record SQ_INSTS_VALU / SQ_WAVES per dispatch of --kernel topk from a counter run")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the 30 single launches after a 1 GiB cache flush each (protocol_flush30)")
     ap.add_argument("--graph", action="store_true",
@@ -487,6 +541,9 @@ def main():
                          "reduce: the weighted top-k reduce")
     args = ap.parse_args()
 
+    if args.summarize_valu:
+        summarize_valu(args.summarize_valu, args.kernel, args.seed)
+        return
     if args.summarize_pmc:
         from moe_activation_bit_amd import workloads as wl
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel, args.workload or wl.HEADLINE,
