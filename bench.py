@@ -207,6 +207,29 @@ def valu_for(workload: str, kernel: str):
     return rec.get("valu_insts_per_dispatch")
 
 
+INFINITY_CACHE_BYTES = 256 * 2**20  # MI355X last-level (Infinity) cache
+LAUNCH_BOUND_US = 5.0  # below this HBM time per launch, dispatch and ramp dominate
+
+
+def regime(bytes_per_launch, sets, avg_launch_s, compute_us=0.0):
+    """Labels a line by what bounds it.  `cache` is "hot" when every rotating
+    buffer set together fits the Infinity Cache (the timed launches then read
+    from cache, not HBM), else "streamed".  `launch_bound` is set when the
+    algorithmic bytes would take under LAUNCH_BOUND_US at HBM peak and the
+    launch's own issue bound (`compute_us`, e.g. its VALU instructions at the
+    chip's issue rate) is under it too: then the roofline fraction measures
+    launch latency, and `us_per_call` is the number to read."""
+    footprint = bytes_per_launch * sets
+    hbm_us = bytes_per_launch / (HBM_PEAK_GBS * 1e9) * 1e6
+    return {
+        "cache": "hot" if footprint <= INFINITY_CACHE_BYTES else "streamed",
+        "rotating_footprint_bytes": footprint,
+        "launch_bound": max(hbm_us, compute_us) < LAUNCH_BOUND_US,
+        "hbm_peak_us": round(hbm_us, 3),
+        "us_per_call": round(avg_launch_s * 1e6, 3),
+    }
+
+
 def unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, reps, stream, fused_s):
     """The unfused reference of the same step (swiglu_forward writes fp32 y to
     HBM, then the stand-alone cast reads it), timed like the fused step; its
@@ -429,7 +452,9 @@ def bench_aux(args, torch, np, tk, wl):
     assert tk.tk_init(0) == tk.TkStatus.TK_OK
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-    sets = max(1, args.sets)
+    # the gating's 17.8 MB per launch would stay in the Infinity Cache over 4
+    # sets; 32 sets (570 MB) make it read from HBM like the other lines
+    sets = max(1, args.sets if args.sets is not None else (32 if args.kernel == "topk" else 4))
     if args.copy_calibration:
         copy_calibration(torch, dev)
     name, nbytes = aux_workload(args.kernel, wl, args.seed)
@@ -500,6 +525,7 @@ def bench_aux(args, torch, np, tk, wl):
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(name, args.kernel),
                         "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
                         "avg_launch_us": round(avg * 1e6, 3)},
+           "regime": regime(nbytes, sets, avg),
            "cpu_baseline": None}
     if args.kernel == "topk":
         # the gating is bound by VALU issue, not by its bytes: VALU instructions
@@ -508,6 +534,8 @@ def bench_aux(args, torch, np, tk, wl):
         out["valu_issue"] = None if v is None else {
             "insts_per_launch": round(v), "achieved": round(v / avg / 1e9, 2), "peak": VALU_PEAK_INSTS_PER_S / 1e9,
             "unit": "G wave64 VALU instructions/s", "frac": round(v / avg / VALU_PEAK_INSTS_PER_S, 4)}
+        if v is not None:
+            out["regime"] = regime(nbytes, sets, avg, v / VALU_PEAK_INSTS_PER_S * 1e6)
     print(json.dumps(out), flush=True)
 
 
@@ -522,7 +550,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="rotating input/output buffer sets (default 4; 32 for --kernel topk)")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling measurement")
@@ -581,7 +610,7 @@ def main():
     x_host = wl.make_x(w, args.seed)
     w_host = wl.make_w(w, args.seed)
     sets = []
-    for _ in range(max(1, args.sets)):
+    for _ in range(max(1, args.sets if args.sets is not None else 4)):
         sets.append(dict(
             x=torch.from_numpy(x_host.view(np.int16)).to(dev),
             w=torch.from_numpy(w_host).to(dev),
@@ -656,6 +685,7 @@ def main():
             "algorithmic_bytes_per_launch": bytes_per_step,
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
         },
+        "regime": regime(bytes_per_step, len(sets), avg_launch_s),
         "cpu_baseline": None,
     }
     if not args.no_flushed:
