@@ -2,6 +2,10 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 python bench.py --kernel cast|topk|reduce   (the next-row kernels, each on its own workload)
+python bench.py --suite [--record FILE] [--baseline FILE]
+    (every workload of every kernel, one JSON record per case; a case more
+    than 15% slower than its committed baseline record is a regression and
+    the exit code is 1)
 
 One step = one launch of the kernel over one whole batch of the workload
 (inputs resident in HBM).  The timed region is exactly K back-to-back steps
@@ -441,27 +445,18 @@ CAST_TOKENS, CAST_HIDDEN, CAST_GROUP = 32768, 2048, 128
 TOPK_SHAPE = (16384, 256, 8, 8, 4)  # tokens, experts, k, groups, groups kept
 
 
-def bench_aux(args, torch, np, tk, wl):
-    """The next-row kernels on their own workloads, one JSON line like the
-    headline's: the stand-alone cast (bf16 [65536, 2048] -> E4M3, groups of
-    128, UE8M0), the top-k gating (16384 tokens x 256 experts, 8 groups,
-    keep 4, top-8, normalised) or the weighted top-k reduce (4096 tokens x
-    top-8, hidden 7168, bf16 rows gathered through the position map)."""
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    assert tk.tk_init(0) == tk.TkStatus.TK_OK
-    stream = torch.cuda.current_stream()
-    sh = int(stream.cuda_stream)
-    # the gating's 17.8 MB per launch would stay in the Infinity Cache over 4
-    # sets; 32 sets (570 MB) make it read from HBM like the other lines
-    sets = max(1, args.sets if args.sets is not None else (32 if args.kernel == "topk" else 4))
-    if args.copy_calibration:
-        copy_calibration(torch, dev)
-    name, nbytes = aux_workload(args.kernel, wl, args.seed)
-    if args.kernel == "cast":
+def aux_setup(kernel, torch, np, tk, wl, seed, sets, dev, sh):
+    """Device buffers and the launch closure of one next-row kernel on its own
+    workload: the stand-alone cast (bf16 [65536, 2048] -> E4M3, groups of 128,
+    UE8M0), the top-k gating (16384 tokens x 256 experts, 8 groups, keep 4,
+    top-8, normalised) or the weighted top-k reduce (4096 tokens x top-8,
+    hidden 7168, bf16 rows gathered through the position map).  Returns
+    (workload name, algorithmic bytes per launch, step(i), metric, config, rows)."""
+    name, nbytes = aux_workload(kernel, wl, seed)
+    if kernel == "cast":
         n, hidden, group = CAST_TOKENS, CAST_HIDDEN, CAST_GROUP
         w = wl.Workload(name, n, hidden, 2.0, "fp8", group, "ue8m0", None, "uniform")
-        xh = wl.make_x(w, args.seed)  # [n, 2*hidden] bf16 N(0,2) samples, read as [2n, hidden] rows
+        xh = wl.make_x(w, seed)  # [n, 2*hidden] bf16 N(0,2) samples, read as [2n, hidden] rows
         assert xh.size == 2 * n * hidden
         n2 = 2 * n
         xs = [torch.from_numpy(xh.view(np.int16)).to(dev) for _ in range(sets)]
@@ -469,27 +464,28 @@ def bench_aux(args, torch, np, tk, wl):
         ss = [torch.empty((n2, hidden // group), dtype=torch.uint8, device=dev) for _ in range(sets)]
         del xh
 
-        def step(i):
+        def step(i, stream_handle=sh):
             k = i % sets
-            rc = tk.tk_cast_fp8(xs[k], tk.TK_DTYPE_BF16, n2, hidden, group, tk.TK_SCALE_UE8M0, cs[k], ss[k], sh)
+            rc = tk.tk_cast_fp8(xs[k], tk.TK_DTYPE_BF16, n2, hidden, group, tk.TK_SCALE_UE8M0, cs[k], ss[k],
+                                stream_handle)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "stand-alone bf16->FP8 cast HBM GB/s (frac of peak) at 1 MI355X"
         config = {"workload": name, "rows": n2, "hidden": hidden, "group_size": group, "format": "e4m3",
                   "scale": "ue8m0", "input": "bf16 [rows, hidden]"}
         rows = n2
-    elif args.kernel == "reduce":
+    elif kernel == "reduce":
         r = wl.REDUCE_WORKLOADS[wl.REDUCE_HEADLINE]
-        pos, wts, rsc, n_rows = wl.make_routing(r, args.seed)
-        xh = wl.make_expert_rows(r, args.seed, n_rows)
+        pos, wts, rsc, n_rows = wl.make_routing(r, seed)
+        xh = wl.make_expert_rows(r, seed, n_rows)
         xs = [torch.from_numpy(xh.view(np.int16)).to(dev) for _ in range(sets)]
         del xh
         pd, wd, rd = (torch.from_numpy(pos).to(dev), torch.from_numpy(wts).to(dev), torch.from_numpy(rsc).to(dev))
         outs = [torch.empty((r.tokens, r.hidden), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
 
-        def step(i):
+        def step(i, stream_handle=sh):
             j = i % sets
             rc = tk.tk_moe_reduce(xs[j], rd, pd, wd, r.global_scale, r.tokens, r.k, r.hidden, n_rows,
-                                  tk.TK_DTYPE_BF16, outs[j], sh)
+                                  tk.TK_DTYPE_BF16, outs[j], stream_handle)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "weighted top-k MoE reduce HBM GB/s (frac of peak) at 1 MI355X"
         config = {"workload": name, "tokens": r.tokens, "k": r.k, "experts": r.experts, "hidden": r.hidden,
@@ -498,20 +494,42 @@ def bench_aux(args, torch, np, tk, wl):
         rows = r.tokens
     else:
         T, E, k, ng, tg = TOPK_SHAPE
-        key = wl.stream_key("topk_gate", args.seed, "scores")
+        key = wl.stream_key("topk_gate", seed, "scores")
         sh_ = wl.uniform(key, 0, T * E).reshape(T, E).astype(np.float32)
         sc = [torch.from_numpy(sh_).to(dev) for _ in range(sets)]
         idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(sets)]
         wt = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(sets)]
 
-        def step(i):
+        def step(i, stream_handle=sh):
             j = i % sets
-            rc = tk.tk_topk_gate(sc[j], T, E, k, ng, tg, 1, idx[j], wt[j], sh)
+            rc = tk.tk_topk_gate(sc[j], T, E, k, ng, tg, 1, idx[j], wt[j], stream_handle)
             assert rc == tk.TkStatus.TK_OK, rc
         metric = "deterministic top-k gating tokens/s and HBM GB/s at 1 MI355X"
         config = {"workload": name, "tokens": T, "experts": E, "k": k, "n_group": ng, "topk_group": tg,
                   "normalise": True, "scores": "U(0,1) fp32"}
         rows = T
+    return name, nbytes, step, metric, config, rows
+
+
+def aux_sets(kernel, requested=None):
+    """Rotating buffer sets of a next-row line: 4, or 32 for the gating, whose
+    17.8 MB per launch would otherwise stay in the Infinity Cache (32 sets,
+    570 MB, make it read from HBM like the other lines)."""
+    return max(1, requested if requested is not None else (32 if kernel == "topk" else 4))
+
+
+def bench_aux(args, torch, np, tk, wl):
+    """The next-row kernels on their own workloads, one JSON line like the
+    headline's (see aux_setup for the workloads)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    assert tk.tk_init(0) == tk.TkStatus.TK_OK
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    sets = aux_sets(args.kernel, args.sets)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    name, nbytes, step, metric, config, rows = aux_setup(args.kernel, torch, np, tk, wl, args.seed, sets, dev, sh)
     kernel = KERNELS[args.kernel][1].replace("\\b", "").rstrip("<")
     wall, gpu = _timed(torch, stream, step, args.steps, args.warmup)
     avg = gpu / args.steps
@@ -537,6 +555,141 @@ def bench_aux(args, torch, np, tk, wl):
         if v is not None:
             out["regime"] = regime(nbytes, sets, avg, v / VALU_PEAK_INSTS_PER_S * 1e6)
     print(json.dumps(out), flush=True)
+
+
+def fused_setup(torch, np, tk, wl, name, seed, nsets, dev, sh):
+    """Device buffers (nsets rotating sets of x, topk_weight, codes, scales and
+    the clamp counter) and the launch closure step(i[, stream]) of one fused
+    workload.  Returns (workload, rows, fmt, scale fmt, clamp limit, sets, step)."""
+    w = wl.workload(name)
+    n = wl.num_rows(w, seed)
+    fmt = 8 if w.fmt == "fp8" else 4
+    sfmt = tk.TK_SCALE_FP32 if w.scale_fmt == "fp32" else tk.TK_SCALE_UE8M0
+    fn = tk.tk_swiglu_cast_fp8 if fmt == 8 else tk.tk_swiglu_cast_fp4
+    clamp = math.inf if w.clamp_limit is None else w.clamp_limit
+    x_host = wl.make_x(w, seed)
+    w_host = wl.make_w(w, seed)
+    sets = []
+    for _ in range(max(1, nsets)):
+        sets.append(dict(
+            x=torch.from_numpy(x_host.view(np.int16)).to(dev),
+            w=torch.from_numpy(w_host).to(dev),
+            codes=torch.empty((n, w.code_bytes_per_row), dtype=torch.uint8, device=dev),
+            scales=torch.empty((n, w.groups_per_row), dtype=torch.float32 if sfmt == 0 else torch.uint8, device=dev),
+            count=torch.zeros(1, dtype=torch.int64, device=dev),
+        ))
+    del x_host
+
+    def step(i, stream_handle=sh):
+        s = sets[i % len(sets)]
+        rc = fn(s["x"], s["w"], n, w.hidden, w.group_size, clamp, sfmt, s["codes"], s["scales"],
+                s["count"] if w.clamp_limit is not None else None, stream_handle)
+        if rc != tk.TkStatus.TK_OK:
+            raise RuntimeError(tk.tk_status_str(rc))
+    return w, n, fmt, sfmt, clamp, sets, step
+
+
+# The benchmark suite: every workload of the fused kernel and the next-row
+# kernels' lines, one record per case, compared with a committed baseline by
+# the regression rule of TileKernels' benchmark plugin ("TileKernels从入门到精通"
+# ch.5, "铁血防线"): a case regresses when its time exceeds the baseline's by
+# more than the threshold (15% there).
+BASELINES = os.path.join(ROOT, "profiles", "bench_baselines.jsonl")
+REGRESSION_THRESHOLD = 0.15
+SUITE_AUX = ("cast", "reduce", "topk")
+SUITE_OPS = {"fused": "swiglu_cast", "cast": "cast", "reduce": "moe_reduce", "topk": "topk_gate"}
+
+
+def case_key(kernel: str, params: dict) -> str:
+    """Record key in the pages' shape, op/fwd[k=v,...], sorted by parameter name."""
+    inner = ",".join(f"{k}={params[k]}" for k in sorted(params))
+    return f"{SUITE_OPS[kernel]}/fwd[{inner}]"
+
+
+def compare_records(records, baseline, threshold=REGRESSION_THRESHOLD):
+    """Each record against the baseline record of the same key.  Returns
+    [(key, time_us, baseline_us or None, ratio or None, status)] with status
+    "ok", "REGRESSION" (time / baseline > 1 + threshold), "new" (no baseline)
+    and, for baseline keys this run did not measure, "missing"."""
+    base = {b["key"]: b for b in baseline}
+    out = []
+    for r in records:
+        b = base.get(r["key"])
+        if b is None:
+            out.append((r["key"], r["time_us"], None, None, "new"))
+            continue
+        ratio = r["time_us"] / b["time_us"]
+        out.append((r["key"], r["time_us"], b["time_us"], ratio, "REGRESSION" if ratio > 1.0 + threshold else "ok"))
+    seen = {r["key"] for r in records}
+    out += [(k, None, b["time_us"], None, "missing") for k, b in base.items() if k not in seen]
+    return out
+
+
+def read_records(path):
+    with open(path) as fh:
+        return [json.loads(line) for line in fh if line.strip()]
+
+
+def run_suite(args, torch, np, tk, wl):
+    """Times every case (W warm-up then K back-to-back launches between two
+    HIP events, as the headline line; launch-bound cases by the same K
+    launches replayed from one HIP graph), prints one JSON record per case,
+    optionally writes them to --record, and compares them with the baseline
+    file; returns the process exit code (1 when a case regressed)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    assert tk.tk_init(0) == tk.TkStatus.TK_OK
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    cases = [("fused", name) for name in wl.WORKLOADS] + [(k, None) for k in SUITE_AUX]
+    records = []
+    for kernel, name in cases:
+        if kernel == "fused":
+            nsets = args.sets if args.sets is not None else 4
+            w, n, fmt, _, _, sets, step = fused_setup(torch, np, tk, wl, name, args.seed, nsets, dev, sh)
+            nbytes = w.algorithmic_bytes(n)
+            params = {"workload": name, "num_tokens": n, "hidden": w.hidden, "group_size": w.group_size,
+                      "fmt": "e4m3" if fmt == 8 else "e2m1", "scale": w.scale_fmt, "seed": args.seed}
+            del sets
+        else:
+            nsets = aux_sets(kernel, args.sets)
+            name, nbytes, step, _, _, _ = aux_setup(kernel, torch, np, tk, wl, args.seed, nsets, dev, sh)
+            params = {"workload": name, "seed": args.seed}
+        log(f"[suite] {kernel} {name} ...")
+        _, gpu = _timed(torch, stream, step, args.steps, args.warmup)
+        avg = gpu / args.steps
+        v = valu_for(name, kernel) if kernel == "topk" else None
+        reg = regime(nbytes, nsets, avg, 0.0 if v is None else v / VALU_PEAK_INSTS_PER_S * 1e6)
+        timing = "events"
+        if reg["launch_bound"]:
+            # eager back-to-back launches of a few microseconds measure the host's
+            # launch issue; the launches replayed from one HIP graph measure the GPU
+            avg = graph_replay(torch, step, args.steps, nbytes)["us_per_launch"] / 1e6
+            timing = "graph"
+        rec = {"key": case_key(kernel, params), "kernel": KERNELS[kernel][1].replace("\\b", "").rstrip("<"),
+               "operation": "fwd", "params": params, "time_us": round(avg * 1e6, 3), "timing": timing,
+               "bandwidth_gbs": round(nbytes / avg / 1e9, 1), "frac_of_peak": round(nbytes / avg / 1e9 / HBM_PEAK_GBS, 4),
+               "regime": reg}
+        records.append(rec)
+        print(json.dumps(rec), flush=True)
+        del step
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if args.record:
+        with open(args.record, "w") as fh:
+            for r in records:
+                fh.write(json.dumps(r) + "\n")
+    if not args.baseline or args.baseline == "none" or not os.path.exists(args.baseline):
+        log("[suite] no baseline to compare with")
+        return 0
+    rows = compare_records(records, read_records(args.baseline), args.threshold)
+    log(f"[suite] against {os.path.relpath(args.baseline, ROOT)} (regression: > {args.threshold:.0%} slower)")
+    for key, t, b, ratio, status in rows:
+        tt = "-" if t is None else f"{t:.2f}"
+        bb = "-" if b is None else f"{b:.2f}"
+        rr = "-" if ratio is None else f"{ratio:.3f}"
+        log(f"  {status:<10} {tt:>9} us  baseline {bb:>9} us  ratio {rr:>6}  {key}")
+    return 1 if any(r[4] == "REGRESSION" for r in rows) else 0
 
 
 def main():
@@ -568,6 +721,13 @@ def main():
     ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce"], default="fused",
                     help="fused (default): the fused SwiGLU + cast; cast: the stand-alone cast; topk: the gating; "
                          "reduce: the weighted top-k reduce")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload of every kernel, one JSON record per case, and compare with "
+                         "--baseline (exit code 1 when a case is more than --threshold slower)")
+    ap.add_argument("--baseline", default=BASELINES,
+                    help="baseline records for --suite ('none' to skip the comparison)")
+    ap.add_argument("--record", default=None, help="write --suite's records to this JSONL file")
+    ap.add_argument("--threshold", type=float, default=REGRESSION_THRESHOLD)
     args = ap.parse_args()
 
     if args.summarize_valu:
@@ -590,44 +750,22 @@ def main():
     import moe_activation_bit_amd as tk
     from moe_activation_bit_amd import workloads as wl
 
+    if args.suite:
+        sys.exit(run_suite(args, torch, np, tk, wl))
     if args.kernel != "fused":
         return bench_aux(args, torch, np, tk, wl)
 
     name = args.workload or wl.HEADLINE
-    w = wl.workload(name)
-    n = wl.num_rows(w, args.seed)
-    fmt = 8 if w.fmt == "fp8" else 4
-    sfmt = tk.TK_SCALE_FP32 if w.scale_fmt == "fp32" else tk.TK_SCALE_UE8M0
-    fn = tk.tk_swiglu_cast_fp8 if fmt == 8 else tk.tk_swiglu_cast_fp4
-    clamp = math.inf if w.clamp_limit is None else w.clamp_limit
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     assert tk.tk_init(0) == tk.TkStatus.TK_OK
-
-    log(f"[bench] workload {name}: rows {n}, hidden {w.hidden}, steps {args.steps}, warmup {args.warmup}")
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    x_host = wl.make_x(w, args.seed)
-    w_host = wl.make_w(w, args.seed)
-    sets = []
-    for _ in range(max(1, args.sets if args.sets is not None else 4)):
-        sets.append(dict(
-            x=torch.from_numpy(x_host.view(np.int16)).to(dev),
-            w=torch.from_numpy(w_host).to(dev),
-            codes=torch.empty((n, w.code_bytes_per_row), dtype=torch.uint8, device=dev),
-            scales=torch.empty((n, w.groups_per_row), dtype=torch.float32 if sfmt == 0 else torch.uint8, device=dev),
-            count=torch.zeros(1, dtype=torch.int64, device=dev),
-        ))
-    del x_host
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-
-    def step(i, stream_handle=sh):
-        s = sets[i % len(sets)]
-        rc = fn(s["x"], s["w"], n, w.hidden, w.group_size, clamp, sfmt, s["codes"], s["scales"],
-                s["count"] if w.clamp_limit is not None else None, stream_handle)
-        if rc != tk.TkStatus.TK_OK:
-            raise RuntimeError(tk.tk_status_str(rc))
+    w, n, fmt, sfmt, clamp, sets, step = fused_setup(torch, np, tk, wl, name, args.seed,
+                                                     args.sets if args.sets is not None else 4, dev, sh)
+    log(f"[bench] workload {name}: rows {n}, hidden {w.hidden}, steps {args.steps}, warmup {args.warmup}")
 
     for i in range(args.warmup):
         step(i)
