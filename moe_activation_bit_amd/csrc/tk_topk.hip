@@ -19,10 +19,12 @@
 //      group ranks from wave-uniform reads of every group sum; lanes of
 //      dropped groups empty their lists.
 //   3. k rounds of a tournament between the lanes' list heads: a DPP max of
-//      the head keys (quad_perm, row_half_mirror, row_mirror, then four
-//      v_readlane), the first lane whose head equals it (ballot + s_ff1: the
-//      smallest index among equal scores), the winner's index by v_readlane,
-//      and the winner pops its head; lane `round` keeps the pick's index.
+//      the head keys (quad_perm, row_half_mirror, row_mirror, then row
+//      broadcasts into lane 63 and one v_readlane), the first lane whose head
+//      equals it (ballot + s_ff1: the smallest index among equal scores), the
+//      winner's expert index from its packed slot list (one v_readlane and
+//      scalar arithmetic), and the winner pops its head (its keys shift, its
+//      slot list shifts by 3 bits); lane `round` keeps the pick's index.
 //      Output lane j then re-reads pick j's own score, and the
 //      normalising sum adds those k values in pick order after the rounds.
 // Each round is about three dozen VALU/SALU instructions with no LDS traffic.
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     for (int j = 0; j < C; ++j) {
         const uint32_t e = lane * C + j;
         key[j] = e < experts ? ordered(v[j]) : 0u;
-        idx[j] = e;
+        idx[j] = (uint32_t)j; // slot within the lane
     }
 #pragma unroll
     for (int i = 1; i < C; ++i) {
@@ -176,20 +178,25 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         }
     }
 
-    // ---- 3. k rounds between the list heads; pick it goes to lane it
+    // ---- 3. k rounds between the list heads; pick it goes to lane it.  The
+    // lane's sorted slots are packed 3 bits each (C <= 8), head lowest, so a
+    // pop is one shift and the winner's expert index comes from one readlane.
+    uint32_t slots = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        slots |= idx[j] << (3 * j);
     int32_t my_idx = 0;
     for (uint32_t it = 0; it < k; ++it) {
         const uint32_t best = wave_umax(key[0]);
         const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == best);
         const uint32_t owner = (uint32_t)__builtin_ctzll(hit); // lowest lane = smallest index
-        const uint32_t e = __builtin_amdgcn_readlane(idx[0], owner);
+        const uint32_t e = owner * C + (__builtin_amdgcn_readlane(slots, owner) & 7u);
         if (lane == owner) {
 #pragma unroll
-            for (int j = 0; j + 1 < C; ++j) {
+            for (int j = 0; j + 1 < C; ++j)
                 key[j] = key[j + 1];
-                idx[j] = idx[j + 1];
-            }
             key[C - 1] = 0u;
+            slots >>= 3;
         }
         my_idx = lane == it ? (int32_t)e : my_idx;
     }
