@@ -336,7 +336,9 @@ int oracle_cast_bf16(const uint16_t* x, int64_t n, int64_t hidden, int64_t group
  *
  * Readings: "a beats b" means score_a > score_b, or score_a == score_b (as
  * numbers, so -0 == +0) and a < b.  With n_group > 1 the experts form n_group
- * consecutive groups; a group's score is RN(best + second best) of its members;
+ * consecutive groups; a group's score is RN(best + second best) of its members,
+ * and a score that is NaN (best +inf, second best -inf) counts as -inf, so that
+ * groups are totally ordered (the pages do not say how such a group ranks);
  * the topk_group best groups (same tie rule on group index) are kept and the k
  * experts are chosen among their members only.  Output order: best first.
  * Weights are the chosen scores, or, when normalise is set, each chosen score
@@ -375,6 +377,8 @@ int oracle_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64
                     }
                 }
                 gscore[g] = s[b1] + s[b2];
+                if (gscore[g] != gscore[g]) /* +inf + -inf: ranks as -inf */
+                    gscore[g] = -INFINITY;
             }
             memset(taken, 0, (size_t)n_group);
             memset(allowed, 0, (size_t)experts);

@@ -35,6 +35,8 @@ MUTANTS = [
      "(uint8_t)(tmp[2 * i + 1] | (tmp[2 * i] << 4))"),
     ("topk_ties_to_larger_index", "return sa > sb || (sa == sb && a < b);", "return sa > sb || (sa == sb && a > b);"),
     ("topk_group_score_best_only", "gscore[g] = s[b1] + s[b2];", "gscore[g] = s[b1];"),
+    ("topk_nan_group_score_kept_as_nan",
+     "if (gscore[g] != gscore[g]) /* +inf + -inf: ranks as -inf */\n                    gscore[g] = -INFINITY;", ""),
     ("topk_sum_worst_first", "for (int64_t j = 0; j < k; ++j)\n                sum += w_out[t * k + j];",
      "for (int64_t j = k - 1; j >= 0; --j)\n                sum += w_out[t * k + j];"),
     ("reduce_scale_by_slot", "w[t * k + j] * row_scale[p]", "w[t * k + j] * row_scale[j]"),

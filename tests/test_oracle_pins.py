@@ -317,7 +317,8 @@ def _brute_topk(s, k, n_group, topk_group, normalise):
         gsum = []
         for g in range(n_group):
             vals = sorted((float(v) for v in s[g * per:(g + 1) * per]), reverse=True)
-            gsum.append(float(np.float32(vals[0]) + np.float32(vals[1])))
+            v = float(np.float32(vals[0]) + np.float32(vals[1]))
+            gsum.append(-math.inf if math.isnan(v) else v)  # +inf + -inf ranks as -inf
         groups = sorted(range(n_group), key=lambda g: (-gsum[g], g))[:topk_group]
         allowed = {e for g in groups for e in range(g * per, (g + 1) * per)}
     order = sorted(allowed, key=lambda e: (-float(s[e]), e))[:k]
@@ -348,6 +349,38 @@ def test_topk_gate_matches_brute_force(E, k, ng, tg, normalise):
         order, ww = _brute_topk(s[t], k, ng, tg, normalise)
         assert idx[t].tolist() == order, t
         assert w[t].tolist() == ww, t
+
+
+@pytest.mark.parametrize("ng,tg", [(8, 4), (8, 7), (4, 2), (16, 3)])
+def test_topk_gate_infinite_scores_and_nan_group_sums(ng, tg):
+    """Groups whose two best scores are +inf and -inf (a NaN sum, ranked as
+    -inf) at every group position, whole groups of -inf, +inf pairs and
+    finite rows, against brute force by sorting."""
+    E, k = 256, 8
+    per = E // ng
+    rng = np.random.default_rng(ng * 31 + tg)
+    T = 3 * ng + 6
+    s = rng.uniform(-1, 1, (T, E)).astype(np.float32)
+    for t in range(T):
+        g = t % ng
+        if t < 2 * ng:  # group g: one +inf, the rest -inf (NaN sum)
+            s[t, g * per:(g + 1) * per] = -np.inf
+            s[t, g * per + (t % per)] = np.inf
+        if ng <= t < 2 * ng:  # and the next group all -inf (a -inf sum that ties with it)
+            h = (g + 1) % ng
+            s[t, h * per:(h + 1) * per] = -np.inf
+        elif 2 * ng <= t < 3 * ng:  # two +inf in group g (an +inf sum)
+            s[t, g * per] = s[t, g * per + 1] = np.inf
+    kk = min(k, tg * per)
+    idx, w = oracle.topk_gate(s, kk, ng, tg, False)
+    for t in range(T):
+        order, ww = _brute_topk(s[t], kk, ng, tg, False)
+        assert idx[t].tolist() == order, (t, idx[t].tolist(), order)
+        assert w[t].tolist() == ww, t
+    # the NaN group of the first rows is never kept while tg finite groups remain
+    for t in range(ng):
+        if tg < ng:
+            assert not any(int(e) // per == t % ng for e in idx[t]), t
 
 
 def test_topk_gate_invariants():
