@@ -16,8 +16,11 @@
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
 //      quad_perm / half-row and row mirrors, lane shuffles past 16 lanes);
-//      group ranks from wave-uniform reads of every group sum; lanes of
-//      dropped groups empty their lists.
+//      a NaN group sum (+inf and -inf) counts as -inf.  Group ranks: with at
+//      most 8 groups, lane 8h + h' compares group h' with group h and one
+//      ballot holds every pair (group h's rank = set bits in byte h); with
+//      more, wave-uniform reads of every group sum.  Lanes of dropped groups
+//      empty their lists.
 //   3. k rounds of a tournament between the lanes' list heads: a DPP max of
 //      the head keys (quad_perm, row_half_mirror, row_mirror, then row
 //      broadcasts into lane 63 and one v_readlane), the first lane whose head
@@ -164,12 +167,32 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
             merge_top2<0x140>(a1, a2); // row_mirror
         for (uint32_t m = 16; m < (1u << gl_log2); m <<= 1)
             merge_top2_from(a1, a2, (uint32_t)__shfl_xor((int)a1, (int)m), (uint32_t)__shfl_xor((int)a2, (int)m));
-        const float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
+        float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
+        if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf (groups stay totally ordered)
+            gsum = -INFINITY;
         const uint32_t my_g = lane >> gl_log2;
         uint32_t rank = 0;
-        for (uint32_t h = 0; h < n_group; ++h) {
-            const float gh = ffrom(__builtin_amdgcn_readlane(fbits(gsum), h << gl_log2));
-            rank += beats(gh, h, gsum, my_g) ? 1u : 0u;
+        if (n_group <= 8) {
+            // all pairs at once: lane 8h + h' compares group h' against group
+            // h, and group h's rank is the count of set bits in byte h of the
+            // ballot
+            const uint32_t h = lane >> 3, h2 = lane & 7u;
+            // ds_bpermute addresses lanes in bytes; rows and columns past the
+            // last group read the last group and are masked out below
+            const float g_h = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)((min(h, n_group - 1u) << gl_log2) << 2), (int)fbits(gsum)));
+            const float g_h2 = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)((min(h2, n_group - 1u) << gl_log2) << 2), (int)fbits(gsum)));
+            // beats(g_h2, h2, g_h, h) without short-circuit branches
+            const uint32_t b = (uint32_t)(max(h, h2) < n_group) &
+                               ((uint32_t)(g_h2 > g_h) | ((uint32_t)(g_h2 == g_h) & (uint32_t)(h2 < h)));
+            const uint64_t m = __builtin_amdgcn_ballot_w64(b != 0u);
+            rank = (uint32_t)__builtin_popcountll((m >> (8u * my_g)) & 0xFFull);
+        } else {
+            for (uint32_t hh = 0; hh < n_group; ++hh) {
+                const float gh = ffrom(__builtin_amdgcn_readlane(fbits(gsum), hh << gl_log2));
+                rank += beats(gh, hh, gsum, my_g) ? 1u : 0u;
+            }
         }
         if (rank >= topk_group) {
 #pragma unroll

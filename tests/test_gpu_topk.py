@@ -32,6 +32,8 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     # 5 to 8 experts per lane
     (320, 6, 1, 1), (384, 8, 1, 1), (384, 8, 12, 4), (448, 8, 1, 1), (512, 8, 8, 4), (512, 16, 16, 4),
     (512, 64, 1, 1), (500, 7, 1, 1),
+    # group counts the all-pairs group rank covers: 2 groups of 32 lanes, 3, 6 (not a power of two), all kept
+    (256, 3, 2, 1), (96, 5, 3, 2), (48, 4, 6, 3), (256, 8, 8, 8),
 ]
 
 
@@ -102,3 +104,31 @@ def test_topk_special_values_and_extremes():
     one = np.array([[0.25]], dtype=np.float32)
     gi, gw = run(one, 1, 1, 1, 1)
     assert gi[0, 0] == 0 and gw[0, 0] == 1.0
+
+
+@pytest.mark.parametrize("ng,tg", [(8, 4), (8, 7), (4, 2), (16, 3), (6, 3)])
+def test_topk_nan_group_sums(ng, tg):
+    """A group whose two best scores are +inf and -inf sums to NaN and ranks
+    as -inf; such a group at every position, tied with an all -inf group, and
+    groups with two +inf."""
+    E = 256 if ng != 6 else 48
+    per = E // ng
+    k = min(8, tg * per)
+    T = 3 * ng + 6
+    print("[gpu-case] topk NaN group sums", ng, tg, flush=True)
+    u = wl.uniform(wl.stream_key("topk_test", ng * 10 + tg, "nan_groups"), 0, T * E).reshape(T, E)
+    s = (2 * u - 1).astype(np.float32)
+    for t in range(T):
+        g = t % ng
+        if t < 2 * ng:
+            s[t, g * per:(g + 1) * per] = -np.inf
+            s[t, g * per + (t % per)] = np.inf
+        if ng <= t < 2 * ng:
+            h = (g + 1) % ng
+            s[t, h * per:(h + 1) * per] = -np.inf
+        elif 2 * ng <= t < 3 * ng:
+            s[t, g * per] = s[t, g * per + 1] = np.inf
+    gi, gw = run(s, k, ng, tg, 0)
+    oi, ow = oracle.topk_gate(s, k, ng, tg, False)
+    assert np.array_equal(gi, oi), np.argwhere(gi != oi)[:4]
+    assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32))
