@@ -1,6 +1,6 @@
 """GPU parity on a seeded random sweep of the parameters of the fused step
-(tk_swiglu_cast_fp8/fp4) and the stand-alone cast (tk_cast_fp8/fp4) against
-the oracle, bit-exact.
+(tk_swiglu_cast_fp8/fp4), the stand-alone cast (tk_cast_fp8/fp4) and the
+weighted top-k reduce (tk_moe_reduce) against the oracle, bit-exact.
 
 Each case draws its rows (1 .. 300), width (multiples of 8 from 8 to 8192,
 with and without a partial last 512-column step), group (per-token or any
@@ -70,3 +70,31 @@ def test_random_standalone_cast_case(i):
     xd = torch.from_numpy(x.view(np.int16)).to(DEV)
     got = run_standalone_cast(xd, tk.TK_DTYPE_BF16, n, hidden, group, fmt, sfmt)
     same_cast(got, oracle.cast_bf16(x, group, fmt, sfmt), f"random cast case {i}")
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_reduce_case(i):
+    """tk_moe_reduce on a random draw: tokens, k (1 .. 32), width, position
+    map with repeated rows, dropped (-1) and out-of-range entries, weights
+    with zeros and negatives, optional per-row scales, global scale of
+    either sign and tiny magnitude, bf16 or fp32 output."""
+    from test_gpu_reduce import run_reduce, same as same_reduce
+    rng = np.random.default_rng(30_000 + i)
+    tokens = int(rng.choice([1, 7, 64, 200]))
+    k = int(rng.choice([1, 2, 3, 5, 8, 9, 12, 16, 24, 32]))
+    hidden = int(rng.choice([8, 24, 64, 520, 1024, 2056, 7168]))
+    n_rows = int(rng.integers(1, 3 * tokens * k // 2 + 2))
+    pos = rng.integers(0, n_rows, size=(tokens, k)).astype(np.int32)
+    pos[rng.random((tokens, k)) < 0.1] = -1
+    pos[rng.random((tokens, k)) < 0.03] = n_rows + 5
+    w = rng.uniform(-0.25, 1.0, (tokens, k)).astype(np.float32)
+    w[rng.random((tokens, k)) < 0.1] = 0.0
+    rs = rng.uniform(0.5, 2.0, n_rows).astype(np.float32) if rng.random() < 0.5 else None
+    gs = float(rng.choice([1.0, 2.5, -0.75, 1e-30]))
+    out_bf16 = bool(rng.random() < 0.6)
+    mag = rng.choice(MAGNITUDES, size=(n_rows, 1))
+    x = bf16_bits(rng.standard_normal((n_rows, hidden)) * mag)
+    say("random reduce", i, dict(tokens=tokens, k=k, hidden=hidden, n_rows=n_rows, scaled=rs is not None, gs=gs,
+                                 bf16=out_bf16))
+    got = run_reduce(x, pos, w, rs, gs, out_bf16)
+    same_reduce(got, oracle.moe_reduce(x, pos, w, rs, gs, out_bf16), f"random reduce case {i}")
