@@ -46,6 +46,7 @@
 #include <cstring>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "tk.h"
 #include "tk_quant.h"
@@ -156,23 +157,73 @@ __device__ __forceinline__ float lut_sigma(const float2* lut, uint32_t word, uin
 
 constexpr int kLutLdsBytes = kLutSize * 8;
 
+// Clamp counters: a wave's count of gates above the limit.  WaveCount keeps
+// the wave's total in scalar registers (a ballot and popcount per element);
+// LaneCount keeps one count per lane (a VALU add per element) and sums the
+// lanes once at the end.  Row-reduced units use WaveCount; per-block units use
+// LaneCount, because there the compiler holds every element's compare mask in
+// scalar registers until the step's group reductions are done and spills them
+// to VGPR lanes (the per-block clamp launch of 32768 x 2048 took 65 us without
+// the counter's atomics against 57 us unclamped; with LaneCount, 59.5 us).
+struct WaveCount {
+    unsigned long long n = 0;
+    __device__ __forceinline__ void add(bool hit) { n += __builtin_popcountll(__ballot(hit)); }
+    __device__ __forceinline__ unsigned long long total() const { return n; }
+};
+struct LaneCount {
+    uint32_t n = 0;
+    __device__ __forceinline__ void add(bool hit) { n += hit ? 1u : 0u; }
+    // every lane of the wave must call this
+    __device__ __forceinline__ unsigned long long total() const
+    {
+        unsigned long long t = n;
+#pragma unroll
+        for (int m = kWaveSize / 2; m >= 1; m >>= 1)
+            t += __shfl_xor(t, m);
+        return t;
+    }
+};
+
+// The workgroup's clamp count into the caller's int64 counter: each wave adds
+// its total to `wg` in LDS and one global atomic goes out per workgroup.
+// Adding from every wave put 2048 atomics on one address at the end of a
+// persistent launch, where they serialise: 11-16 us at the end of a
+// 32768-row launch.  Every thread of the workgroup calls this; `wg` was
+// zeroed by thread 0 before an earlier barrier.
+template <class CNT>
+__device__ __forceinline__ void flush_clamp_count(unsigned long long* count, unsigned long long* wg, const CNT& c,
+                                                  uint32_t lane)
+{
+    const unsigned long long t = c.total();
+    if (lane == 0 && t)
+        atomicAdd(wg, t);
+    __syncthreads();
+    if (threadIdx.x == 0 && count && *wg)
+        atomicAdd(count, *wg);
+}
+
 // One element: gate and up are the bf16 halves at bit POS of `gword` / `uword`.
 // a = RN(g * sigma(g)) (or the clamped gate's activation), b = RN(a * u),
 // y = RN(b * w); three fp32 products, never fused.  `counts` is false on lanes
 // past the end of the row, whose gates must not enter the clamp count.
-template <int POS, bool CLAMP>
+template <int POS, bool CLAMP, class CNT>
 __device__ __forceinline__ float swiglu_elem(const LutT* lut, uint32_t gword, uint32_t uword, float w,
-                                             float limit, float a_limit, unsigned long long& clamped,
-                                             bool counts = true)
+                                             float limit, float a_limit, CNT& clamped, bool counts = true)
 {
     const uint32_t gbits = POS ? (gword & 0xFFFF0000u) : (gword << 16);
     float u = as_float(POS ? (uword & 0xFFFF0000u) : (uword << 16));
     const float g = as_float(gbits);
     float a = g * lut_sigma<POS>(lut, gword, gbits);
     if constexpr (CLAMP) {
-        const bool over = g > limit;
-        clamped += __builtin_popcountll(__ballot(over && counts));
-        a = over ? a_limit : a;
+        clamped.add(g > limit && counts);
+        // The clamped gate's activation, RN(min(g, L) * sigma(min(g, L))), is
+        // min(a, a_limit) with a_limit = RN(L * sigma(L)): L > 0, and
+        // RN(g * sigma(g)) does not decrease with g > 0 and is <= -0 for g <= -0,
+        // so a >= a_limit when g > L and a <= a_limit when g <= L.  The min is
+        // taken on the bit patterns as signed integers, which order every
+        // negative value (-0 included) below a_limit >= +0: a gate of -0 keeps
+        // its -0 even when a_limit rounds to +0 (the smallest L).
+        a = __builtin_bit_cast(float, min(__builtin_bit_cast(int32_t, a), __builtin_bit_cast(int32_t, a_limit)));
         u = __builtin_amdgcn_fmed3f(u, -limit, limit);
     }
     const float b = a * u;
@@ -212,9 +263,9 @@ __device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t 
 
 // One 8-column step of a loaded unit: ys = w * silu(gate) * up for the lane's
 // columns; returns the lane's abs-max bits (0 for a lane past the row end).
-template <bool CLAMP, bool PARTIAL>
+template <bool CLAMP, bool PARTIAL, class CNT>
 __device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4 u, float w, bool valid, float limit,
-                                                 float a_limit, unsigned long long& clamped, float (&ys)[8])
+                                                 float a_limit, CNT& clamped, float (&ys)[8])
 {
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
@@ -238,9 +289,9 @@ __device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4
 constexpr int kStreamMinSteps = 8;
 constexpr int kStreamDepth = 4;
 
-template <bool CLAMP, int SPU, bool PARTIAL>
+template <bool CLAMP, int SPU, bool PARTIAL, class CNT>
 __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, uint32_t lane, uint32_t u, float limit,
-                                            float a_limit, unsigned long long& clamped, uint32_t& row,
+                                            float a_limit, CNT& clamped, uint32_t& row,
                                             uint32_t& unit_in_row, uint32_t& step0, uint32_t& nst, float (&y)[SPU][8],
                                             uint32_t (&mbits)[SPU])
 {
@@ -295,9 +346,9 @@ __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, ui
     }
 }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, class CNT>
 __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
-                                             float limit, float a_limit, unsigned long long& clamped)
+                                             float limit, float a_limit, CNT& clamped)
 {
     float y[SPU][8];
     uint32_t mbits[SPU];
@@ -313,9 +364,11 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
 // The persistent loop for row-reduced units of kStreamMinSteps steps or more:
 // the table first, then every unit of the wave streamed (stream_unit).
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool PARTIAL>
-__device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut, uint32_t lane, uint32_t wave,
-                                                     uint32_t nwaves)
+__device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut, unsigned long long* wg_clamped,
+                                                     uint32_t lane, uint32_t wave, uint32_t nwaves)
 {
+    if (CLAMP && threadIdx.x == 0)
+        *wg_clamped = 0;
     load_lut_to_lds(lut);
     float limit = 0.0f, a_limit = 0.0f;
     if constexpr (CLAMP) {
@@ -323,7 +376,7 @@ __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut,
         a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                                __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
     }
-    unsigned long long clamped = 0;
+    WaveCount clamped;
     for (uint32_t u = wave; u < p.units; u += nwaves) {
         float y[SPU][8];
         uint32_t mbits[SPU];
@@ -332,16 +385,15 @@ __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut,
                                          mbits);
         quantize_unit<FMT, SFMT, SPU, true, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mbits);
     }
-    if constexpr (CLAMP) {
-        if (p.count && lane == 0 && clamped)
-            atomicAdd(p.count, clamped);
-    }
+    if constexpr (CLAMP)
+        flush_clamp_count(p.count, wg_clamped, clamped, lane);
 }
 
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
     LutT* lut = reinterpret_cast<LutT*>(lut_raw);
 
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
@@ -359,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(block * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
     if constexpr (ROWRED && SPU >= kStreamMinSteps) {
-        streamed_rowred_loop<FMT, SFMT, CLAMP, SPU, PARTIAL>(p, lut, lane, wave, nwaves);
+        streamed_rowred_loop<FMT, SFMT, CLAMP, SPU, PARTIAL>(p, lut, &wg_clamped, lane, wave, nwaves);
         return;
     }
 
@@ -373,6 +425,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 #pragma unroll
     for (int i = 0; i < kLutPerThread; ++i)
         lut_part[i] = reinterpret_cast<const uint4*>(g_sigma_lut)[i * kThreads + threadIdx.x];
+    if (CLAMP && threadIdx.x == 0)
+        wg_clamped = 0;
     Unit<SPU> first;
     if (wave < p.units)
         load_unit<SPU, ROWRED, PARTIAL>(p, wave, lane, first);
@@ -387,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
         a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                                __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
     }
-    unsigned long long clamped = 0;
+    std::conditional_t<ROWRED, WaveCount, LaneCount> clamped;
 
     if (wave < p.units)
         process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, first, limit, a_limit, clamped);
@@ -397,10 +451,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
         process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, d, limit, a_limit, clamped);
     }
 
-    if constexpr (CLAMP) {
-        if (p.count && lane == 0 && clamped)
-            atomicAdd(p.count, clamped);
-    }
+    if constexpr (CLAMP)
+        flush_clamp_count(p.count, &wg_clamped, clamped, lane);
 }
 
 // Row-reduced groups longer than one wave holds (per-token rows or 512k-column
@@ -418,7 +470,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
     static_assert(kWaves % W == 0, "waves per group must divide the workgroup");
     __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
     __shared__ uint32_t part_max[2][kWaves];
+    __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
     LutT* lut = reinterpret_cast<LutT*>(lut_raw);
+    if (CLAMP && threadIdx.x == 0)
+        wg_clamped = 0;
     load_lut_to_lds(lut);
 
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
@@ -436,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
         a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                                __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
     }
-    unsigned long long clamped = 0;
+    WaveCount clamped;
     uint32_t parity = 0;
     for (uint32_t it = block; it < passes; it += gridDim.x, parity ^= 1u) {
         const uint32_t g = it * kGroupsPerPass + slot_in_pass;
@@ -460,10 +515,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
             quantize_rowred<FMT, SFMT, SPU, PARTIAL>(p, lane, row, unit_in_row / W, step0, nst, y, gm,
                                                      part == 0 && lane == 0);
     }
-    if constexpr (CLAMP) {
-        if (p.count && lane == 0 && clamped)
-            atomicAdd(p.count, clamped);
-    }
+    if constexpr (CLAMP)
+        flush_clamp_count(p.count, &wg_clamped, clamped, lane);
 }
 
 // The unfused first stage (swiglu_forward): fp32 y [n][hidden], same
@@ -477,14 +530,17 @@ __global__ __launch_bounds__(kThreads) void swiglu_forward_kernel(const uint4* _
                                                                   unsigned long long* count)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
     LutT* lut = reinterpret_cast<LutT*>(lut_raw);
+    if (CLAMP && threadIdx.x == 0)
+        wg_clamped = 0;
     load_lut_to_lds(lut);
     float limit = 0.0f, a_limit = 0.0f;
     if constexpr (CLAMP) {
         limit = limit_in;
         a_limit = limit * sigmoid_rn(limit);
     }
-    unsigned long long clamped = 0;
+    WaveCount clamped;
     const uint64_t total = (uint64_t)n * slots;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     // every lane runs the same trip count so that the clamp ballots see whole waves
@@ -515,10 +571,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_forward_kernel(const uint4* _
             y[2 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
         }
     }
-    if constexpr (CLAMP) {
-        if (count && (threadIdx.x & (kWaveSize - 1)) == 0 && clamped)
-            atomicAdd(count, clamped);
-    }
+    if constexpr (CLAMP)
+        flush_clamp_count(count, &wg_clamped, clamped, threadIdx.x & (kWaveSize - 1));
 }
 
 // ---------------------------------------------------------------------------
