@@ -325,3 +325,27 @@ def test_side_stream():
     with torch.cuda.stream(s):
         got = run_cast(x, wt, w.hidden, w.group_size, None, 4, 1, stream=s)
     assert_same(got, oracle_cast(x, wt, w), "side stream")
+
+
+@pytest.mark.parametrize("limit", [2.0 ** -149, 2.0 ** -148, 1e-30, 0.5, 10.0], ids=str)
+def test_clamp_limits_and_signed_zero_gates(limit):
+    """The clamped gate's activation for every kind of gate: +-0, the smallest
+    bf16 magnitudes, values at and around the limit, large values.  At the
+    smallest limit (2^-149) the limit's own activation rounds to +0, and a -0
+    gate must keep its -0; row-reduced and per-block units, both formats."""
+    say("clamp limit", limit)
+    hidden = 1024
+    gates = np.array([0.0, -0.0, 2.0 ** -133, -(2.0 ** -133), 2.0 ** -126, 1e-30, limit, -limit, 0.25, 0.5, 0.75,
+                      10.0, 10.0625, -10.0, 3.0e38, -3.0e38], dtype=np.float32)
+    rng = np.random.default_rng(7)
+    rows = 24
+    g = rng.choice(gates, size=(rows, hidden)).astype(np.float32)
+    u = rng.choice(np.array([0.0, -0.0, 1.0, -2.0, 1e-20, 3.0e5], dtype=np.float32), size=(rows, hidden))
+    f = np.concatenate([g, u], axis=1)
+    b = f.view(np.uint32).astype(np.uint64)
+    x = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)  # bf16, nearest even
+    wt = rng.uniform(0.0, 1.0, rows).astype(np.float32)
+    for fmt, group, sfmt in [(8, 0, tk.TK_SCALE_FP32), (8, 128, tk.TK_SCALE_UE8M0), (4, 32, tk.TK_SCALE_UE8M0),
+                             (4, 0, tk.TK_SCALE_FP32)]:
+        got = run_cast(x, wt, hidden, group, limit, fmt, sfmt)
+        assert_same(got, oracle.swiglu_cast(x, wt, group, limit, fmt, sfmt), f"limit {limit} fmt {fmt} group {group}")
