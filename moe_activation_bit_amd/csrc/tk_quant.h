@@ -75,6 +75,28 @@ __device__ __forceinline__ uint32_t group_umax(uint32_t v, uint32_t gl_log2)
     return v;
 }
 
+// The same for the N steps of a unit at once: one uniform branch per level
+// serves all N steps, whose lane exchanges then overlap.  Used for groups of
+// 32 or 64 lanes, whose ds_bpermute levels each wait for LDS (E2M1, 256
+// columns, fp32 scales: 56.2 -> 53.0 us at 32768 x 2048); for groups of up to
+// 16 lanes (DPP only) the step-by-step order above is faster, because a step's
+// codes can leave before the next step's maximum is known.
+template <int N>
+__device__ __forceinline__ void group_umax_steps(uint32_t (&v)[N], uint32_t gl_log2)
+{
+#define TK_LEVEL(COND, EXPR)                 \
+    if (COND) {                              \
+        _Pragma("unroll") for (int s = 0; s < N; ++s) v[s] = EXPR; \
+    }
+    TK_LEVEL(gl_log2 >= 1, dpp_umax<0xB1>(v[s]))  // quad_perm [1,0,3,2]: lane ^ 1
+    TK_LEVEL(gl_log2 >= 2, dpp_umax<0x4E>(v[s]))  // quad_perm [2,3,0,1]: lane ^ 2
+    TK_LEVEL(gl_log2 >= 3, dpp_umax<0x141>(v[s])) // row_half_mirror: quads of 8 lanes
+    TK_LEVEL(gl_log2 >= 4, dpp_umax<0x140>(v[s])) // row_mirror: halves of 16 lanes
+    TK_LEVEL(gl_log2 >= 5, max(v[s], (uint32_t)__shfl_xor((int)v[s], 16)))
+    TK_LEVEL(gl_log2 >= 6, max(v[s], (uint32_t)__shfl_xor((int)v[s], 32)))
+#undef TK_LEVEL
+}
+
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v)
 {
     v = dpp_umax<0xB1>(v);
@@ -216,7 +238,9 @@ __device__ __forceinline__ void quantize_rowred(const Params& p, uint32_t lane, 
 // scales.  Per-block mode (ROWRED false): groups are 2^gl_log2 lanes of one
 // step; row mode: the whole unit is one group (per-token, or a 512k-column
 // group).
-template <int FMT, int SFMT, int SPU, bool ROWRED, bool PARTIAL>
+// WIDE: per-block groups of 32 or 64 lanes (p.gl_log2 >= 5), compiled apart
+// so that the other kernels keep their code as it is.
+template <int FMT, int SFMT, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false>
 __device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, uint32_t row, uint32_t unit_in_row,
                                               uint32_t step0, uint32_t nst, const float (&y)[SPU][8],
                                               const uint32_t (&mbits)[SPU])
@@ -226,9 +250,7 @@ __device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, ui
         const uint32_t mb = wave_umax(lane_max<SPU>(mbits, nst));
         quantize_rowred<FMT, SFMT, SPU, PARTIAL>(p, lane, row, unit_in_row, step0, nst, y, mb, lane == 0);
     } else {
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-            const uint32_t mb = group_umax(mbits[s], p.gl_log2);
+        auto finish = [&](int s, uint32_t mb) { // scale, codes and the group's scale of step s
             float s32 = 0.0f;
             uint32_t s8 = 0;
             const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
@@ -238,6 +260,20 @@ __device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, ui
                 if ((lane & ((1u << p.gl_log2) - 1u)) == 0)
                     store_scale<SFMT>(p, row, slot >> p.gl_log2, s32, s8);
             }
+        };
+        if constexpr (WIDE) {
+            uint32_t gmax[SPU];
+#pragma unroll
+            for (int s = 0; s < SPU; ++s)
+                gmax[s] = mbits[s];
+            group_umax_steps<SPU>(gmax, p.gl_log2);
+#pragma unroll
+            for (int s = 0; s < SPU; ++s)
+                finish(s, gmax[s]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < SPU; ++s)
+                finish(s, group_umax(mbits[s], p.gl_log2));
         }
     }
 }

@@ -346,7 +346,7 @@ __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, ui
     }
 }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, class CNT>
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE, class CNT>
 __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
                                              float limit, float a_limit, CNT& clamped)
 {
@@ -358,7 +358,7 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
             mbits[s] = compute_step<CLAMP, PARTIAL>(lut, d.g[s], d.u[s], d.w,
                                                     !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots, limit,
                                                     a_limit, clamped, y[s]);
-    quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
+    quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL, WIDE>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
 }
 
 // The persistent loop for row-reduced units of kStreamMinSteps steps or more:
@@ -389,7 +389,7 @@ __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut,
         flush_clamp_count(p.count, wg_clamped, clamped, lane);
 }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false>
 __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
@@ -444,11 +444,11 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     std::conditional_t<ROWRED, WaveCount, LaneCount> clamped;
 
     if (wave < p.units)
-        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, first, limit, a_limit, clamped);
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE>(p, lut, lane, first, limit, a_limit, clamped);
     for (uint32_t u = wave + nwaves; u < p.units; u += nwaves) {
         Unit<SPU> d;
         load_unit<SPU, ROWRED, PARTIAL>(p, u, lane, d);
-        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>(p, lut, lane, d, limit, a_limit, clamped);
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE>(p, lut, lane, d, limit, a_limit, clamped);
     }
 
     if constexpr (CLAMP)
@@ -622,6 +622,13 @@ tk_status ensure_device(int& dev);
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 void launch_one(const Params& p, int blocks, hipStream_t stream)
 {
+    if constexpr (!ROWRED) {
+        if (p.gl_log2 >= 5) { // per-block groups of 32 or 64 lanes
+            hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true>), dim3(blocks),
+                               dim3(kThreads), 0, stream, p);
+            return;
+        }
+    }
     hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL>), dim3(blocks), dim3(kThreads),
                        0, stream, p);
 }
