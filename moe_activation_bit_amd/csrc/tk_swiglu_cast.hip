@@ -171,6 +171,9 @@ struct WaveCount {
     __device__ __forceinline__ unsigned long long total() const { return n; }
 };
 struct LaneCount {
+    // a lane counts at most 32 gates per unit and ceil(units / waves) units,
+    // with units < 2^31 and 8 waves per CU: below 2^32 on any device of more
+    // than two CUs
     uint32_t n = 0;
     __device__ __forceinline__ void add(bool hit) { n += hit ? 1u : 0u; }
     // every lane of the wave must call this
