@@ -349,3 +349,42 @@ def test_clamp_limits_and_signed_zero_gates(limit):
                              (4, 0, tk.TK_SCALE_FP32)]:
         got = run_cast(x, wt, hidden, group, limit, fmt, sfmt)
         assert_same(got, oracle.swiglu_cast(x, wt, group, limit, fmt, sfmt), f"limit {limit} fmt {fmt} group {group}")
+
+
+def test_concurrent_clamp_counts_on_streams():
+    """Clamped launches in flight together on four streams: each counter gets
+    exactly its launches' gates above the limit (two launches share one
+    counter and must add up), per-token and per-block units alike."""
+    w = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    say("concurrent clamp counts")
+    jobs = []  # (rows, group, scale fmt, counter slot)
+    for j, (group, sfmt, slot) in enumerate([(0, 0, 0), (128, 1, 1), (32, 1, 2), (0, 0, 3), (128, 1, 4), (0, 0, 4)]):
+        rows = range(j * 3001, j * 3001 + 2500 + 97 * j)
+        jobs.append((wl.make_x(w, 3, rows=rows), wl.make_w(w, 3)[list(rows)], group, sfmt, slot))
+    counts = torch.zeros(8, dtype=torch.int64, device=DEV)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    bufs = []
+    for x, wt, group, sfmt, slot in jobs:
+        n = x.shape[0]
+        xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+        wd = torch.from_numpy(wt).to(DEV)
+        codes = torch.empty((n, w.hidden), dtype=torch.uint8, device=DEV)
+        scales = torch.empty((n, w.hidden // (group or w.hidden)), dtype=torch.float32 if sfmt == 0 else torch.uint8,
+                             device=DEV)
+        bufs.append((xd, wd, codes, scales))
+    torch.cuda.synchronize()
+    for j, ((x, wt, group, sfmt, slot), (xd, wd, codes, scales)) in enumerate(zip(jobs, bufs)):
+        s = streams[j % 4]
+        rc = tk.tk_swiglu_cast_fp8(xd, wd, x.shape[0], w.hidden, group, 10.0, sfmt, codes, scales,
+                                   counts.data_ptr() + 8 * slot, s)
+        assert rc == OK, tk.tk_status_str(rc)
+    torch.cuda.synchronize()
+    want_counts = [0] * 8
+    for (x, wt, group, sfmt, slot), (_, _, codes, scales) in zip(jobs, bufs):
+        wc, ws, wk = oracle.swiglu_cast(x, wt, group, 10.0, 8, sfmt)
+        assert np.array_equal(codes.cpu().numpy(), wc), f"codes group {group}"
+        assert np.array_equal(scales.cpu().numpy().view(np.uint8), ws.view(np.uint8)), f"scales group {group}"
+        want_counts[slot] += wk
+    got = counts.cpu().numpy().tolist()
+    assert got == want_counts, (got, want_counts)
+    assert min(want_counts[:5]) > 0
