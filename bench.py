@@ -43,13 +43,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 
-# Each timed kernel: the sources its counters depend on, and how its name
-# reads in a rocprofv3 trace.
+# Each timed kernel: the sources its counters depend on, how its name reads
+# in a rocprofv3 trace, and the name the bench line gives it.
 KERNELS = {
-    "fused": (("tk_swiglu_cast.hip", "tk_quant.h"), r"\bswiglu_cast_kernel<"),
-    "cast": (("tk_cast.hip", "tk_quant.h"), r"\bcast_kernel<"),
-    "reduce": (("tk_reduce.hip",), r"\bmoe_reduce_kernel<"),
-    "topk": (("tk_topk.hip",), r"\btopk_kernel<"),
+    "fused": (("tk_swiglu_cast.hip", "tk_quant.h"), r"\bswiglu_cast_kernel<", "swiglu_cast_kernel"),
+    "cast": (("tk_cast.hip", "tk_quant.h"), r"\bcast_kernel<", "cast_kernel"),
+    "reduce": (("tk_reduce.hip",), r"\bmoe_reduce_kernel<", "moe_reduce_kernel"),
+    # (topk_pair_kernel serves up to 256 experts, the gating workload's case)
+    "topk": (("tk_topk.hip",), r"\btopk_(?:pair_)?kernel<", "topk_pair_kernel"),
 }
 
 
@@ -530,7 +531,7 @@ def bench_aux(args, torch, np, tk, wl):
     if args.copy_calibration:
         copy_calibration(torch, dev)
     name, nbytes, step, metric, config, rows = aux_setup(args.kernel, torch, np, tk, wl, args.seed, sets, dev, sh)
-    kernel = KERNELS[args.kernel][1].replace("\\b", "").rstrip("<")
+    kernel = KERNELS[args.kernel][2]
     wall, gpu = _timed(torch, stream, step, args.steps, args.warmup)
     avg = gpu / args.steps
     achieved = nbytes / avg / 1e9
@@ -666,7 +667,7 @@ def run_suite(args, torch, np, tk, wl):
             # launch issue; the launches replayed from one HIP graph measure the GPU
             avg = graph_replay(torch, step, args.steps, nbytes)["us_per_launch"] / 1e6
             timing = "graph"
-        rec = {"key": case_key(kernel, params), "kernel": KERNELS[kernel][1].replace("\\b", "").rstrip("<"),
+        rec = {"key": case_key(kernel, params), "kernel": KERNELS[kernel][2],
                "operation": "fwd", "params": params, "time_us": round(avg * 1e6, 3), "timing": timing,
                "bandwidth_gbs": round(nbytes / avg / 1e9, 1), "frac_of_peak": round(nbytes / avg / 1e9 / HBM_PEAK_GBS, 4),
                "regime": reg}

@@ -9,28 +9,34 @@
 // equal sums going to the smaller group index; then pick the best, label it,
 // pick the next).
 //
-// gfx950 design: one 64-lane wave per token (the pages use a 32-lane warp);
-// lane l holds experts l*C .. l*C+C-1 (C = ceil(experts/64) <= 8), so a group
-// of experts is a block of consecutive lanes and lane order is index order.
+// gfx950 design (the pages use a 32-lane warp per token).  Up to 256 experts
+// and k <= 32 (topk_pair_kernel): one 64-lane wave serves two tokens, lanes
+// 0-31 the first and 32-63 the second, lane l holding experts
+// (l & 31)*C .. +C-1 of its token (C = ceil(experts/32) <= 8).  Otherwise
+// (topk_kernel): one wave per token, lane l holding experts l*C .. l*C+C-1
+// (C = ceil(experts/64) <= 8).  Either way a group of experts is a block of
+// consecutive lanes and lane order is index order.
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
 //      quad_perm / half-row and row mirrors, lane shuffles past 16 lanes);
 //      a NaN group sum (+inf and -inf) counts as -inf.  Group ranks: with at
 //      most 8 groups, lane 8h + h' compares group h' with group h and one
-//      ballot holds every pair (group h's rank = set bits in byte h); with
-//      more, wave-uniform reads of every group sum.  Lanes of dropped groups
-//      empty their lists.
+//      ballot per token holds every pair (group h's rank = set bits in byte
+//      h); with more, wave-uniform reads of every group sum.  Lanes of
+//      dropped groups empty their lists.
 //   3. k rounds of a tournament between the lanes' list heads: a DPP max of
 //      the head keys (quad_perm, row_half_mirror, row_mirror, then row
-//      broadcasts into lane 63 and one v_readlane), the first lane whose head
-//      equals it (ballot + s_ff1: the smallest index among equal scores), the
-//      winner's expert index from its packed slot list (one v_readlane and
-//      scalar arithmetic), and the winner pops its head (its keys shift, its
-//      slot list shifts by 3 bits); lane `round` keeps the pick's index.
+//      broadcasts; v_readlane of the lane that ends with the maximum), the
+//      first lane whose head equals it (ballot + s_ff1: the smallest index
+//      among equal scores), the winner's expert index from its packed slot
+//      list (one v_readlane and scalar arithmetic), and the winner pops its
+//      head (its keys shift, its slot list shifts by 3 bits); lane `round`
+//      keeps the pick's index.  In the two-token layout every one of these
+//      wave-wide instructions serves both tokens.
 //      Output lane j then re-reads pick j's own score, and the
 //      normalising sum adds those k values in pick order after the rounds.
-// Each round is about three dozen VALU/SALU instructions with no LDS traffic.
+// No LDS traffic beyond the two lane shuffles of the group rank.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -236,6 +242,196 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     }
 }
 
+// Two tokens per wave, for up to 256 experts and k <= 32: lanes 0-31 serve
+// token 2w and lanes 32-63 token 2w+1, lane l holding experts
+// (l & 31)*C .. +C-1 of its token (C = ceil(experts/32)).  The steps are those
+// of topk_kernel, each wave-wide instruction of a round now serving both
+// tokens; the price is a longer per-lane sort (8 keys at 256 experts).
+
+// maximum over each 16-lane row, then row 0's into row 1 and row 2's into
+// row 3: lane 31 ends with the low half's maximum, lane 63 with the high half's
+__device__ __forceinline__ uint32_t half_umax_at_ends(uint32_t v)
+{
+    v = dpp_umax<0xB1>(v);  // quad_perm [1,0,3,2]
+    v = dpp_umax<0x4E>(v);  // quad_perm [2,3,0,1]
+    v = dpp_umax<0x141>(v); // row_half_mirror
+    v = dpp_umax<0x140>(v); // row_mirror
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
+}
+
+template <int C, bool FULL>
+__global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, uint32_t n_group,
+                                                             uint32_t topk_group, uint32_t gl_log2, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t t0 = 2u * __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
+    if (t0 >= tokens)
+        return;
+    const bool hi = lane >= 32u;
+    const uint32_t hl = lane & 31u;
+    const uint32_t t = t0 + (hi ? 1u : 0u);
+    // a wave past an odd last token repeats that token in its high half and stores nothing from it
+    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
+
+    // ---- 1. this lane's candidates, sorted best first.  The slot of entry j
+    // is kept as 7 - j, so that as a low word beside the key it breaks ties
+    // toward the smaller index.
+    // (FULL: experts == 32*C, every slot holds an expert)
+    uint32_t key[C], idx[C];
+    float v[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        v[j] = FULL ? s_row[hl * C + j] : s_row[min(hl * C + j, experts - 1u)];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        key[j] = (FULL || hl * C + j < experts) ? ordered(v[j]) : 0u;
+    if constexpr (C == 8) {
+        // 19-comparator network on (key, 7 - slot): every pair of entries is
+        // strictly ordered, so the network's lack of stability does not matter
+        uint64_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = ((uint64_t)key[j] << 32) | (uint32_t)(7 - j);
+        constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                                    {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+        for (int c = 0; c < 19; ++c) {
+            // one 64-bit compare drives both selects (the round trip through
+            // a lane mask keeps them from being rebuilt as a max and a min)
+            const uint64_t a = x[net[c][0]], b = x[net[c][1]];
+            const bool swap = __builtin_amdgcn_inverse_ballot_w64(__builtin_amdgcn_ballot_w64(b > a));
+            x[net[c][0]] = swap ? b : a;
+            x[net[c][1]] = swap ? a : b;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            key[j] = (uint32_t)(x[j] >> 32);
+            idx[j] = (uint32_t)x[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            idx[j] = (uint32_t)(7 - j);
+        // stable insertion by strict comparison (slots start in index order)
+#pragma unroll
+        for (int i = 1; i < C; ++i) {
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                const bool swap = key[j] > key[j - 1];
+                const uint32_t k0 = key[j - 1], i0 = idx[j - 1];
+                key[j - 1] = swap ? key[j] : k0;
+                idx[j - 1] = swap ? idx[j] : i0;
+                key[j] = swap ? k0 : key[j];
+                idx[j] = swap ? i0 : idx[j];
+            }
+        }
+    }
+
+    // ---- 2. group selection, per half (a group is 2^gl_log2 <= 32 lanes)
+    if (n_group > 1) {
+        uint32_t a1 = key[0], a2 = C > 1 ? key[C > 1 ? 1 : 0] : 0u;
+        if (gl_log2 >= 1)
+            merge_top2<0xB1>(a1, a2);
+        if (gl_log2 >= 2)
+            merge_top2<0x4E>(a1, a2);
+        if (gl_log2 >= 3)
+            merge_top2<0x141>(a1, a2);
+        if (gl_log2 >= 4)
+            merge_top2<0x140>(a1, a2);
+        if (gl_log2 >= 5)
+            merge_top2_from(a1, a2, (uint32_t)__shfl_xor((int)a1, 16), (uint32_t)__shfl_xor((int)a2, 16));
+        float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
+        if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf
+            gsum = -INFINITY;
+        const uint32_t my_g = hl >> gl_log2;
+        uint32_t rank = 0;
+        if (n_group <= 8) {
+            // one ballot per token: lane 8h + h' compares that token's group
+            // h' against its group h; group h's rank is the count of set bits
+            // in byte h
+            const uint32_t h = lane >> 3, h2 = lane & 7u;
+            const uint32_t in = (uint32_t)(max(h, h2) < n_group);
+            const uint32_t lt = (uint32_t)(h2 < h);
+            uint64_t m[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const uint32_t base = 32u * p;
+                const float g_h = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                    (int)((base + (min(h, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
+                const float g_h2 = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                    (int)((base + (min(h2, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
+                const uint32_t b = in & ((uint32_t)(g_h2 > g_h) | ((uint32_t)(g_h2 == g_h) & lt));
+                m[p] = __builtin_amdgcn_ballot_w64(b != 0u);
+            }
+            rank = (uint32_t)__builtin_popcountll(((hi ? m[1] : m[0]) >> (8u * my_g)) & 0xFFull);
+        } else {
+            for (uint32_t hh = 0; hh < n_group; ++hh) {
+                const float g0 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), hh << gl_log2));
+                const float g1 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), 32u + (hh << gl_log2)));
+                rank += beats(hi ? g1 : g0, hh, gsum, my_g) ? 1u : 0u;
+            }
+        }
+        if (rank >= topk_group) {
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                key[j] = 0u;
+        }
+    }
+
+    // ---- 3. k rounds, both tokens at once; pick it goes to lane it of its half
+    uint32_t slots = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        slots |= idx[j] << (3 * j);
+    int32_t my_idx = 0;
+    // Lane masks are built as scalars and turned into per-lane conditions by
+    // inverse ballots, so the round's lane selections cost no vector compares.
+    // Rounds are taken in pairs (the loop cannot be unrolled by the compiler
+    // across its cross-lane operations): the pop then compiles to masked moves
+    // in place rather than selects plus a register rotation per round.
+    auto round = [&](uint32_t it) {
+        const uint32_t m = half_umax_at_ends(key[0]);
+        const uint32_t b0 = __builtin_amdgcn_readlane(m, 31), b1 = __builtin_amdgcn_readlane(m, 63);
+        const uint32_t h0 = (uint32_t)__builtin_amdgcn_ballot_w64(key[0] == b0);
+        const uint32_t h1 = (uint32_t)(__builtin_amdgcn_ballot_w64(key[0] == b1) >> 32);
+        // each half's maximum is held by one of its lanes, so neither h0 nor h1 is 0
+        const uint32_t o0 = (uint32_t)__builtin_ctz(h0), o1 = (uint32_t)__builtin_ctz(h1);
+        const uint32_t e0 = o0 * C + 7u - (__builtin_amdgcn_readlane(slots, o0) & 7u);
+        const uint32_t e1 = o1 * C + 7u - (__builtin_amdgcn_readlane(slots, 32u + o1) & 7u);
+        if (__builtin_amdgcn_inverse_ballot_w64((uint64_t)(h0 & (0u - h0)) | ((uint64_t)(h1 & (0u - h1)) << 32))) {
+#pragma unroll
+            for (int j = 0; j + 1 < C; ++j)
+                key[j] = key[j + 1];
+            key[C - 1] = 0u;
+            slots >>= 3;
+        }
+        my_idx = __builtin_amdgcn_inverse_ballot_w64(1ull << it) ? (int32_t)e0 : my_idx;
+        my_idx = __builtin_amdgcn_inverse_ballot_w64(1ull << (32u + it)) ? (int32_t)e1 : my_idx;
+    };
+    uint32_t it = 0;
+    for (; it + 1 < k; it += 2) {
+        round(it);
+        round(it + 1);
+    }
+    if (it < k)
+        round(it);
+    const float my_w = hl < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
+    float sum0 = 0.0f, sum1 = 0.0f;
+    if (normalise) {
+        for (uint32_t it = 0; it < k; ++it) {
+            sum0 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), it));
+            sum1 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), 32u + it));
+        }
+    }
+    const float sum = hi ? sum1 : sum0;
+    if (hl < k && t < tokens) {
+        idx_out[(size_t)t * k + hl] = my_idx;
+        w_out[(size_t)t * k + hl] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
+    }
+}
+
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
 {
     if (!a || !b || an == 0 || bn == 0)
@@ -280,8 +476,39 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
     }
     if (tokens == 0)
         return TK_OK;
-    const uint32_t blocks = (uint32_t)((tokens + kThreads / kWave - 1) / (kThreads / kWave));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (experts <= 8 * (kWave / 2) && k <= kWave / 2) {
+        // the two-tokens-per-wave layout, where its groups are whole lanes too
+        const uint32_t C2 = (uint32_t)((experts + kWave / 2 - 1) / (kWave / 2));
+        const uint32_t lanes2 = n_group > 1 ? (uint32_t)(per / C2) : 1u;
+        if (n_group == 1 || (per % C2 == 0 && (lanes2 & (lanes2 - 1)) == 0)) {
+            const uint32_t gl2 = n_group > 1 ? (uint32_t)__builtin_ctz(lanes2) : 0u;
+            const uint32_t tpb = 2 * (kThreads / kWave);
+            const uint32_t pblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+#define TK_TOPK2(CC)                                                                                          \
+    if (experts == 32 * (CC))                                                                                 \
+        hipLaunchKernelGGL((topk_pair_kernel<CC, true>), dim3(pblocks), dim3(kThreads), 0, s, scores,         \
+                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,                \
+                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight);                       \
+    else                                                                                                      \
+        hipLaunchKernelGGL((topk_pair_kernel<CC, false>), dim3(pblocks), dim3(kThreads), 0, s, scores,        \
+                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,                \
+                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight)
+            switch (C2) {
+            case 1: TK_TOPK2(1); break;
+            case 2: TK_TOPK2(2); break;
+            case 3: TK_TOPK2(3); break;
+            case 4: TK_TOPK2(4); break;
+            case 5: TK_TOPK2(5); break;
+            case 6: TK_TOPK2(6); break;
+            case 7: TK_TOPK2(7); break;
+            default: TK_TOPK2(8); break;
+            }
+#undef TK_TOPK2
+            return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+        }
+    }
+    const uint32_t blocks = (uint32_t)((tokens + kThreads / kWave - 1) / (kThreads / kWave));
 #define TK_TOPK(CC)                                                                                           \
     hipLaunchKernelGGL(topk_kernel<CC>, dim3(blocks), dim3(kThreads), 0, s, scores, (uint32_t)tokens,         \
                        (uint32_t)experts, (uint32_t)k, (uint32_t)n_group, (uint32_t)topk_group, gl_log2, normalise, \

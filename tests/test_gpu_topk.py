@@ -34,6 +34,9 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     (512, 64, 1, 1), (500, 7, 1, 1),
     # group counts the all-pairs group rank covers: 2 groups of 32 lanes, 3, 6 (not a power of two), all kept
     (256, 3, 2, 1), (96, 5, 3, 2), (48, 4, 6, 3), (256, 8, 8, 8),
+    # two tokens per wave up to k = 32, one token per wave above; 7 experts in every lane of the
+    # two-token layout, whose lanes cannot hold 32-expert groups whole (the one-token kernel serves it)
+    (256, 32, 1, 1), (256, 33, 1, 1), (224, 8, 1, 1), (224, 8, 7, 3),
 ]
 
 
