@@ -259,7 +259,7 @@ __device__ __forceinline__ uint32_t half_umax_at_ends(uint32_t v)
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
 }
 
-template <int C, bool FULL>
+template <int C, bool FULL, bool K8>
 __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __restrict__ scores, uint32_t tokens,
                                                              uint32_t experts, uint32_t k, uint32_t n_group,
                                                              uint32_t topk_group, uint32_t gl_log2, int normalise,
@@ -391,7 +391,10 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
     // Rounds are taken in pairs (the loop cannot be unrolled by the compiler
     // across its cross-lane operations): the pop then compiles to masked moves
     // in place rather than selects plus a register rotation per round.
-    auto round = [&](uint32_t it) {
+    // depth: the picks left including this one (a lane popped now can be
+    // popped at most depth - 1 more times, so only its first depth - 1
+    // entries are read again)
+    auto round = [&](uint32_t it, uint32_t depth) {
         const uint32_t m = half_umax_at_ends(key[0]);
         const uint32_t b0 = __builtin_amdgcn_readlane(m, 31), b1 = __builtin_amdgcn_readlane(m, 63);
         const uint32_t h0 = (uint32_t)__builtin_amdgcn_ballot_w64(key[0] == b0);
@@ -403,26 +406,47 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
         if (__builtin_amdgcn_inverse_ballot_w64((uint64_t)(h0 & (0u - h0)) | ((uint64_t)(h1 & (0u - h1)) << 32))) {
 #pragma unroll
             for (int j = 0; j + 1 < C; ++j)
-                key[j] = key[j + 1];
-            key[C - 1] = 0u;
+                if (j + 1u < depth)
+                    key[j] = key[j + 1];
+            if (depth > (uint32_t)C)
+                key[C - 1] = 0u;
             slots >>= 3;
         }
         my_idx = __builtin_amdgcn_inverse_ballot_w64(1ull << it) ? (int32_t)e0 : my_idx;
         my_idx = __builtin_amdgcn_inverse_ballot_w64(1ull << (32u + it)) ? (int32_t)e1 : my_idx;
     };
-    uint32_t it = 0;
-    for (; it + 1 < k; it += 2) {
-        round(it);
-        round(it + 1);
+    if constexpr (K8) {
+        // k == 8, straight-line rounds: each pop shifts only what later rounds read
+#pragma unroll
+        for (uint32_t it = 0; it < 8; ++it)
+            round(it, 8u - it);
+    } else {
+        uint32_t it = 0;
+        for (; it + 1 < k; it += 2) {
+            round(it, 64u);
+            round(it + 1, 64u);
+        }
+        if (it < k)
+            round(it, 64u);
     }
-    if (it < k)
-        round(it);
     const float my_w = hl < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
     float sum0 = 0.0f, sum1 = 0.0f;
     if (normalise) {
-        for (uint32_t it = 0; it < k; ++it) {
-            sum0 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), it));
-            sum1 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), 32u + it));
+        if (k <= 16) {
+            // running sum in pick order inside each half's first 16-lane row:
+            // after step m lane i holds ((w[i-m+1] + ...) + w[i]) added oldest
+            // first (row_shr:1 reads 0 into a row's first lane), so lane k-1
+            // of each half ends with 0 + w[0] + w[1] + ... + w[k-1] in that order
+            float run = 0.0f;
+            for (uint32_t it = 0; it < k; ++it)
+                run = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(run), 0x111, 0xF, 0xF, true)) + my_w;
+            sum0 = ffrom(__builtin_amdgcn_readlane(fbits(run), k - 1u));
+            sum1 = ffrom(__builtin_amdgcn_readlane(fbits(run), 31u + k));
+        } else {
+            for (uint32_t it = 0; it < k; ++it) {
+                sum0 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), it));
+                sum1 += ffrom(__builtin_amdgcn_readlane(fbits(my_w), 32u + it));
+            }
         }
     }
     const float sum = hi ? sum1 : sum0;
@@ -485,15 +509,22 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
             const uint32_t gl2 = n_group > 1 ? (uint32_t)__builtin_ctz(lanes2) : 0u;
             const uint32_t tpb = 2 * (kThreads / kWave);
             const uint32_t pblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+#define TK_TOPK2_LAUNCH(CC, FULL, K8)                                                                         \
+    hipLaunchKernelGGL((topk_pair_kernel<CC, FULL, K8>), dim3(pblocks), dim3(kThreads), 0, s, scores,         \
+                       (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group, (uint32_t)topk_group, \
+                       gl2, normalise, topk_idx, topk_weight)
 #define TK_TOPK2(CC)                                                                                          \
-    if (experts == 32 * (CC))                                                                                 \
-        hipLaunchKernelGGL((topk_pair_kernel<CC, true>), dim3(pblocks), dim3(kThreads), 0, s, scores,         \
-                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,                \
-                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight);                       \
-    else                                                                                                      \
-        hipLaunchKernelGGL((topk_pair_kernel<CC, false>), dim3(pblocks), dim3(kThreads), 0, s, scores,        \
-                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,                \
-                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight)
+    if (experts == 32 * (CC)) {                                                                               \
+        if (k == 8)                                                                                           \
+            TK_TOPK2_LAUNCH(CC, true, true);                                                                  \
+        else                                                                                                  \
+            TK_TOPK2_LAUNCH(CC, true, false);                                                                 \
+    } else {                                                                                                  \
+        if (k == 8)                                                                                           \
+            TK_TOPK2_LAUNCH(CC, false, true);                                                                 \
+        else                                                                                                  \
+            TK_TOPK2_LAUNCH(CC, false, false);                                                                \
+    }
             switch (C2) {
             case 1: TK_TOPK2(1); break;
             case 2: TK_TOPK2(2); break;
@@ -505,6 +536,7 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
             default: TK_TOPK2(8); break;
             }
 #undef TK_TOPK2
+#undef TK_TOPK2_LAUNCH
             return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
         }
     }
