@@ -37,6 +37,8 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     # two tokens per wave up to k = 32, one token per wave above; 7 experts in every lane of the
     # two-token layout, whose lanes cannot hold 32-expert groups whole (the one-token kernel serves it)
     (256, 32, 1, 1), (256, 33, 1, 1), (224, 8, 1, 1), (224, 8, 7, 3),
+    # the normalising sum as a running sum within 16 lanes (k <= 16) and serially above
+    (256, 16, 1, 1), (256, 17, 1, 1), (128, 16, 4, 2),
 ]
 
 
