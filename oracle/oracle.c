@@ -258,34 +258,102 @@ int oracle_cast(const float* y, int64_t n, int64_t hidden, int64_t group_size, i
     return 0;
 }
 
-/* The fused form (Tutorial ch.2; Summary ch.2): one row at a time, the row's
- * fp32 values never leave this loop.  Same arguments as the two stages
- * combined. */
+/* UE8M0 exponent from the binary exponents and significands of amax and
+ * fmt_max (a closed form, independent of oracle_ue8m0_exponent's search):
+ * with amax = ma*2^ea and fmt_max = mf*2^ef, ma and mf in [0.5, 1), the
+ * smallest k with fmt_max*2^k >= amax is ea - ef, plus 1 when ma > mf;
+ * clamped to [-127, 127]; amax == 0 gives -127. */
+static int ue8m0_exponent_closed_form(float amax, float fmt_max)
+{
+    if (amax == 0.0f)
+        return -127;
+    int ea, ef;
+    const double ma = frexp((double)amax, &ea);
+    const double mf = frexp((double)fmt_max, &ef);
+    int k = ea - ef + (ma > mf ? 1 : 0);
+    if (k < -127)
+        k = -127;
+    if (k > 127)
+        k = 127;
+    return k;
+}
+
+/* The fused form (Tutorial ch.2 "算子融合的“三重境界”"; Summary ch.2): one row
+ * at a time and, within it, one column group at a time.  Each value of the
+ * group goes from the bf16 pair through the clamp, sigma and the three
+ * products into a buffer of one group, its magnitude into the running
+ * abs-max; then the group's scale, then its codes, written straight into the
+ * output row (FP4: element 2i into the low nibble of byte i, 2i+1 into the
+ * high nibble).  It calls neither stage function of the unfused form, so the
+ * two agree only if both follow the same statement of the step. */
 int oracle_swiglu_cast(const uint16_t* x, const float* w, int64_t n, int64_t hidden,
                        int64_t group_size, float clamp_limit, int fmt, int scale_fmt,
                        uint8_t* codes, void* scales, int64_t* clamped_count)
 {
     if (check_args(n, hidden, group_size, fmt, scale_fmt))
         return 1;
-    float* row_y = (float*)malloc((size_t)hidden * sizeof(float));
-    if (!row_y)
+    const int64_t G = group_size ? group_size : hidden;
+    const int64_t groups = hidden / G;
+    const float fmt_max = fmt == ORACLE_FP8 ? 448.0f : 6.0f;
+    float* vals = (float*)malloc((size_t)G * sizeof(float));
+    if (!vals)
         return 2;
-    const int64_t groups = hidden / (group_size ? group_size : hidden);
-    const int64_t code_bytes = fmt == ORACLE_FP8 ? hidden : hidden / 2;
-    const size_t scale_bytes = scale_fmt == ORACLE_SCALE_FP32 ? sizeof(float) : 1;
+    int64_t clamped = 0;
     for (int64_t r = 0; r < n; ++r) {
-        const float* wr = w ? w + r : NULL;
-        int rc = oracle_swiglu_forward(x + r * 2 * hidden, wr, 1, hidden, clamp_limit, row_y,
-                                       clamped_count);
-        if (rc == 0)
-            rc = oracle_cast(row_y, 1, hidden, group_size, fmt, scale_fmt, codes + r * code_bytes,
-                             (uint8_t*)scales + (size_t)(r * groups) * scale_bytes);
-        if (rc) {
-            free(row_y);
-            return rc;
+        const uint16_t* gate_row = x + r * 2 * hidden;
+        const uint16_t* up_row = gate_row + hidden;
+        uint8_t* out_row = codes + (fmt == ORACLE_FP8 ? r * hidden : r * (hidden / 2));
+        for (int64_t k = 0; k < groups; ++k) {
+            float group_amax = 0.0f;
+            for (int64_t j = 0; j < G; ++j) {
+                const int64_t col = k * G + j;
+                float gv = bf16_to_float(gate_row[col]);
+                float uv = bf16_to_float(up_row[col]);
+                if (clamp_limit < INFINITY) {
+                    if (gv > clamp_limit) {
+                        ++clamped;
+                        gv = clamp_limit;
+                    }
+                    if (uv < -clamp_limit)
+                        uv = -clamp_limit;
+                    else if (uv > clamp_limit)
+                        uv = clamp_limit;
+                }
+                const float act = gv * oracle_sigmoid(gv);
+                const float prod = act * uv;
+                const float v = w != NULL ? prod * w[r] : prod;
+                vals[j] = v;
+                const float mag = v < 0.0f ? -v : v;
+                if (mag > group_amax)
+                    group_amax = mag;
+            }
+            float mult;
+            if (scale_fmt == ORACLE_SCALE_FP32) {
+                ((float*)scales)[r * groups + k] = group_amax / fmt_max;
+                mult = group_amax > 0.0f ? fmt_max / group_amax : FLT_MAX;
+                if (mult > FLT_MAX)
+                    mult = FLT_MAX;
+            } else {
+                const int e = ue8m0_exponent_closed_form(group_amax, fmt_max);
+                ((uint8_t*)scales)[r * groups + k] = (uint8_t)(e + 127);
+                mult = ldexpf(1.0f, -e);
+            }
+            for (int64_t j = 0; j < G; ++j) {
+                const int64_t col = k * G + j;
+                const float q = vals[j] * mult;
+                if (fmt == ORACLE_FP8) {
+                    out_row[col] = oracle_e4m3(q);
+                } else if (col % 2 == 0) {
+                    out_row[col / 2] = oracle_e2m1(q);
+                } else {
+                    out_row[col / 2] = (uint8_t)(out_row[col / 2] | (oracle_e2m1(q) << 4));
+                }
+            }
         }
     }
-    free(row_y);
+    free(vals);
+    if (clamped_count)
+        *clamped_count += clamped;
     return 0;
 }
 

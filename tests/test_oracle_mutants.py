@@ -51,6 +51,28 @@ MUTANTS = [
     ("reduce_scale_per_term", "const float o = acc * global_scale;", "const float o = acc * global_scale * 1.0000001f;"),
     ("bf16_ties_up", "up = (int)((lo_b >> 16) & 1u); /* tie: go to the even code */", "up = 1;"),
     ("bf16_truncates", "if (dlo < dhi)\n        up = 0;", "if (dlo <= dhi || 1)\n        up = 0;"),
+    # the fused per-row form, written apart from the two stages
+    ("fused_clamp_count_at_limit", "if (gv > clamp_limit) {", "if (gv >= clamp_limit) {"),
+    ("fused_up_not_clamped",
+     "if (uv < -clamp_limit)\n                        uv = -clamp_limit;\n                    else if (uv > clamp_limit)\n"
+     "                        uv = clamp_limit;", ""),
+    ("fused_product_order",
+     "const float act = gv * oracle_sigmoid(gv);\n                const float prod = act * uv;",
+     "const float act = oracle_sigmoid(gv) * uv;\n                const float prod = act * gv;"),
+    ("fused_weight_dropped", "const float v = w != NULL ? prod * w[r] : prod;", "const float v = prod;"),
+    ("fused_amax_without_abs", "const float mag = v < 0.0f ? -v : v;", "const float mag = v;"),
+    ("fused_ue8m0_off_by_one", "int k = ea - ef + (ma > mf ? 1 : 0);", "int k = ea - ef + (ma >= mf ? 1 : 0);"),
+    ("fused_inverse_of_rounded_scale", "mult = group_amax > 0.0f ? fmt_max / group_amax : FLT_MAX;",
+     "mult = 1.0f / (group_amax / fmt_max);"),
+    ("fused_fp4_nibbles_swapped", "} else if (col % 2 == 0) {", "} else if (col % 2 == 1) {"),
+    ("fused_scale_index", "((float*)scales)[r * groups + k] = group_amax / fmt_max;",
+     "((float*)scales)[r + k] = group_amax / fmt_max;"),
+    # the stand-alone cast of bf16 rows
+    ("cast_bf16_row_stride", "row[j] = bf16_to_float(x[r * hidden + j]);", "row[j] = bf16_to_float(x[j]);"),
+    ("cast_bf16_widening_drops_a_bit", "row[j] = bf16_to_float(x[r * hidden + j]);",
+     "row[j] = bf16_to_float((uint16_t)(x[r * hidden + j] & 0xFFFEu));"),
+    ("cast_bf16_scale_stride", "(uint8_t*)scales + (size_t)(r * groups) * scale_bytes);",
+     "(uint8_t*)scales + (size_t)r * scale_bytes);"),
 ]
 
 

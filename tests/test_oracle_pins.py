@@ -417,3 +417,110 @@ def test_scale_inverse_is_rn_of_fmt_max_over_amax():
     assert codes[0].tolist() == want_codes
     assert codes[0, 0] == 0x7E and codes[0, 1] == 0x38 and codes[0, 2] == 0xB8
     assert scales[0, 0] == np.float32(want_scales[0])
+
+
+# ---------------------------------------------------------------------------
+# The stand-alone cast of bf16 rows against the exact evaluator
+# ---------------------------------------------------------------------------
+def _bf16_cast_rows():
+    """Four bf16 rows of 16 values, built so that each row's abs-max makes the
+    codes land on known ties: row 0 has amax 448 (fp32 inverse exactly 1, so
+    1.0625 and 1.1875 are E4M3 midpoints, and 6's inverse makes 0.25 .. 5 E2M1
+    midpoints in the FP4 groups), row 1 signed zeros and the smallest bf16
+    subnormals, row 2 values whose last mantissa bit is set (a widening that
+    dropped it would move them), row 3 an all-zero group next to a huge one."""
+    f = E.float_to_bf16
+    odd = lambda v: E.bf16_to_float((E.float_to_bf16(v) | 1))  # noqa: E731  last mantissa bit set
+    rows = [
+        [448.0, 1.0625, -1.1875, 0.25, 0.75, -1.25, 2.5, 5.0, 6.0, 0.25, -0.75, 1.75, 3.5, -5.0, 1.25, 2.5],
+        [-0.0, 0.0, 2.0 ** -133, -(2.0 ** -133), 2.0 ** -127, 3 * 2.0 ** -130, -0.0, 0.0,
+         1.5 * 2.0 ** -127, -(1.25 * 2.0 ** -127), 2.0 ** -126, -(2.0 ** -126), -0.0, 2.0 ** -133, 0.0,
+         -(2.0 ** -132)],
+        [odd(1.0), -odd(1.0), odd(3.0), odd(255.0), -odd(250.0), odd(0.5), 127.5, -63.75,
+         odd(1.5), odd(2.0), -odd(4.0), odd(8.0), odd(16.0), -odd(32.0), odd(64.0), -odd(128.0)],
+        [0.0, -0.0, 0.0, 0.0, -0.0, 0.0, 0.0, -0.0, 1.5 * 2.0 ** 127, -(1.25 * 2.0 ** 126), 2.0 ** 100, 1.0, -1.0,
+         0.5, 7.0, -2.0 ** 127],
+    ]
+    return np.array([[f(v) for v in r] for r in rows], dtype=np.uint16)
+
+
+@pytest.mark.parametrize("group,fmt,sfmt", [(0, 8, 0), (0, 8, 1), (8, 8, 0), (8, 8, 1), (0, 4, 0), (0, 4, 1),
+                                            (8, 4, 1), (8, 4, 0), (4, 4, 1), (2, 8, 0)], ids=str)
+def test_cast_bf16_matches_exact_evaluator(group, fmt, sfmt):
+    """oracle_cast_bf16 on several rows (a row-stride mistake reads the wrong
+    row), groups (a scale-index mistake writes the wrong scale) and ties,
+    signed zeros and subnormals (a widening mistake changes a code): every
+    code and scale against the exact-rational evaluator on the bf16 values
+    widened by hand."""
+    x = _bf16_cast_rows()
+    codes, scales = oracle.cast_bf16(x, group, fmt, sfmt)
+    for r in range(x.shape[0]):
+        vals = [E.bf16_to_float(int(h)) for h in x[r]]
+        ecodes, escales = E.cast_row(vals, group, fmt, sfmt)
+        if fmt == 4:
+            ecodes = E.pack_fp4(ecodes)
+        assert codes[r].tolist() == ecodes, r
+        got = [float(v) for v in scales[r]] if sfmt == 0 else scales[r].tolist()
+        assert got == escales, r
+
+
+def test_cast_bf16_hand_ties():
+    """Hand-read codes of row 0 per-token with an fp32 scale: amax 448 gives
+    scale 1 and inverse 1, so the codes are the plain E4M3 casts: 448 -> 0x7E,
+    1.0625 (midway between 1 = 0x38 and 1.125 = 0x39) -> 0x38, -1.1875 (midway
+    between 1.125 and 1.25 = 0x3A) -> 0xBA, 0.25 = 2^-2 -> 0x28, 0.75 = 1.5 * 2^-1 -> 0x34."""
+    codes, scales = oracle.cast_bf16(_bf16_cast_rows()[:1], 0, 8, 0)
+    assert scales[0, 0] == 1.0
+    assert codes[0, :5].tolist() == [0x7E, 0x38, 0xBA, 0x28, 0x34]
+
+
+# ---------------------------------------------------------------------------
+# Rows that pin the fused form's scale step on its own
+# ---------------------------------------------------------------------------
+def test_fused_scale_inverse_is_rn_of_fmt_max_over_amax():
+    """Reading r6 on the fused form.  Gate 0x400b (2.171875) with up 0x3f86
+    (1.046875) gives the row's abs-max y0 = 0x1.0541e4p+1; gate 0x400b with up
+    0x3dc9 (0.0981...) gives y1 = 0x1.87e2d6p-3 (no weight).  With
+    inv = RN(448 / y0), RN(y1 * inv) lands in E4M3 code 0x62; the reciprocal
+    of the rounded scale, RN(1 / RN(y0 / 448)), is one ulp larger and moves it
+    to 0x63.  The row was found by a search over bf16 pairs whose two inverses
+    differ; every value here is re-derived by the exact evaluator."""
+    gate = [0x400B, 0x400B] + [0] * 6
+    up = [0x3F86, 0x3DC9] + [0] * 6
+    x = np.array([gate + up], dtype=np.uint16)
+    codes, scales, _ = oracle.swiglu_cast(x, None, 0, None, 8, 0)
+    y, _ = E.swiglu_row(gate, up, None, None)
+    assert y[0] == float.fromhex("0x1.0541e4p+1") and y[1] == float.fromhex("0x1.87e2d6p-3")
+    want_codes, want_scales = E.cast_row(y, 0, 8, 0)
+    assert codes[0].tolist() == want_codes and want_codes[:2] == [0x7E, 0x62]
+    assert float(scales[0, 0]) == want_scales[0]
+    alt_inv = E.div_f32(1.0, E.div_f32(y[0], 448.0))
+    assert alt_inv != E.div_f32(448.0, y[0])
+    assert E.nearest_code(E.mul_f32(y[1], alt_inv), E.E4M3, 0x80) == 0x63
+
+
+@pytest.mark.parametrize("fmt,gate,up,byte", [
+    (8, 28.0, 16.0, 127),      # sigma(28) = 1 in fp32: amax = 448 exactly, k = 0
+    (8, 28.0, 32.0, 128),      # amax = 896 = 448 * 2, k = 1
+    (8, 24.0, 0.4375, 122),    # amax = 10.5 = 448 * 2^-5.4..: k = -5 (448/32 = 14 >= 10.5 > 7)
+    (4, 24.0, 0.25, 127),      # amax = 6 exactly
+    (4, 24.0, 0.125, 126),     # amax = 3 = 6 / 2
+    (4, 20.0, 0.5, 128),       # amax = 10: 6 < 10 <= 12
+], ids=str)
+def test_fused_ue8m0_amax_on_and_near_a_power_of_two_boundary(fmt, gate, up, byte):
+    """UE8M0 on the fused form when the group's abs-max equals fmt_max * 2^k
+    exactly (the smallest k then satisfies fmt_max * 2^k = amax, so k, not
+    k + 1) and when it lies between two such values.  The gates are large
+    enough that sigma rounds to 1 in fp32, so amax = gate * up exactly."""
+    f = E.float_to_bf16
+    g = [f(gate), f(gate / 2), 0, 0, f(-1.0), 0, 0, 0]
+    u = [f(up), f(up), 0, 0, f(up), 0, 0, 0]
+    x = np.array([g + u, g[::-1] + u[::-1]], dtype=np.uint16)
+    codes, scales, _ = oracle.swiglu_cast(x, None, 0, None, fmt, 1)
+    for r in range(2):
+        y, _ = E.swiglu_row(x[r, :8].tolist(), x[r, 8:].tolist(), None, None)
+        ecodes, escales = E.cast_row(y, 0, fmt, 1)
+        if fmt == 4:
+            ecodes = E.pack_fp4(ecodes)
+        assert escales == [byte]
+        assert scales[r].tolist() == [byte] and codes[r].tolist() == ecodes
