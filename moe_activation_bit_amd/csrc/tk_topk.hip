@@ -487,28 +487,36 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
         return TK_ERR_INVALID_ARG;
     if (experts > kMaxExperts || k > kWave)
         return TK_ERR_UNSUPPORTED;
-    const uint32_t C = (uint32_t)((experts + kWave - 1) / kWave);
-    uint32_t gl_log2 = 0;
-    if (n_group > 1) {
-        // a group must be a block of 2^j whole lanes
-        if (per % C != 0)
-            return TK_ERR_UNSUPPORTED;
-        const uint32_t lanes = (uint32_t)(per / C);
-        if ((lanes & (lanes - 1)) != 0)
-            return TK_ERR_UNSUPPORTED;
-        gl_log2 = (uint32_t)__builtin_ctz(lanes);
-    }
+    // Experts per lane for a layout of `lanes` lanes per token: the smallest C
+    // from ceil(experts / lanes) up to 8 whose groups are blocks of 2^j whole
+    // lanes (per % C == 0 and per / C a power of two); 0 when there is none.
+    // A C above the minimum leaves the lanes past experts / C empty.
+    auto experts_per_lane = [&](int64_t lanes, uint32_t& gl) -> uint32_t {
+        for (int64_t c = (experts + lanes - 1) / lanes; c <= 8; ++c) {
+            if (n_group == 1) {
+                gl = 0;
+                return (uint32_t)c;
+            }
+            const int64_t l = per / c;
+            if (per % c == 0 && (l & (l - 1)) == 0) {
+                gl = (uint32_t)__builtin_ctzll((unsigned long long)l);
+                return (uint32_t)c;
+            }
+        }
+        return 0;
+    };
+    // the two-tokens-per-wave layout (up to 256 experts, k <= 32) first, then one token per wave
+    uint32_t gl2 = 0, gl_log2 = 0;
+    const uint32_t C2 = (experts <= 8 * (kWave / 2) && k <= kWave / 2) ? experts_per_lane(kWave / 2, gl2) : 0u;
+    const uint32_t C = C2 ? 0u : experts_per_lane(kWave, gl_log2);
+    if (!C2 && !C)
+        return TK_ERR_UNSUPPORTED;
     if (tokens == 0)
         return TK_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (experts <= 8 * (kWave / 2) && k <= kWave / 2) {
-        // the two-tokens-per-wave layout, where its groups are whole lanes too
-        const uint32_t C2 = (uint32_t)((experts + kWave / 2 - 1) / (kWave / 2));
-        const uint32_t lanes2 = n_group > 1 ? (uint32_t)(per / C2) : 1u;
-        if (n_group == 1 || (per % C2 == 0 && (lanes2 & (lanes2 - 1)) == 0)) {
-            const uint32_t gl2 = n_group > 1 ? (uint32_t)__builtin_ctz(lanes2) : 0u;
-            const uint32_t tpb = 2 * (kThreads / kWave);
-            const uint32_t pblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+    if (C2) {
+        const uint32_t tpb = 2 * (kThreads / kWave);
+        const uint32_t pblocks = (uint32_t)((tokens + tpb - 1) / tpb);
 #define TK_TOPK2_LAUNCH(CC, FULL, K8)                                                                         \
     hipLaunchKernelGGL((topk_pair_kernel<CC, FULL, K8>), dim3(pblocks), dim3(kThreads), 0, s, scores,         \
                        (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group, (uint32_t)topk_group, \
@@ -525,20 +533,19 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
         else                                                                                                  \
             TK_TOPK2_LAUNCH(CC, false, false);                                                                \
     }
-            switch (C2) {
-            case 1: TK_TOPK2(1); break;
-            case 2: TK_TOPK2(2); break;
-            case 3: TK_TOPK2(3); break;
-            case 4: TK_TOPK2(4); break;
-            case 5: TK_TOPK2(5); break;
-            case 6: TK_TOPK2(6); break;
-            case 7: TK_TOPK2(7); break;
-            default: TK_TOPK2(8); break;
-            }
+        switch (C2) {
+        case 1: TK_TOPK2(1); break;
+        case 2: TK_TOPK2(2); break;
+        case 3: TK_TOPK2(3); break;
+        case 4: TK_TOPK2(4); break;
+        case 5: TK_TOPK2(5); break;
+        case 6: TK_TOPK2(6); break;
+        case 7: TK_TOPK2(7); break;
+        default: TK_TOPK2(8); break;
+        }
 #undef TK_TOPK2
 #undef TK_TOPK2_LAUNCH
-            return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
-        }
+        return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
     }
     const uint32_t blocks = (uint32_t)((tokens + kThreads / kWave - 1) / (kThreads / kWave));
 #define TK_TOPK(CC)                                                                                           \

@@ -180,7 +180,10 @@ def test_topk_unsupported_and_empty():
     assert topk(tokens=0, experts=512, n_group=8) == OK     # 8 per lane, groups of 8 lanes
     assert topk(tokens=0, experts=384, n_group=1, topk_group=1) == OK
     assert topk(experts=256, n_group=1, topk_group=1, k=65) == UNSUPPORTED
-    assert topk(experts=72, n_group=3, topk_group=2, k=5) == UNSUPPORTED
+    assert topk(experts=72, n_group=8, topk_group=2, k=5) == UNSUPPORTED  # 9 experts per group: no layout
+    assert topk(tokens=0, experts=72, n_group=3, topk_group=2, k=5) == OK  # 3 per lane, 8 lanes per group
+    assert topk(tokens=0, experts=160, n_group=8, topk_group=3, k=6) == OK  # 5 per lane, 4 lanes per group
+    assert topk(tokens=0, experts=100, n_group=5, topk_group=2, k=5) == OK  # 5 per lane (above the minimum 4)
     assert topk(tokens=0) == OK
 
 

@@ -26,6 +26,24 @@ def run(scores, k, ng, tg, normalise):
     return i[32:32 + T * k].reshape(T, k), ww[32:32 + T * k].reshape(T, k)
 
 
+def layout_supported(E, k, ng):
+    """The library's layout rule (include/tk.h, tk_topk_gate): 32 lanes per
+    token when E <= 256 and k <= 32, else 64; some experts-per-lane count C
+    from ceil(E / lanes) to 8 must divide E / ng with a power-of-two quotient."""
+    per = E // ng
+
+    def fits(lanes):
+        for c in range(-(-E // lanes), 9):
+            if ng == 1:
+                return True
+            q = per // c
+            if per % c == 0 and q & (q - 1) == 0:
+                return True
+        return False
+
+    return (E <= 256 and k <= 32 and fits(32)) or fits(64)
+
+
 SHAPES = [  # (experts, k, n_group, topk_group)
     (256, 8, 8, 4), (256, 8, 1, 1), (256, 64, 1, 1), (256, 6, 16, 2), (128, 4, 4, 2), (64, 6, 1, 1), (64, 8, 32, 4),
     (8, 2, 1, 1), (100, 3, 1, 1), (160, 8, 5, 2), (200, 5, 1, 1),
@@ -39,6 +57,10 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     (256, 32, 1, 1), (256, 33, 1, 1), (224, 8, 1, 1), (224, 8, 7, 3),
     # the normalising sum as a running sum within 16 lanes (k <= 16) and serially above
     (256, 16, 1, 1), (256, 17, 1, 1), (128, 16, 4, 2),
+    # groups that only the two-token layout holds whole (160 / 8: 5 experts per lane, 4 lanes per group;
+    # 96 / 4: 3 per lane, 8 lanes), groups that need more experts per lane than the minimum (120 / 6 and
+    # 100 / 5: 5 per lane, 4 lanes), and a shape no layout holds (9 experts per group)
+    (160, 6, 8, 3), (96, 4, 4, 2), (120, 6, 6, 2), (100, 5, 5, 2), (72, 4, 8, 2),
 ]
 
 
@@ -55,9 +77,7 @@ def test_topk_matches_oracle(shape, normalise):
     s[6, ::2] = -0.0
     s[6, 1::2] = 0.0
     s[7] = -u[7].astype(np.float32)
-    C = (E + 63) // 64
-    per = E // ng
-    if ng > 1 and (per % C or ((per // C) & (per // C - 1))):
+    if not layout_supported(E, k, ng):
         sd = torch.from_numpy(s).to(DEV)
         idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
         w = torch.empty((T, k), dtype=torch.float32, device=DEV)
