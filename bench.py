@@ -271,24 +271,44 @@ def unfused_path(torch, tk, dev, w, n, fmt, sfmt, clamp, sets, reps, stream, fus
             "kernels": "tk_swiglu_forward (fp32 y out) + tk_cast (fp32 y in)"}
 
 
-def stream_ceiling(torch, dev, in_bytes: int, reps: int = 30):
-    """GB/s of plain streaming kernels moving the workload's bytes: read-4 /
-    write-1 (x in, one byte out per four read) and read-only."""
+# The 4:1 probe's matrix: cache-policy bits of the loads and of the stores
+# (0: none, 2: nt, 16: sc1, 17: sc0 sc1) x grid (steps per unit, workgroups
+# per CU; 0 = non-persistent, one unit per wave).
+PROBE_POLICIES = (0, 2, 16, 17)
+PROBE_GRIDS = ((1, 0), (4, 0), (4, 2))
+POLICY_NAMES = {0: "plain", 2: "nt", 16: "sc1", 17: "sc0sc1"}
+
+
+def stream_ceiling(torch, dev, rows: int, hidden: int, reps: int = 10, rounds: int = 3):
+    """GB/s of plain streaming kernels moving the workload's bytes with no
+    arithmetic.  The ceiling is the fastest of the 4:1 probe's matrix (the
+    fused step's own layout: gate and up halves of a packed bf16 row in, one
+    byte per column out) over load policy x store policy x grid, each combination
+    timed `rounds` times interleaved (median kept); a plain read-only stream
+    over the same input is reported beside it."""
     import ctypes
+    import statistics
     lib = ctypes.CDLL(os.path.join(ROOT, "moe_activation_bit_amd", "libstreamceil.so"))
-    lib.stream_read4_write1.restype = ctypes.c_int
-    lib.stream_read4_write1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.stream_probe_4to1.restype = ctypes.c_int
+    lib.stream_probe_4to1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.c_uint32, ctypes.c_void_p]
     lib.stream_read_only.restype = ctypes.c_int
     lib.stream_read_only.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
-    in_bytes -= in_bytes % 32
-    sets = 3
+    # the probe needs whole 2048-column rows: the same bytes laid out that way
+    ph = 2048
+    prow = max(1, (rows * hidden + ph - 1) // ph)
+    in_bytes, out_bytes = prow * 4 * ph, prow * ph
+    nbytes = in_bytes + out_bytes
+    sets = 2
     ins = [torch.ones(in_bytes // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
-    outs = [torch.empty(in_bytes // 16, dtype=torch.int32, device=dev) for _ in range(sets)]
+    outs = [torch.empty(out_bytes // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
 
-    def timed(fn, nbytes):
+    def timed(fn):
         for i in range(3):
             fn(i)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -298,18 +318,39 @@ def stream_ceiling(torch, dev, in_bytes: int, reps: int = 30):
             fn(i)
         ev1.record(stream)
         torch.cuda.synchronize()
-        return nbytes / (ev0.elapsed_time(ev1) / 1e3 / reps) / 1e9
+        return ev0.elapsed_time(ev1) / 1e3 / reps
 
-    def rw(i):
-        assert lib.stream_read4_write1(ins[i % sets].data_ptr(), outs[i % sets].data_ptr(), in_bytes, sh) == 0
+    def probe(lp, sp, spu, bpc):
+        def fn(i):
+            assert lib.stream_probe_4to1(ins[i % sets].data_ptr(), outs[i % sets].data_ptr(), prow, ph, lp, sp,
+                                         spu, bpc, cus, sh) == 0
+        return fn
+
+    combos = [(lp, sp, spu, bpc) for lp in PROBE_POLICIES for sp in PROBE_POLICIES for spu, bpc in PROBE_GRIDS]
+    times = {c: [] for c in combos}
+    for _ in range(rounds):
+        for c in combos:
+            times[c].append(timed(probe(*c)))
 
     def ro(i):
         assert lib.stream_read_only(ins[i % sets].data_ptr(), in_bytes, sink.data_ptr(), sh) == 0
 
-    res = {"read4_write1_GBs": round(timed(rw, in_bytes + in_bytes // 4), 1),
-           "read_only_GBs": round(timed(ro, in_bytes), 1),
-           "read_bytes": in_bytes,
-           "kernel": "non-persistent, 32 B read + 8 B written per thread, non-temporal"}
+    ro_s = timed(ro)
+    gbs = {c: nbytes / statistics.median(t) / 1e9 for c, t in times.items()}
+    best = max(gbs, key=gbs.get)
+
+    def label(c):
+        lp, sp, spu, bpc = c
+        grid = f"persistent{bpc}x{spu}" if bpc else f"nonpersistent{spu}"
+        return f"load={POLICY_NAMES[lp]},store={POLICY_NAMES[sp]},grid={grid}"
+
+    res = {"read4_write1_GBs": round(gbs[best], 1),
+           "best": label(best),
+           "read_only_GBs": round(in_bytes / ro_s / 1e9, 1),
+           "bytes_per_launch": nbytes,
+           "matrix_GBs": {label(c): round(v, 1) for c, v in sorted(gbs.items(), key=lambda kv: -kv[1])},
+           "kernel": f"probe_4to1_kernel: packed bf16 [{prow}, {2 * ph}] in as gate/up halves, "
+                     f"[{prow}, {ph}] bytes out; median of {rounds} interleaved rounds of {reps} launches"}
     del ins, outs
     torch.cuda.empty_cache()
     return res
@@ -839,7 +880,7 @@ def main():
                                       avg_launch_s)
     if not args.no_ceiling:
         log("[bench] streaming ceiling ...")
-        ceil = stream_ceiling(torch, dev, 4 * w.hidden * n)
+        ceil = stream_ceiling(torch, dev, n, w.hidden)
         out["roofline"]["measured_ceiling"] = ceil
         out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["read4_write1_GBs"], 4)
     if not args.no_cpu_baseline:

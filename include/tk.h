@@ -44,6 +44,10 @@
  *  - n == 0 returns TK_OK and launches nothing.
  *  - Errors are returned, never thrown; on any error nothing is launched
  *    except for TK_ERR_HIP, which reports a failed launch or device query.
+ *  - Inputs are expected to be finite.  A NaN or infinite input gives codes
+ *    and scales the ABI does not specify; in particular, with the clamp on a
+ *    NaN gate or up value comes out as a finite clamped value (the clamp is a
+ *    min / max that does not propagate NaN), so it does not show in the codes.
  */
 #ifndef TK_H_
 #define TK_H_
@@ -211,8 +215,11 @@ tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
  *  topk_weight  fp32 [tokens, k] (device), in the same order.
  * Returns TK_ERR_INVALID_ARG for violated preconditions, overlapping outputs or
  * misaligned pointers; TK_ERR_UNSUPPORTED when experts > 512 or k > 64, or when
- * a group is not a power-of-two number of whole 64-lane slots (experts/n_group
- * must be a multiple of ceil(experts/64), with a power-of-two quotient).
+ * groups cannot be laid out as blocks of 2^j whole lanes: a token takes 32
+ * lanes when experts <= 256 and k <= 32, else 64, each lane C consecutive
+ * experts, and some C from ceil(experts / lanes) to 8 must divide
+ * experts / n_group with a power-of-two quotient (the 32-lane layout is tried
+ * first).  Example: 160 experts in 8 groups take C = 5, 4 lanes per group.
  */
 tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
                        int64_t topk_group, int normalise, int32_t* topk_idx, float* topk_weight, void* stream);
