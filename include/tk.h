@@ -129,12 +129,14 @@ tk_status tk_init(int device);
  * multiple of 8; group_size < 0, not a multiple of 8 or not dividing hidden;
  * clamp_limit is NaN or <= 0; scale_fmt is unknown; n > 0 and x, codes or
  * scales is NULL; a pointer breaks its alignment; an output overlaps an input.
- * Returns TK_ERR_UNSUPPORTED when the group (in units of 8 columns) is not a
- * power of two up to 64 and not a multiple of 64; when one group spans more
- * than 32768 columns; or when a row holds several groups longer than 8192
- * columns whose number of 512-column steps is odd (groups up to 16384
- * columns) or not a multiple of 4 (longer groups).  A group longer than 8192
- * columns is shared by 2 or 4 waves of one workgroup.
+ * Every group_size that is valid has a kernel: groups of 2^j * 8 columns up to
+ * 512 are reduced inside one 512-column step, groups of whole steps over one
+ * to four waves, other widths up to 8192 columns as runs of whole groups per
+ * wave reduced through LDS, and the remaining ones (wider than 8192 columns
+ * and not split evenly over 2 or 4 waves, or wider than 32768) by one wave
+ * per group that reads the group twice.  TK_ERR_UNSUPPORTED is returned only
+ * when the plan would need 2^31 or more units of work (n times the units per
+ * row).
  */
 tk_status tk_swiglu_cast_fp8(const void* x, const float* topk_weight, int64_t n, int64_t hidden,
                              int64_t group_size, float clamp_limit, tk_scale_fmt scale_fmt,
@@ -180,7 +182,8 @@ tk_status tk_swiglu_forward(const void* x, const float* topk_weight, int64_t n, 
  *             tk_swiglu_cast_fp8.
  * Returns TK_ERR_INVALID_ARG for the same conditions as tk_swiglu_cast_fp8
  * (without weight, clamp and counter) and for an unknown in_dtype;
- * TK_ERR_UNSUPPORTED for the same group shapes.
+ * TK_ERR_UNSUPPORTED only when the plan would need 2^31 or more units of work,
+ * as for tk_swiglu_cast_fp8 (every valid group_size has a kernel).
  */
 tk_status tk_cast_fp8(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidden, int64_t group_size,
                       tk_scale_fmt scale_fmt, void* codes, void* scales, void* stream);

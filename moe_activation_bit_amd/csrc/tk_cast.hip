@@ -147,6 +147,156 @@ __global__ __launch_bounds__(kThreads) void cast_xw_kernel(Params p)
     }
 }
 
+// A span of `nslots` lane slots of row `row` from slot `slot0` on, widened to
+// fp32: lane l of step s holds slot slot0 + 64*s + l; lanes past the span
+// re-read its last slot and give abs-max bits 0.  Loads run up to four steps
+// ahead of the widening.  Used by the segmented and two-pass kernels, whose
+// spans start at any slot.
+template <bool F32IN, int SPU>
+__device__ __forceinline__ void cast_span_load(const Params& p, uint32_t lane, uint32_t row, uint32_t slot0,
+                                               uint32_t nslots, float (&y)[SPU][8], uint32_t (&mbits)[SPU])
+{
+    constexpr uint32_t kSlotBytes = F32IN ? 32u : 16u;
+    constexpr int D = SPU < 4 ? SPU : 4;
+    constexpr int P = F32IN ? 2 : 1;
+    const char* xr = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * kSlotBytes);
+    const uint32_t last = slot0 + nslots - 1u;
+    auto off = [&](int s) { return min(slot0 + (uint32_t)s * kWaveSize + lane, last) * kSlotBytes; };
+    uint4 q[D][P];
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+#pragma unroll
+        for (int h = 0; h < P; ++h)
+            q[s][h] = load16(reinterpret_cast<const uint4*>(xr + off(s) + 16u * h));
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        uint4 cur[P];
+#pragma unroll
+        for (int h = 0; h < P; ++h)
+            cur[h] = q[s % D][h];
+        if (s + D < SPU) {
+#pragma unroll
+            for (int h = 0; h < P; ++h)
+                q[s % D][h] = load16(reinterpret_cast<const uint4*>(xr + off(s + D) + 16u * h));
+        }
+        if constexpr (F32IN) {
+            const uint32_t w[8] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w,
+                                   cur[P - 1].x, cur[P - 1].y, cur[P - 1].z, cur[P - 1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                y[s][j] = as_float(w[j]);
+        } else {
+            const uint32_t w[4] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[s][2 * k] = bf16_lo(w[k]);
+                y[s][2 * k + 1] = bf16_hi(w[k]);
+            }
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2)
+            m = fmaxf(m, fmaxf(fabsf(y[s][j]), fabsf(y[s][j + 1])));
+        mbits[s] = (uint32_t)s * kWaveSize + lane < nslots ? as_uint(m) : 0u;
+    }
+}
+
+// Groups whose width is not a power of two of lane slots up to 64 and not a
+// multiple of 64, up to 8192 columns: each unit is a run of whole groups of
+// one row that one wave holds in SPU steps, reduced in the wave's own LDS
+// buffer (quantize_seg).  One unit per wave, like cast_kernel.
+template <int FMT, int SFMT, bool F32IN, int SPU>
+__global__ __launch_bounds__(kThreads) void cast_seg_kernel(Params p)
+{
+    constexpr int kWaves = kThreads / kWaveSize;
+    __shared__ uint32_t seg_buf[kWaves][SegLds<SPU>::kSlots];
+    __shared__ float seg_inv[kWaves][SegLds<SPU>::kGroups];
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wib);
+    const uint32_t nwaves = gridDim.x * kWaves;
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t g0 = (u - row * p.upr) * p.gpu;
+        const uint32_t ngr = min(p.gpu, p.groups_row - g0);
+        const uint32_t slot0 = g0 * p.gslots;
+        float y[SPU][8];
+        uint32_t mbits[SPU];
+        cast_span_load<F32IN, SPU>(p, lane, row, slot0, ngr * p.gslots, y, mbits);
+        quantize_seg<FMT, SFMT, SPU>(p, lane, row, g0, ngr, slot0, y, mbits, seg_buf[wib], seg_inv[wib]);
+    }
+}
+
+// Groups no other kernel covers (wider than 8192 columns and not split evenly
+// over 2 or 4 waves, or wider than 32768 columns): one wave per group, which
+// reads the group twice, kTwoPassSteps steps at a time -- first for its
+// abs-max, then for the codes with the group's scale.
+template <int FMT, int SFMT, bool F32IN>
+__global__ __launch_bounds__(kThreads) void cast_2p_kernel(Params p)
+{
+    constexpr int S = kTwoPassSteps;
+    constexpr uint32_t kChunk = S * kWaveSize;
+    constexpr int kWaves = kThreads / kWaveSize;
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x / kWaveSize));
+    const uint32_t nwaves = gridDim.x * kWaves;
+    const uint32_t gs = p.gslots;
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t k = u - row * p.upr;
+        const uint32_t slot0 = k * gs;
+        uint32_t mb = 0;
+        for (uint32_t c = 0; c < gs; c += kChunk) {
+            float y[S][8];
+            uint32_t mbits[S];
+            cast_span_load<F32IN, S>(p, lane, row, slot0 + c, min(kChunk, gs - c), y, mbits);
+            mb = max(mb, lane_max<S>(mbits, S));
+        }
+        mb = wave_umax(mb);
+        float s32 = 0.0f;
+        uint32_t s8 = 0;
+        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+        if (lane == 0)
+            store_scale<SFMT>(p, row, k, s32, s8);
+        uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+        for (uint32_t c = 0; c < gs; c += kChunk) {
+            float y[S][8];
+            uint32_t mbits[S];
+            cast_span_load<F32IN, S>(p, lane, row, slot0 + c, min(kChunk, gs - c), y, mbits);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t rel = c + (uint32_t)s * kWaveSize + lane;
+                if (rel < gs)
+                    quantize_store<FMT>(row_codes, slot0 + rel, y[s], inv);
+            }
+        }
+    }
+}
+
+template <int FMT, int SFMT, bool F32IN>
+bool launch_cast_seg(const UnitPlan& plan, const Params& p, int blocks, hipStream_t s)
+{
+    if (plan.twopass) {
+        hipLaunchKernelGGL((cast_2p_kernel<FMT, SFMT, F32IN>),
+                           dim3(blocks < (int)kMaxCastXwBlocks ? blocks : (int)kMaxCastXwBlocks), dim3(kThreads), 0, s,
+                           p);
+        return true;
+    }
+    switch (plan.spu_max) {
+#define TK_CAST_SEG(N)                                                                                          \
+    case N:                                                                                                     \
+        hipLaunchKernelGGL((cast_seg_kernel<FMT, SFMT, F32IN, N>), dim3(blocks), dim3(kThreads), 0, s, p);      \
+        return true;
+        TK_CAST_SEG(1)
+        TK_CAST_SEG(2)
+        TK_CAST_SEG(4)
+        TK_CAST_SEG(8)
+        TK_CAST_SEG(16)
+#undef TK_CAST_SEG
+    default: return false;
+    }
+}
+
 template <int FMT, int SFMT, bool F32IN, bool ROWRED, bool PARTIAL>
 bool launch_cast(int spu_max, const Params& p, int blocks, hipStream_t s)
 {
@@ -225,6 +375,13 @@ bool launch_cast_xw(const UnitPlan& plan, const Params& p, hipStream_t s)
 template <int FMT>
 bool dispatch_cast(int sfmt, bool f32in, const UnitPlan& plan, const Params& p, int blocks, hipStream_t s)
 {
+    if (plan.seg || plan.twopass) {
+        if (sfmt == TK_SCALE_FP32)
+            return f32in ? launch_cast_seg<FMT, TK_SCALE_FP32, true>(plan, p, blocks, s)
+                         : launch_cast_seg<FMT, TK_SCALE_FP32, false>(plan, p, blocks, s);
+        return f32in ? launch_cast_seg<FMT, TK_SCALE_UE8M0, true>(plan, p, blocks, s)
+                     : launch_cast_seg<FMT, TK_SCALE_UE8M0, false>(plan, p, blocks, s);
+    }
     if (plan.xwaves > 1) {
         if (sfmt == TK_SCALE_FP32)
             return f32in ? launch_cast_xw<FMT, TK_SCALE_FP32, true>(plan, p, s)

@@ -41,6 +41,9 @@ struct Params {
     float clamp;            // L (clamp variants)
     uint32_t scale_layout;  // kScaleRowMajor, kScaleColMajor or kScalePacked
     uint32_t scale_ld;      // column-major / packed: elements between consecutive groups' columns
+    uint32_t gslots;        // segmented and two-pass units: lane slots (8 columns) per group
+    uint32_t gpu;           // segmented units: groups per unit
+    uint32_t gmagic;        // segmented units: ceil(2^32 / gslots), so that q / gslots = mulhi(q, gmagic)
 };
 
 // Scale layouts (the value kind -- fp32 or UE8M0 byte -- is the SFMT template):
@@ -277,6 +280,69 @@ __device__ __forceinline__ void quantize_unit(const Params& p, uint32_t lane, ui
     }
 }
 
+// Segmented units: groups whose width is not a power of two of lane slots up
+// to 64 and not a multiple of 64 (24, 40, 48, 96, 896 columns, ...).  A unit
+// is a run of ngr whole groups of one row starting at lane slot slot0; lane l
+// of step s holds slot slot0 + 64*s + l, so a group's slots straddle lanes and
+// steps at any offset.  The lanes' per-slot abs-max bits go to `buf` (the
+// wave's own SPU*64 words of LDS); lanes then reduce the groups from there --
+// L = 64/ngr lanes per group (a power of two, 1 when ngr > 64), each over a
+// contiguous chunk of its group's slots, then a butterfly over the L lanes --
+// and the group's first lane stores the scale and leaves the multiplier in
+// `invs`; finally every lane reads its slot's multiplier back (the group of a
+// slot by a multiply-high with p.gmagic) and quantises.  All lanes of the wave
+// must call this; `mbits` is 0 for lanes past the unit's last slot.
+template <int FMT, int SFMT, int SPU>
+__device__ __forceinline__ void quantize_seg(const Params& p, uint32_t lane, uint32_t row, uint32_t g0, uint32_t ngr,
+                                             uint32_t slot0, const float (&y)[SPU][8], const uint32_t (&mbits)[SPU],
+                                             uint32_t* buf, float* invs)
+{
+    const uint32_t gs = p.gslots;
+    const uint32_t nslots = ngr * gs;
+#pragma unroll
+    for (int s = 0; s < SPU; ++s)
+        buf[s * kWaveSize + lane] = mbits[s];
+    __builtin_amdgcn_wave_barrier();
+    // lanes per group, as a power of two: floor(log2(64 / ngr)), 0 when ngr > 64 (wave-uniform)
+    const uint32_t l_log2 = ngr > (uint32_t)kWaveSize ? 0u : 31u - (uint32_t)__builtin_clz((uint32_t)kWaveSize / ngr);
+    const uint32_t lpg = 1u << l_log2;
+    const uint32_t chunk = (gs + lpg - 1u) >> l_log2; // slots per lane
+    for (uint32_t base = 0; base < ngr; base += (uint32_t)kWaveSize >> l_log2) {
+        const uint32_t k = base + (lane >> l_log2);
+        const uint32_t sub = lane & (lpg - 1u);
+        uint32_t m = 0;
+        if (k < ngr) {
+            const uint32_t b = k * gs + sub * chunk;
+            const uint32_t e = min(b + chunk, (k + 1u) * gs);
+            for (uint32_t i = b; i < e; ++i)
+                m = max(m, buf[i]);
+        }
+        m = group_umax(m, l_log2);
+        if (k < ngr && sub == 0) {
+            float s32 = 0.0f;
+            uint32_t s8 = 0;
+            invs[k] = group_scale<FMT, SFMT>(m, s32, s8);
+            store_scale<SFMT>(p, row, g0 + k, s32, s8);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        const uint32_t rel = (uint32_t)s * kWaveSize + lane;
+        if (rel < nslots)
+            quantize_store<FMT>(row_codes, slot0 + rel, y[s], invs[__umulhi(rel, p.gmagic)]);
+    }
+}
+
+// The steps one wave holds for a segmented unit of up to SPU*64 slots, and the
+// size of the per-wave multiplier array (groups are at least 3 slots wide).
+template <int SPU>
+struct SegLds {
+    static constexpr int kSlots = SPU * kWaveSize;
+    static constexpr int kGroups = kSlots / 3 + 1;
+};
+
 // ---------------------------------------------------------------------------
 // Host helpers
 // ---------------------------------------------------------------------------
@@ -349,9 +415,17 @@ inline bool scale_spec(int scale_fmt, int64_t n, int64_t groups, ScaleSpec& sp)
 struct UnitPlan {
     bool rowred = false;
     bool partial = false;
+    bool seg = false;     // segmented units (quantize_seg)
+    bool twopass = false; // one wave per group, read twice: abs-max, then codes
     uint32_t spu_max = 1; // the kernel's compile-time steps per unit (per wave for split groups)
     uint32_t xwaves = 1;  // row-reduced groups: waves of one workgroup per group (1, 2 or 4)
 };
+
+// Segmented units hold whole groups of up to kMaxSegSlots lane slots (8192
+// columns, 16 steps of one wave); wider groups that the row-reduced kernels
+// do not cover take the two-pass kernels.
+constexpr uint32_t kMaxSegSlots = (uint32_t)(kMaxStepsPerUnit * kWaveSize);
+constexpr uint32_t kTwoPassSteps = 4; // steps per pass chunk of a two-pass group
 
 // A row-reduced group of k steps: one wave up to kMaxStepsPerUnit steps, else
 // split over 2 or 4 waves of one workgroup, each holding ceil(k / waves)
@@ -371,6 +445,17 @@ inline bool rowred_split(uint32_t k, uint32_t groups_row, uint32_t& waves, uint3
     return groups_row == 1 || k % waves == 0;
 }
 
+// One wave per group, the group read twice (abs-max, then codes), kTwoPassSteps
+// steps at a time: for groups no other plan covers.
+inline void plan_twopass(uint32_t gslots, uint32_t groups, Params& p, UnitPlan& plan)
+{
+    plan.twopass = true;
+    plan.spu_max = kTwoPassSteps;
+    p.gslots = gslots;
+    p.spu = kTwoPassSteps;
+    p.upr = groups;
+}
+
 inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint32_t spu_pref, Params& p,
                             UnitPlan& plan)
 {
@@ -378,15 +463,18 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
     const uint32_t slots = (uint32_t)(hidden / kSlotCols);
     const uint32_t steps_row = (slots + kWaveSize - 1) / kWaveSize;
     const uint32_t gslots = (uint32_t)(G / kSlotCols);
+    const uint32_t groups = (uint32_t)(hidden / G);
     if (G == hidden) {
         uint32_t waves = 1, spw = 1;
-        if (!rowred_split(steps_row, 1, waves, spw))
-            return TK_ERR_UNSUPPORTED;
-        plan.rowred = true;
-        plan.xwaves = waves;
-        p.spu = spw;
-        p.upr = waves;
-        plan.spu_max = template_steps(spw);
+        if (rowred_split(steps_row, 1, waves, spw)) {
+            plan.rowred = true;
+            plan.xwaves = waves;
+            p.spu = spw;
+            p.upr = waves;
+            plan.spu_max = template_steps(spw);
+        } else {
+            plan_twopass(gslots, 1, p, plan);
+        }
     } else if ((gslots & (gslots - 1)) == 0 && gslots <= (uint32_t)kWaveSize) {
         plan.rowred = false;
         p.gl_log2 = (uint32_t)__builtin_ctz(gslots);
@@ -398,24 +486,38 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
         p.upr = steps_row / spu;
     } else if (gslots % kWaveSize == 0) {
         const uint32_t k = gslots / kWaveSize;
-        const uint32_t groups = (uint32_t)(hidden / G);
         uint32_t waves = 1, spw = 1;
-        if (!rowred_split(k, groups, waves, spw))
-            return TK_ERR_UNSUPPORTED;
-        plan.rowred = true;
-        plan.xwaves = waves;
-        p.spu = spw;
-        p.upr = groups * waves;
-        plan.spu_max = template_steps(spw);
+        if (rowred_split(k, groups, waves, spw)) {
+            plan.rowred = true;
+            plan.xwaves = waves;
+            p.spu = spw;
+            p.upr = groups * waves;
+            plan.spu_max = template_steps(spw);
+        } else {
+            plan_twopass(gslots, groups, p, plan);
+        }
+    } else if (gslots <= kMaxSegSlots) {
+        // the smallest step count of 1, 2, 4, 8, 16 that holds one group and
+        // is at least spu_pref; as many whole groups per unit as fit
+        uint32_t spu = 1;
+        while (spu < (uint32_t)kMaxStepsPerUnit && (spu * kWaveSize < gslots || spu < spu_pref))
+            spu <<= 1;
+        plan.seg = true;
+        plan.spu_max = spu;
+        p.spu = spu;
+        p.gslots = gslots;
+        p.gpu = min(spu * (uint32_t)kWaveSize / gslots, groups);
+        p.upr = (groups + p.gpu - 1) / p.gpu;
+        p.gmagic = (uint32_t)(((1ull << 32) + gslots - 1) / gslots);
     } else {
-        return TK_ERR_UNSUPPORTED;
+        plan_twopass(gslots, groups, p, plan);
     }
     if ((uint64_t)n * p.upr >= (uint64_t)INT_MAX)
         return TK_ERR_UNSUPPORTED;
     p.slots = slots;
     p.steps_row = steps_row;
     p.units = (uint32_t)(n * p.upr);
-    p.groups_row = (uint32_t)(hidden / G);
+    p.groups_row = groups;
     plan.partial = (slots % kWaveSize) != 0;
     return TK_OK;
 }

@@ -522,6 +522,162 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
         flush_clamp_count(p.count, &wg_clamped, clamped, lane);
 }
 
+// A span of `nslots` lane slots of row `row` from slot `slot0` on: lane l of
+// step s holds slot slot0 + 64*s + l; lanes past the span re-read its last
+// slot and give abs-max bits 0 and no clamp count.  Loads run up to
+// kStreamDepth steps ahead of the arithmetic.  Used by the segmented and
+// two-pass kernels, whose spans start at any slot.
+template <bool CLAMP, int SPU, class CNT>
+__device__ __forceinline__ void span_compute(const Params& p, const LutT* lut, uint32_t lane, uint32_t row,
+                                             uint32_t slot0, uint32_t nslots, float w, float limit, float a_limit,
+                                             CNT& clamped, float (&y)[SPU][8], uint32_t (&mbits)[SPU])
+{
+    constexpr int D = SPU < kStreamDepth ? SPU : kStreamDepth;
+    const char* xg = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * 32u);
+    const char* xu = xg + p.slots * 16u;
+    const uint32_t last = slot0 + nslots - 1u;
+    auto off = [&](int s) { return min(slot0 + (uint32_t)s * kWaveSize + lane, last) * 16u; };
+    uint4 gq[D], uq[D];
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        gq[s] = load16(reinterpret_cast<const uint4*>(xg + off(s)));
+        uq[s] = load16(reinterpret_cast<const uint4*>(xu + off(s)));
+    }
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+        const uint4 g = gq[s % D], uu = uq[s % D];
+        if (s + D < SPU) {
+            gq[s % D] = load16(reinterpret_cast<const uint4*>(xg + off(s + D)));
+            uq[s % D] = load16(reinterpret_cast<const uint4*>(xu + off(s + D)));
+        }
+        mbits[s] = compute_step<CLAMP, true>(lut, g, uu, w, (uint32_t)s * kWaveSize + lane < nslots, limit, a_limit,
+                                             clamped, y[s]);
+    }
+}
+
+// A clamp counter that counts nothing (the second pass of a two-pass group).
+struct NoCount {
+    __device__ __forceinline__ void add(bool) {}
+};
+
+// Groups whose width is not a power of two of lane slots up to 64 and not a
+// multiple of 64, up to 8192 columns (24, 40, 48, 96, 384, 896 columns ...):
+// each unit is a run of whole groups of one row (p.gpu groups of p.gslots
+// slots) that one wave holds in SPU steps; the groups' abs-maxes are formed in
+// the wave's own LDS buffer (quantize_seg).  Persistent like the one-wave
+// kernel, with the sigmoid table in LDS.
+template <int FMT, int SFMT, bool CLAMP, int SPU>
+__global__ __launch_bounds__(kThreads) void swiglu_cast_seg_kernel(Params p)
+{
+    constexpr int kWaves = kThreads / kWaveSize;
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    __shared__ uint32_t seg_buf[kWaves][SegLds<SPU>::kSlots];
+    __shared__ float seg_inv[kWaves][SegLds<SPU>::kGroups];
+    __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
+    LutT* lut = reinterpret_cast<LutT*>(lut_raw);
+    if (CLAMP && threadIdx.x == 0)
+        wg_clamped = 0;
+    load_lut_to_lds(lut);
+
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    uint32_t block = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
+        block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(block * kWaves + wib);
+    const uint32_t nwaves = gridDim.x * kWaves;
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = p.clamp;
+        a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
+    }
+    LaneCount clamped;
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t g0 = (u - row * p.upr) * p.gpu;
+        const uint32_t ngr = min(p.gpu, p.groups_row - g0);
+        const uint32_t slot0 = g0 * p.gslots;
+        const float w = p.w ? p.w[row] : 1.0f;
+        float y[SPU][8];
+        uint32_t mbits[SPU];
+        span_compute<CLAMP, SPU>(p, lut, lane, row, slot0, ngr * p.gslots, w, limit, a_limit, clamped, y, mbits);
+        quantize_seg<FMT, SFMT, SPU>(p, lane, row, g0, ngr, slot0, y, mbits, seg_buf[wib], seg_inv[wib]);
+    }
+    if constexpr (CLAMP)
+        flush_clamp_count(p.count, &wg_clamped, clamped, lane);
+}
+
+// Groups no other kernel covers (wider than 8192 columns and not split evenly
+// over 2 or 4 waves, or wider than 32768 columns): one wave per group, which
+// reads the group twice, kTwoPassSteps steps at a time -- first for its
+// abs-max (and the clamp count), then again for the codes with the group's
+// scale.  The second read of a group is often still in the caches.
+template <int FMT, int SFMT, bool CLAMP>
+__global__ __launch_bounds__(kThreads) void swiglu_cast_2p_kernel(Params p)
+{
+    constexpr int S = kTwoPassSteps;
+    constexpr uint32_t kChunk = S * kWaveSize;
+    constexpr int kWaves = kThreads / kWaveSize;
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
+    LutT* lut = reinterpret_cast<LutT*>(lut_raw);
+    if (CLAMP && threadIdx.x == 0)
+        wg_clamped = 0;
+    load_lut_to_lds(lut);
+
+    const uint32_t lane = threadIdx.x & (kWaveSize - 1);
+    uint32_t block = blockIdx.x;
+    if ((gridDim.x & 7u) == 0)
+        block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(block * kWaves + (threadIdx.x / kWaveSize));
+    const uint32_t nwaves = gridDim.x * kWaves;
+    float limit = 0.0f, a_limit = 0.0f;
+    if constexpr (CLAMP) {
+        limit = p.clamp;
+        a_limit = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, limit * sigmoid_rn(limit))));
+    }
+    WaveCount clamped;
+    NoCount none;
+    const uint32_t gs = p.gslots;
+    for (uint32_t u = wave; u < p.units; u += nwaves) {
+        const uint32_t row = u / p.upr;
+        const uint32_t k = u - row * p.upr;
+        const uint32_t slot0 = k * gs;
+        const float w = p.w ? p.w[row] : 1.0f;
+        uint32_t mb = 0;
+        for (uint32_t c = 0; c < gs; c += kChunk) {
+            float y[S][8];
+            uint32_t mbits[S];
+            span_compute<CLAMP, S>(p, lut, lane, row, slot0 + c, min(kChunk, gs - c), w, limit, a_limit, clamped, y,
+                                   mbits);
+            mb = max(mb, lane_max<S>(mbits, S));
+        }
+        mb = wave_umax(mb);
+        float s32 = 0.0f;
+        uint32_t s8 = 0;
+        const float inv = group_scale<FMT, SFMT>(mb, s32, s8);
+        if (lane == 0)
+            store_scale<SFMT>(p, row, k, s32, s8);
+        uint8_t* row_codes = p.codes + (size_t)row * (FMT == 8 ? p.slots * 8u : p.slots * 4u);
+        for (uint32_t c = 0; c < gs; c += kChunk) {
+            float y[S][8];
+            uint32_t mbits[S];
+            span_compute<CLAMP, S>(p, lut, lane, row, slot0 + c, min(kChunk, gs - c), w, limit, a_limit, none, y,
+                                   mbits);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t rel = c + (uint32_t)s * kWaveSize + lane;
+                if (rel < gs)
+                    quantize_store<FMT>(row_codes, slot0 + rel, y[s], inv);
+            }
+        }
+    }
+    if constexpr (CLAMP)
+        flush_clamp_count(p.count, &wg_clamped, clamped, lane);
+}
+
 // The unfused first stage (swiglu_forward): fp32 y [n][hidden], same
 // per-element arithmetic as the fused kernel.  Thread t of the grid-stride
 // loop owns one 8-column lane slot of one row.
@@ -711,6 +867,44 @@ bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, cons
 }
 
 
+template <int FMT, int SFMT, bool CLAMP>
+bool launch_seg(uint32_t spu_max, const Params& p, int blocks, hipStream_t s)
+{
+    switch (spu_max) {
+#define TK_SEG(N)                                                                                              \
+    case N:                                                                                                    \
+        hipLaunchKernelGGL((swiglu_cast_seg_kernel<FMT, SFMT, CLAMP, N>), dim3(blocks), dim3(kThreads), 0, s, p); \
+        return true;
+        TK_SEG(1)
+        TK_SEG(2)
+        TK_SEG(4)
+        TK_SEG(8)
+        TK_SEG(16)
+#undef TK_SEG
+    default: return false;
+    }
+}
+
+template <int FMT>
+bool dispatch_seg(int sfmt, bool clamp, bool twopass, uint32_t spu_max, const Params& p, int blocks, hipStream_t s)
+{
+    if (twopass) {
+#define TK_2P(SF, CL) hipLaunchKernelGGL((swiglu_cast_2p_kernel<FMT, SF, CL>), dim3(blocks), dim3(kThreads), 0, s, p)
+        if (sfmt == TK_SCALE_FP32) {
+            if (clamp) TK_2P(TK_SCALE_FP32, true); else TK_2P(TK_SCALE_FP32, false);
+        } else {
+            if (clamp) TK_2P(TK_SCALE_UE8M0, true); else TK_2P(TK_SCALE_UE8M0, false);
+        }
+#undef TK_2P
+        return true;
+    }
+    if (sfmt == TK_SCALE_FP32)
+        return clamp ? launch_seg<FMT, TK_SCALE_FP32, true>(spu_max, p, blocks, s)
+                     : launch_seg<FMT, TK_SCALE_FP32, false>(spu_max, p, blocks, s);
+    return clamp ? launch_seg<FMT, TK_SCALE_UE8M0, true>(spu_max, p, blocks, s)
+                 : launch_seg<FMT, TK_SCALE_UE8M0, false>(spu_max, p, blocks, s);
+}
+
 // Persistent grid: workgroups of 256 threads per CU.  Two measured best for
 // large launches; launches of at most kSmallUnitsPerCU units per CU take four,
 // so that each wave has at most four units to work through (a headline-shaped
@@ -793,7 +987,10 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool ok;
-    if (plan.xwaves > 1)
+    if (plan.seg || plan.twopass)
+        ok = fmt == 8 ? dispatch_seg<8>(sp.kind, clamp, plan.twopass, plan.spu_max, p, blocks, s)
+                      : dispatch_seg<4>(sp.kind, clamp, plan.twopass, plan.spu_max, p, blocks, s);
+    else if (plan.xwaves > 1)
         ok = fmt == 8 ? dispatch_xw<8>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s)
                       : dispatch_xw<4>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s);
     else

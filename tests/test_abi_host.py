@@ -89,34 +89,29 @@ def test_ue8m0_scales_need_no_alignment_and_n0_is_a_noop():
 
 
 @pytest.mark.parametrize("kw", [
-    dict(hidden=48, group_size=24),        # 3 lane slots per group: not a power of two
-    dict(hidden=1536, group_size=768),     # 96 slots: neither <= 64 and a power of two, nor a multiple of 64
-    dict(hidden=32776, group_size=0),      # per-token group longer than 32768 columns
+    dict(hidden=48, group_size=24),        # 3 lane slots per group: segmented units
+    dict(hidden=1536, group_size=768),     # 96 slots: segmented
+    dict(hidden=7168, group_size=896),     # 112 slots: segmented, a group straddles steps
+    dict(hidden=9600, group_size=4800),    # 600 slots: segmented, 16 steps per unit
+    dict(hidden=17600, group_size=8800),   # 1100 slots, not whole steps: two-pass
+    dict(hidden=32776, group_size=0),      # per-token group longer than 32768 columns: two-pass
     dict(hidden=40960, group_size=40960),
-    dict(hidden=17408, group_size=8704),   # two groups of 17 steps: odd
-    dict(hidden=34816, group_size=17408),  # two groups of 34 steps: not a multiple of 4
-], ids=str)
-def test_unsupported_shapes(kw):
-    assert cast8(**kw) == UNSUPPORTED
-    assert cast8(n=0, **kw) == UNSUPPORTED
-
-
-@pytest.mark.parametrize("kw", [
+    dict(hidden=17408, group_size=8704),   # two groups of 17 steps (odd): two-pass
+    dict(hidden=34816, group_size=17408),  # two groups of 34 steps (not a multiple of 4): two-pass
     dict(hidden=8200, group_size=0),       # 17 steps: two waves
     dict(hidden=32768, group_size=0),      # 64 steps: four waves
     dict(hidden=16384, group_size=16384),
     dict(hidden=17408, group_size=17408),  # one group of 34 steps: four waves, the last short
     dict(hidden=36864, group_size=18432),  # two groups of 36 steps
     dict(hidden=32768, group_size=16384),  # two groups of 32 steps
-    dict(hidden=17408, group_size=8704) | dict(hidden=34816),  # four groups of 17 steps: odd
 ], ids=str)
-def test_long_groups_pass_validation(kw):
-    # groups beyond 8192 columns are planned over several waves; with n == 0
-    # the call returns after planning, before any HIP call
-    expect = UNSUPPORTED if kw["group_size"] == 8704 else OK
-    assert cast8(n=0, **kw) == expect
-    assert cast4(n=0, **kw) == expect
-    assert cast_only(tk.tk_cast_fp8, n=0, **kw) == expect
+def test_every_valid_group_is_planned(kw):
+    # every group width that is a multiple of 8 dividing hidden has a kernel;
+    # with n == 0 the call returns after planning, before any HIP call
+    assert cast8(n=0, **kw) == OK
+    assert cast4(n=0, **kw) == OK
+    assert cast_only(tk.tk_cast_fp8, n=0, **kw) == OK
+    assert cast_only(tk.tk_cast_fp4, n=0, **kw) == OK
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(hidden=4), dict(y=None), dict(y=X + 4), dict(y=X),
@@ -151,9 +146,9 @@ def test_cast_invalid_arguments(kw):
     assert cast_only(tk.tk_cast_fp4, **kw) == INVALID
 
 
-def test_cast_unsupported_and_empty():
-    assert cast_only(tk.tk_cast_fp8, hidden=48, group_size=24) == UNSUPPORTED
-    assert cast_only(tk.tk_cast_fp8, hidden=32776, group_size=0) == UNSUPPORTED
+def test_cast_empty():
+    assert cast_only(tk.tk_cast_fp8, n=0, hidden=48, group_size=24) == OK
+    assert cast_only(tk.tk_cast_fp8, n=0, hidden=32776, group_size=0) == OK
     assert cast_only(tk.tk_cast_fp8, n=0, hidden=8200, group_size=0) == OK
     assert cast_only(tk.tk_cast_fp8, n=0) == OK
     assert cast_only(tk.tk_cast_fp4, n=0, x=None, codes=None, scales=None) == OK

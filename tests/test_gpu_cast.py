@@ -52,6 +52,9 @@ def same(got, want, what):
 CASES = [  # (hidden, group, fmt, scale_fmt)
     (2048, 128, 8, 1), (2048, 0, 8, 0), (4096, 32, 4, 1), (7168, 128, 8, 0), (1000, 8, 4, 0), (1000, 0, 8, 1),
     (2048, 1024, 4, 1), (64, 32, 8, 0), (8192, 0, 4, 0), (6144, 0, 8, 1), (5000, 0, 4, 0),
+    # groups that straddle lanes and steps (segmented units) and groups read twice (two-pass)
+    (1944, 24, 8, 1), (1944, 24, 4, 0), (2040, 40, 4, 1), (2976, 96, 8, 0), (7168, 896, 8, 1), (7168, 896, 4, 0),
+    (9600, 4800, 8, 0), (17600, 8800, 4, 1), (17408, 8704, 8, 1), (32776, 0, 8, 0), (40960, 0, 4, 1),
 ]
 
 

@@ -264,47 +264,59 @@ SHAPES = [  # (hidden, group, fmt, scale_fmt, clamp, weighted)
 ]
 
 
-def planned(hidden, group):
-    """Whether the library covers (hidden, group): groups of 2^j <= 64 lane
-    slots, or of k whole 512-column steps with k <= 64 (k > 16 split over 2 or
-    4 waves, several groups in a row only when k divides evenly)."""
-    slots, G = hidden // 8, group or hidden
-    gslots = G // 8
-    if group and (gslots & (gslots - 1)) == 0 and gslots <= 64:
-        return True
-    if group == 0:
-        k = (slots + 63) // 64
-        return k <= 64
-    if gslots % 64:
-        return False
-    k = gslots // 64
-    waves = 1 if k <= 16 else 2 if k <= 32 else 4
-    return k <= 64 and (hidden == G or k % waves == 0)
-
-
 @pytest.mark.parametrize("shape", SHAPES, ids=str)
 def test_shapes_groups_and_formats(shape):
     hidden, group, fmt, sfmt, clamp, weighted = shape
-    supported = planned(hidden, group)
     base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
     rows = 67
     say("shape", shape)
-    full = wl.make_x(base, 4, rows=range(rows))
-    x = np.concatenate([full[:, :hidden], full[:, 2048:2048 + hidden]], axis=1) if hidden <= 2048 else \
-        np.tile(full, (1, (2 * hidden + 4095) // 4096))[:, :2 * hidden]
-    x = np.ascontiguousarray(x)
+    x = rows_of_width(base, 4, rows, hidden)
     wt = wl.make_w(base, 4)[:rows] if weighted else None
-    if not supported:
-        n = x.shape[0]
-        out = Out(n, hidden, group, fmt, sfmt)
-        fn = tk.tk_swiglu_cast_fp8 if fmt == 8 else tk.tk_swiglu_cast_fp4
-        xd = torch.from_numpy(x.view(np.int16)).to(DEV)
-        rc = fn(xd, None, n, hidden, group, math.inf, sfmt, out.codes_ptr, out.scales_ptr, None, None)
-        assert rc == tk.TkStatus.TK_ERR_UNSUPPORTED
-        return
     got = run_cast(x, wt, hidden, group, clamp, fmt, sfmt)
     want = oracle.swiglu_cast(x, wt, group, clamp, fmt, sfmt)
     assert_same(got, want, str(shape))
+
+
+def rows_of_width(base, seed, rows, hidden):
+    """`rows` packed [gate | up] rows of the given width cut from (or tiled
+    out of) a workload's rows."""
+    full = wl.make_x(base, seed, rows=range(rows))
+    x = np.concatenate([full[:, :hidden], full[:, 2048:2048 + hidden]], axis=1) if hidden <= 2048 else \
+        np.tile(full, (1, (2 * hidden + 4095) // 4096))[:, :2 * hidden]
+    return np.ascontiguousarray(x)
+
+
+# Group widths that are neither a power of two of 8-column lane slots up to 64
+# slots nor a multiple of 512 columns (segmented units: a group straddles
+# lanes and steps at any offset), and groups no one-wave or multi-wave unit
+# holds (two-pass: wider than 8192 columns and not whole 512-column steps,
+# several 17- or 34-step groups in a row, a row longer than 32768 columns).
+ANY_GROUP = [  # (hidden, group, rows)
+    (1944, 24, 67), (1944, 24, 1100), (2040, 40, 67), (1536, 48, 300), (2976, 96, 67), (2976, 96, 1100),
+    (3840, 192, 67), (2688, 384, 67), (4608, 1536, 67), (7168, 896, 67), (7168, 896, 1100), (7168, 56, 300),
+    (7168, 1792, 67), (9600, 4800, 40), (4104, 1368, 67), (2400, 24, 33),
+    (17600, 8800, 20), (17408, 8704, 20), (34816, 17408, 10), (32776, 0, 12), (40960, 40960, 6),
+]
+
+
+@pytest.mark.parametrize("clamp", [None, 10.0], ids=["noclamp", "clamp10"])
+@pytest.mark.parametrize("fmt,sfmt", [(8, 0), (8, 1), (4, 0), (4, 1)], ids=["e4m3-fp32", "e4m3-ue8m0", "e2m1-fp32",
+                                                                           "e2m1-ue8m0"])
+@pytest.mark.parametrize("case", ANY_GROUP, ids=str)
+def test_any_group_width(case, fmt, sfmt, clamp):
+    """Every group width the ABI calls valid, both formats and scale kinds,
+    with and without the clamp: every code, scale and clamp count against the
+    oracle (per-block quantisation splits hidden into blocks of any width:
+    "TileLang + TileKernels" "3. Quantization")."""
+    hidden, group, rows = case
+    if clamp is not None and rows > 100:
+        rows = 100
+    say("any group", case, fmt, sfmt, clamp)
+    base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    x = rows_of_width(base, 6, rows, hidden)
+    wt = wl.make_w(base, 6)[:rows]
+    got = run_cast(x, wt, hidden, group, clamp, fmt, sfmt)
+    assert_same(got, oracle.swiglu_cast(x, wt, group, clamp, fmt, sfmt), f"{case} {fmt} {sfmt} {clamp}")
 
 
 def test_batch_invariance_and_pointer_offsets():
