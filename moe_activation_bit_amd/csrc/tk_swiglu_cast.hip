@@ -65,6 +65,13 @@ constexpr int kLutSize = 4096;
 static_assert(kLutLast - kLutFirst + 1 == kLutSize, "table span");
 
 __device__ float2 g_sigma_lut[kLutSize];
+// The same sigmoids in 16 KiB, for small launches (where filling and reading
+// the table is a fifth of the launch): per magnitude sigma(-|g|), which lies in
+// (0, 0.5] so its two top bits are 0, and in those two bits 1 + the difference
+// in ulps between sigma(+|g|) and RN(1 - sigma(-|g|)).  That difference is -1,
+// 0 or +1 for every tabulated magnitude, so sigma(+|g|) is recovered exactly
+// from one subtraction and one integer add.
+__device__ uint32_t g_sigma_lut16[kLutSize];
 
 // ---------------------------------------------------------------------------
 // Correctly rounded fp32 sigmoid for table set-up and for the clamp limit.
@@ -120,7 +127,10 @@ __global__ void sigma_lut_init_kernel()
     if (i >= kLutSize)
         return;
     const float g = as_float((kLutFirst + (uint32_t)i) << 16);
-    g_sigma_lut[i] = make_float2(sigmoid_rn(g), sigmoid_rn(-g));
+    const float sp = sigmoid_rn(g), sn = sigmoid_rn(-g);
+    g_sigma_lut[i] = make_float2(sp, sn);
+    const int corr = (int)(as_uint(sp) - as_uint(1.0f - sn));
+    g_sigma_lut16[i] = as_uint(sn) | ((uint32_t)(corr + 1) << 30);
 }
 
 // ---------------------------------------------------------------------------
@@ -155,7 +165,20 @@ __device__ __forceinline__ float lut_sigma(const float2* lut, uint32_t word, uin
     return ((int32_t)gbits < 0) ? pr.y : pr.x;
 }
 
+// The 16 KiB form of the same lookup (g_sigma_lut16's layout).
+template <int POS>
+__device__ __forceinline__ float lut16_sigma(const uint32_t* lut, uint32_t word, uint32_t gbits)
+{
+    const uint32_t m = __builtin_amdgcn_ubfe(word, POS, 15);
+    const uint32_t c = min(max(m, kLutFirst), kLutLast) - kLutFirst;
+    const uint32_t e = lut[c];
+    const float sn = as_float(e & 0x3FFFFFFFu);
+    const float sp = as_float(as_uint(1.0f - sn) + (e >> 30) - 1u);
+    return ((int32_t)gbits < 0) ? sn : sp;
+}
+
 constexpr int kLutLdsBytes = kLutSize * 8;
+constexpr int kLut16LdsBytes = kLutSize * 4;
 
 // Clamp counters: a wave's count of gates above the limit.  WaveCount keeps
 // the wave's total in scalar registers (a ballot and popcount per element);
@@ -209,14 +232,15 @@ __device__ __forceinline__ void flush_clamp_count(unsigned long long* count, uns
 // a = RN(g * sigma(g)) (or the clamped gate's activation), b = RN(a * u),
 // y = RN(b * w); three fp32 products, never fused.  `counts` is false on lanes
 // past the end of the row, whose gates must not enter the clamp count.
-template <int POS, bool CLAMP, class CNT>
+template <int POS, bool CLAMP, class CNT, bool T16 = false>
 __device__ __forceinline__ float swiglu_elem(const LutT* lut, uint32_t gword, uint32_t uword, float w,
                                              float limit, float a_limit, CNT& clamped, bool counts = true)
 {
     const uint32_t gbits = POS ? (gword & 0xFFFF0000u) : (gword << 16);
     float u = as_float(POS ? (uword & 0xFFFF0000u) : (uword << 16));
     const float g = as_float(gbits);
-    float a = g * lut_sigma<POS>(lut, gword, gbits);
+    float a = g * (T16 ? lut16_sigma<POS>(reinterpret_cast<const uint32_t*>(lut), gword, gbits)
+                       : lut_sigma<POS>(lut, gword, gbits));
     if constexpr (CLAMP) {
         clamped.add(g > limit && counts);
         // The clamped gate's activation, RN(min(g, L) * sigma(min(g, L))), is
@@ -266,7 +290,7 @@ __device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t 
 
 // One 8-column step of a loaded unit: ys = w * silu(gate) * up for the lane's
 // columns; returns the lane's abs-max bits (0 for a lane past the row end).
-template <bool CLAMP, bool PARTIAL, class CNT>
+template <bool CLAMP, bool PARTIAL, class CNT, bool T16 = false>
 __device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4 u, float w, bool valid, float limit,
                                                  float a_limit, CNT& clamped, float (&ys)[8])
 {
@@ -275,8 +299,8 @@ __device__ __forceinline__ uint32_t compute_step(const LutT* lut, uint4 g, uint4
     float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        ys[2 * k] = swiglu_elem<0, CLAMP>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
-        ys[2 * k + 1] = swiglu_elem<16, CLAMP>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
+        ys[2 * k] = swiglu_elem<0, CLAMP, CNT, T16>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
+        ys[2 * k + 1] = swiglu_elem<16, CLAMP, CNT, T16>(lut, gw[k], uw[k], w, limit, a_limit, clamped, valid);
         m = fmaxf(m, fmaxf(fabsf(ys[2 * k]), fabsf(ys[2 * k + 1])));
     }
     if (PARTIAL && !valid)
@@ -349,7 +373,7 @@ __device__ __forceinline__ void stream_unit(const Params& p, const LutT* lut, ui
     }
 }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE, class CNT>
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE, bool T16, class CNT>
 __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, uint32_t lane, const Unit<SPU>& d,
                                              float limit, float a_limit, CNT& clamped)
 {
@@ -358,7 +382,7 @@ __device__ __forceinline__ void process_unit(const Params& p, const LutT* lut, u
 #pragma unroll
     for (int s = 0; s < SPU; ++s)
         if (!ROWRED || s < (int)d.nst)
-            mbits[s] = compute_step<CLAMP, PARTIAL>(lut, d.g[s], d.u[s], d.w,
+            mbits[s] = compute_step<CLAMP, PARTIAL, CNT, T16>(lut, d.g[s], d.u[s], d.w,
                                                     !PARTIAL || (d.step0 + s) * kWaveSize + lane < p.slots, limit,
                                                     a_limit, clamped, y[s]);
     quantize_unit<FMT, SFMT, SPU, ROWRED, PARTIAL, WIDE>(p, lane, d.row, d.unit_in_row, d.step0, d.nst, y, mbits);
@@ -392,10 +416,16 @@ __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut,
         flush_clamp_count(p.count, wg_clamped, clamped, lane);
 }
 
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false>
+// T16: the 16 KiB form of the table (small launches: half the fill and a
+// 4-byte read per lookup, for four more VALU operations per element; interleaved
+// A/B, bit-identical: 349 x 7168 ragged 5.56 -> 5.24 us replayed from a graph,
+// 1000 x 7168 9.70 -> 9.03, 2400 x 2048 per-block 8.22 -> 7.98; on the large
+// launches it cost 1-3%).
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false, bool T16 = false>
 __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kLutLdsBytes];
+    constexpr int kTableBytes = T16 ? kLut16LdsBytes : kLutLdsBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char lut_raw[kTableBytes];
     __shared__ unsigned long long wg_clamped; // the workgroup's clamp count
     LutT* lut = reinterpret_cast<LutT*>(lut_raw);
 
@@ -414,6 +444,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(block * waves_per_block + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * waves_per_block;
     if constexpr (ROWRED && SPU >= kStreamMinSteps) {
+        static_assert(!T16, "the streamed loop reads the 32 KiB table");
         streamed_rowred_loop<FMT, SFMT, CLAMP, SPU, PARTIAL>(p, lut, &wg_clamped, lane, wave, nwaves);
         return;
     }
@@ -422,12 +453,13 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     // behind them; loads return in order, so the table reaches LDS without
     // waiting for the unit, and the unit's latency overlaps the table fill
     // (what a launch of a few hundred rows spends most of its time on).
-    constexpr int kLutPerThread = kLutLdsBytes / 16 / kThreads;
-    static_assert(kLutPerThread * 16 * kThreads == kLutLdsBytes, "table split");
+    constexpr int kLutPerThread = kTableBytes / 16 / kThreads;
+    static_assert(kLutPerThread * 16 * kThreads == kTableBytes, "table split");
+    const uint4* table = T16 ? reinterpret_cast<const uint4*>(g_sigma_lut16) : reinterpret_cast<const uint4*>(g_sigma_lut);
     uint4 lut_part[kLutPerThread];
 #pragma unroll
     for (int i = 0; i < kLutPerThread; ++i)
-        lut_part[i] = reinterpret_cast<const uint4*>(g_sigma_lut)[i * kThreads + threadIdx.x];
+        lut_part[i] = table[i * kThreads + threadIdx.x];
     if (CLAMP && threadIdx.x == 0)
         wg_clamped = 0;
     Unit<SPU> first;
@@ -447,11 +479,11 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     std::conditional_t<ROWRED, WaveCount, LaneCount> clamped;
 
     if (wave < p.units)
-        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE>(p, lut, lane, first, limit, a_limit, clamped);
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE, T16>(p, lut, lane, first, limit, a_limit, clamped);
     for (uint32_t u = wave + nwaves; u < p.units; u += nwaves) {
         Unit<SPU> d;
         load_unit<SPU, ROWRED, PARTIAL>(p, u, lane, d);
-        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE>(p, lut, lane, d, limit, a_limit, clamped);
+        process_unit<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, WIDE, T16>(p, lut, lane, d, limit, a_limit, clamped);
     }
 
     if constexpr (CLAMP)
@@ -778,12 +810,27 @@ tk_status init_device(int dev)
 
 tk_status ensure_device(int& dev);
 
+// small: a launch of at most kSmallUnitsPerCU units per CU, which takes the
+// 16 KiB table (units of up to 4 steps; longer row-reduced units stream their
+// loads and keep the 32 KiB table).
 template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
-void launch_one(const Params& p, int blocks, hipStream_t stream)
+void launch_one(const Params& p, int blocks, bool small, hipStream_t stream)
 {
+    constexpr bool kCanT16 = !(ROWRED && SPU >= kStreamMinSteps);
     if constexpr (!ROWRED) {
         if (p.gl_log2 >= 5) { // per-block groups of 32 or 64 lanes
-            hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true>), dim3(blocks),
+            if (small)
+                hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true, true>),
+                                   dim3(blocks), dim3(kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true>), dim3(blocks),
+                                   dim3(kThreads), 0, stream, p);
+            return;
+        }
+    }
+    if constexpr (kCanT16) {
+        if (small) {
+            hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, false, true>), dim3(blocks),
                                dim3(kThreads), 0, stream, p);
             return;
         }
@@ -793,20 +840,20 @@ void launch_one(const Params& p, int blocks, hipStream_t stream)
 }
 
 template <int FMT, int SFMT, bool CLAMP, bool ROWRED, bool PARTIAL>
-bool launch_spu(int spu_max, const Params& p, int blocks, hipStream_t stream)
+bool launch_spu(int spu_max, const Params& p, int blocks, bool small, hipStream_t stream)
 {
     switch (spu_max) {
-    case 1: launch_one<FMT, SFMT, CLAMP, 1, ROWRED, PARTIAL>(p, blocks, stream); return true;
-    case 2: launch_one<FMT, SFMT, CLAMP, 2, ROWRED, PARTIAL>(p, blocks, stream); return true;
-    case 4: launch_one<FMT, SFMT, CLAMP, 4, ROWRED, PARTIAL>(p, blocks, stream); return true;
+    case 1: launch_one<FMT, SFMT, CLAMP, 1, ROWRED, PARTIAL>(p, blocks, small, stream); return true;
+    case 2: launch_one<FMT, SFMT, CLAMP, 2, ROWRED, PARTIAL>(p, blocks, small, stream); return true;
+    case 4: launch_one<FMT, SFMT, CLAMP, 4, ROWRED, PARTIAL>(p, blocks, small, stream); return true;
     case 8:
-        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 8, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 8, ROWRED, PARTIAL>(p, blocks, small, stream); return true; }
         return false;
     case 12:
-        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 12, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 12, ROWRED, PARTIAL>(p, blocks, small, stream); return true; }
         return false;
     case 16:
-        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 16, ROWRED, PARTIAL>(p, blocks, stream); return true; }
+        if constexpr (ROWRED) { launch_one<FMT, SFMT, CLAMP, 16, ROWRED, PARTIAL>(p, blocks, small, stream); return true; }
         return false;
     default: return false;
     }
@@ -846,12 +893,12 @@ bool dispatch_xw(int sfmt, bool clamp, bool partial, uint32_t waves, uint32_t sp
 }
 
 template <int FMT>
-bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, const Params& p, int blocks,
+bool dispatch(int sfmt, bool clamp, bool rowred, bool partial, int spu_max, const Params& p, int blocks, bool small,
               hipStream_t s)
 {
 #define TK_BRANCH(SF, CL, RR, PA)                                                                       \
     if (sfmt == SF && clamp == CL && rowred == RR && partial == PA)                                     \
-        return launch_spu<FMT, SF, CL, RR, PA>(spu_max, p, blocks, s);
+        return launch_spu<FMT, SF, CL, RR, PA>(spu_max, p, blocks, small, s);
 #define TK_BRANCH2(SF, CL, RR) TK_BRANCH(SF, CL, RR, false) TK_BRANCH(SF, CL, RR, true)
     TK_BRANCH2(TK_SCALE_FP32, false, false)
     TK_BRANCH2(TK_SCALE_FP32, false, true)
@@ -981,7 +1028,8 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     // one unit per wave (a group of xwaves units per xwaves waves) when the grid is not capped
     const uint32_t want = (p.units + waves_per_block - 1) / waves_per_block;
     const uint32_t cus = (uint32_t)g_dev[dev].cus;
-    const uint32_t per_cu = (uint64_t)p.units <= (uint64_t)cus * kSmallUnitsPerCU ? kBlocksPerCUSmall : kBlocksPerCU;
+    const bool small = (uint64_t)p.units <= (uint64_t)cus * kSmallUnitsPerCU;
+    const uint32_t per_cu = small ? kBlocksPerCUSmall : kBlocksPerCU;
     const uint32_t cap = cus * per_cu;
     const int blocks = (int)(want < cap ? want : cap);
 
@@ -994,8 +1042,8 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
         ok = fmt == 8 ? dispatch_xw<8>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s)
                       : dispatch_xw<4>(sp.kind, clamp, plan.partial, plan.xwaves, plan.spu_max, p, blocks, s);
     else
-        ok = fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s)
-                      : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, s);
+        ok = fmt == 8 ? dispatch<8>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, small, s)
+                      : dispatch<4>(sp.kind, clamp, plan.rowred, plan.partial, (int)plan.spu_max, p, blocks, small, s);
     if (!ok)
         return TK_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess)

@@ -140,6 +140,26 @@ def test_activation_every_bf16_gate(clamp):
     assert cnt == co
 
 
+def test_small_launch_every_bf16_gate():
+    """Small launches read the 16 KiB form of the sigmoid table.  Every bf16
+    gate pattern (non-finite ones replaced by 0) sits alone in a group of 8
+    columns, up and weight 1, so each group's fp32 scale is RN(|y|/448) of one
+    y = RN(g*sigma(g)): codes and scales against the oracle, both formats."""
+    say("small launch, every bf16 gate alone in its group")
+    hidden, rows = 4096, 128
+    pat = np.arange(65536, dtype=np.uint32)
+    finite = np.isfinite((pat << 16).view(np.float32))
+    pat = np.where(finite, pat, 0).astype(np.uint16)
+    gate = np.zeros((rows, hidden), dtype=np.uint16)
+    r = np.arange(rows)[:, None]
+    grp = np.arange(hidden // 8)[None, :]
+    gate[r, grp * 8 + (r % 8)] = pat.reshape(rows, hidden // 8)
+    x = np.concatenate([gate, np.full_like(gate, 0x3F80)], axis=1)
+    for fmt in (8, 4):
+        got = run_cast(x, None, hidden, 8, None, fmt, tk.TK_SCALE_FP32)
+        assert_same(got, oracle.swiglu_cast(x, None, 8, None, fmt, 0), f"every gate, fmt {fmt}")
+
+
 def test_swiglu_forward_workload_rows():
     w = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
     say("swiglu_forward 331 rows", w.name)
