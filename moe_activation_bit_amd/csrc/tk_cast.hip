@@ -151,8 +151,10 @@ __global__ __launch_bounds__(kThreads) void cast_xw_kernel(Params p)
 // fp32: lane l of step s holds slot slot0 + 64*s + l; lanes past the span
 // re-read its last slot and give abs-max bits 0.  Loads run up to four steps
 // ahead of the widening.  Used by the segmented and two-pass kernels, whose
-// spans start at any slot.
-template <bool F32IN, int SPU>
+// spans start at any slot.  NT: non-temporal loads (data read once); a
+// two-pass group's first read leaves NT off so that its second read finds
+// the data in the caches.
+template <bool F32IN, int SPU, bool NT = true>
 __device__ __forceinline__ void cast_span_load(const Params& p, uint32_t lane, uint32_t row, uint32_t slot0,
                                                uint32_t nslots, float (&y)[SPU][8], uint32_t (&mbits)[SPU])
 {
@@ -162,12 +164,13 @@ __device__ __forceinline__ void cast_span_load(const Params& p, uint32_t lane, u
     const char* xr = reinterpret_cast<const char*>(p.x) + (size_t)row * (p.slots * kSlotBytes);
     const uint32_t last = slot0 + nslots - 1u;
     auto off = [&](int s) { return min(slot0 + (uint32_t)s * kWaveSize + lane, last) * kSlotBytes; };
+    auto ld = [](const char* a) { return NT ? load16(reinterpret_cast<const uint4*>(a)) : *reinterpret_cast<const uint4*>(a); };
     uint4 q[D][P];
 #pragma unroll
     for (int s = 0; s < D; ++s)
 #pragma unroll
         for (int h = 0; h < P; ++h)
-            q[s][h] = load16(reinterpret_cast<const uint4*>(xr + off(s) + 16u * h));
+            q[s][h] = ld(xr + off(s) + 16u * h);
 #pragma unroll
     for (int s = 0; s < SPU; ++s) {
         uint4 cur[P];
@@ -177,7 +180,7 @@ __device__ __forceinline__ void cast_span_load(const Params& p, uint32_t lane, u
         if (s + D < SPU) {
 #pragma unroll
             for (int h = 0; h < P; ++h)
-                q[s % D][h] = load16(reinterpret_cast<const uint4*>(xr + off(s + D) + 16u * h));
+                q[s % D][h] = ld(xr + off(s + D) + 16u * h);
         }
         if constexpr (F32IN) {
             const uint32_t w[8] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w,
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void cast_2p_kernel(Params p)
         for (uint32_t c = 0; c < gs; c += kChunk) {
             float y[S][8];
             uint32_t mbits[S];
-            cast_span_load<F32IN, S>(p, lane, row, slot0 + c, min(kChunk, gs - c), y, mbits);
+            cast_span_load<F32IN, S, false>(p, lane, row, slot0 + c, min(kChunk, gs - c), y, mbits);
             mb = max(mb, lane_max<S>(mbits, S));
         }
         mb = wave_umax(mb);
@@ -291,6 +294,7 @@ bool launch_cast_seg(const UnitPlan& plan, const Params& p, int blocks, hipStrea
         TK_CAST_SEG(2)
         TK_CAST_SEG(4)
         TK_CAST_SEG(8)
+        TK_CAST_SEG(12)
         TK_CAST_SEG(16)
 #undef TK_CAST_SEG
     default: return false;

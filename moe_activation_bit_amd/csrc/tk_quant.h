@@ -497,11 +497,11 @@ inline tk_status plan_units(int64_t n, int64_t hidden, int64_t group_size, uint3
             plan_twopass(gslots, groups, p, plan);
         }
     } else if (gslots <= kMaxSegSlots) {
-        // the smallest step count of 1, 2, 4, 8, 16 that holds one group and
-        // is at least spu_pref; as many whole groups per unit as fit
+        // the smallest step count of 1, 2, 4, 8, 12, 16 that holds one group
+        // and is at least spu_pref; as many whole groups per unit as fit
         uint32_t spu = 1;
         while (spu < (uint32_t)kMaxStepsPerUnit && (spu * kWaveSize < gslots || spu < spu_pref))
-            spu <<= 1;
+            spu = spu == 8 ? 12u : spu == 12 ? 16u : spu << 1;
         plan.seg = true;
         plan.spu_max = spu;
         p.spu = spu;

@@ -558,8 +558,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
 // step s holds slot slot0 + 64*s + l; lanes past the span re-read its last
 // slot and give abs-max bits 0 and no clamp count.  Loads run up to
 // kStreamDepth steps ahead of the arithmetic.  Used by the segmented and
-// two-pass kernels, whose spans start at any slot.
-template <bool CLAMP, int SPU, class CNT>
+// two-pass kernels, whose spans start at any slot.  NT: non-temporal loads
+// (data read once); a two-pass group's first read leaves NT off so that its
+// second read finds the data in the caches.
+template <bool CLAMP, int SPU, class CNT, bool NT = true>
 __device__ __forceinline__ void span_compute(const Params& p, const LutT* lut, uint32_t lane, uint32_t row,
                                              uint32_t slot0, uint32_t nslots, float w, float limit, float a_limit,
                                              CNT& clamped, float (&y)[SPU][8], uint32_t (&mbits)[SPU])
@@ -569,18 +571,19 @@ __device__ __forceinline__ void span_compute(const Params& p, const LutT* lut, u
     const char* xu = xg + p.slots * 16u;
     const uint32_t last = slot0 + nslots - 1u;
     auto off = [&](int s) { return min(slot0 + (uint32_t)s * kWaveSize + lane, last) * 16u; };
+    auto ld = [](const char* a) { return NT ? load16(reinterpret_cast<const uint4*>(a)) : *reinterpret_cast<const uint4*>(a); };
     uint4 gq[D], uq[D];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-        gq[s] = load16(reinterpret_cast<const uint4*>(xg + off(s)));
-        uq[s] = load16(reinterpret_cast<const uint4*>(xu + off(s)));
+        gq[s] = ld(xg + off(s));
+        uq[s] = ld(xu + off(s));
     }
 #pragma unroll
     for (int s = 0; s < SPU; ++s) {
         const uint4 g = gq[s % D], uu = uq[s % D];
         if (s + D < SPU) {
-            gq[s % D] = load16(reinterpret_cast<const uint4*>(xg + off(s + D)));
-            uq[s % D] = load16(reinterpret_cast<const uint4*>(xu + off(s + D)));
+            gq[s % D] = ld(xg + off(s + D));
+            uq[s % D] = ld(xu + off(s + D));
         }
         mbits[s] = compute_step<CLAMP, true>(lut, g, uu, w, (uint32_t)s * kWaveSize + lane < nslots, limit, a_limit,
                                              clamped, y[s]);
@@ -682,8 +685,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_2p_kernel(Params p)
         for (uint32_t c = 0; c < gs; c += kChunk) {
             float y[S][8];
             uint32_t mbits[S];
-            span_compute<CLAMP, S>(p, lut, lane, row, slot0 + c, min(kChunk, gs - c), w, limit, a_limit, clamped, y,
-                                   mbits);
+            span_compute<CLAMP, S, WaveCount, false>(p, lut, lane, row, slot0 + c, min(kChunk, gs - c), w, limit,
+                                                     a_limit, clamped, y, mbits);
             mb = max(mb, lane_max<S>(mbits, S));
         }
         mb = wave_umax(mb);
@@ -926,6 +929,7 @@ bool launch_seg(uint32_t spu_max, const Params& p, int blocks, hipStream_t s)
         TK_SEG(2)
         TK_SEG(4)
         TK_SEG(8)
+        TK_SEG(12)
         TK_SEG(16)
 #undef TK_SEG
     default: return false;
