@@ -263,6 +263,8 @@ int main(int argc, char** argv)
         check_fused(8, 96, 2048, 128, TK_SCALE_UE8M0, INFINITY, 2.0, "fp8_g128_ue8m0");
         check_fused(4, 33, 4096, 0, TK_SCALE_FP32, 3.0f, 1.5, "fp4_per_token_clamp3");
         check_fused(8, 7, 1000, 8, TK_SCALE_FP32, INFINITY, 1.0, "fp8_ragged_g8");
+        check_fused(8, 50, 1944, 24, TK_SCALE_UE8M0, 10.0f, 2.0, "fp8_g24_segmented");
+        check_fused(4, 5, 17408, 8704, TK_SCALE_FP32, INFINITY, 1.0, "fp4_g8704_two_pass");
         check_reduce();
         check_topk();
         printf("gpu checks done (%d failures)\n", failures);

@@ -1,8 +1,10 @@
 """The entry points under HIP graph capture: they allocate nothing, record no
 memset and query nothing that capture forbids, so a caller can capture them
 once and replay.  One graph holds a fused FP8 launch (with the clamp counter),
-an FP4 launch, a stand-alone cast, the gating, the reduce and three launches
-of long rows (groups shared by two waves, and 16 streamed steps); it is replayed
+an FP4 launch, a stand-alone cast, the gating, the reduce, three launches
+of long rows (groups shared by two waves, and 16 streamed steps), segmented
+groups of 96 columns (fused and cast) and two-pass groups of 8704 columns;
+small launches among them read the 16 KiB table; it is replayed
 several times with eager work between the replays (outputs poisoned, the
 counter zeroed by torch outside the graph), and every replay must equal the
 eager results bit for bit."""
@@ -42,6 +44,15 @@ def test_capture_and_replay_matches_eager():
     xl_h = wl.make_x(wc, 1, rows=range(nl))
     xl = torch.from_numpy(np.ascontiguousarray(np.tile(xl_h, (1, 2 * hl // xl_h.shape[1]))).view(np.int16)).to(DEV)
 
+    # segmented groups (96 columns of 2016) and two-pass groups (8704 columns of 17408)
+    ns, hs = 300, 2016
+    xs = torch.from_numpy(np.ascontiguousarray(np.concatenate(
+        [wl.make_x(wc, 2, rows=range(ns))[:, :hs], wl.make_x(wc, 2, rows=range(ns))[:, 2048:2048 + hs]], axis=1))
+        .view(np.int16)).to(DEV)
+    n2, h2 = 12, 17408
+    x2 = torch.from_numpy(np.ascontiguousarray(np.tile(xl_h[:n2], (1, (2 * h2 + 4095) // 4096))[:, :2 * h2])
+                          .view(np.int16)).to(DEV)
+
     outs = dict(
         codes=torch.empty((n, 2048), dtype=torch.uint8, device=DEV),
         scales=torch.empty((n, 1), dtype=torch.float32, device=DEV),
@@ -59,6 +70,12 @@ def test_capture_and_replay_matches_eager():
         lscales4=torch.empty((nl, 1), dtype=torch.uint8, device=DEV),
         lccodes=torch.empty((nl, hl), dtype=torch.uint8, device=DEV),
         lcscales=torch.empty((nl, 1), dtype=torch.float32, device=DEV),
+        scodes=torch.empty((ns, hs), dtype=torch.uint8, device=DEV),
+        sscales=torch.empty((ns, hs // 96), dtype=torch.uint8, device=DEV),
+        sccodes=torch.empty((ns, hs), dtype=torch.uint8, device=DEV),
+        sccscales=torch.empty((ns, 2 * hs // 96), dtype=torch.float32, device=DEV),
+        tcodes=torch.empty((n2, h2), dtype=torch.uint8, device=DEV),
+        tscales=torch.empty((n2, 2), dtype=torch.float32, device=DEV),
     )
 
     def work():
@@ -78,6 +95,12 @@ def test_capture_and_replay_matches_eager():
                                      outs["lscales4"], None, s) == OK
         assert tk.tk_cast_fp8(xl, tk.TK_DTYPE_BF16, nl, hl, 0, tk.TK_SCALE_FP32, outs["lccodes"], outs["lcscales"],
                               s) == OK
+        assert tk.tk_swiglu_cast_fp8(xs, w[:ns], ns, hs, 96, 10.0, tk.TK_SCALE_UE8M0, outs["scodes"], outs["sscales"],
+                                     outs["count"], s) == OK
+        assert tk.tk_cast_fp4(xs, tk.TK_DTYPE_BF16, ns, 2 * hs, 96, tk.TK_SCALE_FP32, outs["sccodes"],
+                              outs["sccscales"], s) == OK
+        assert tk.tk_swiglu_cast_fp8(x2, None, n2, h2, 8704, math.inf, tk.TK_SCALE_FP32, outs["tcodes"],
+                                     outs["tscales"], None, s) == OK
 
     def poison():
         for k, t in outs.items():
