@@ -15,7 +15,11 @@
 // (l & 31)*C .. +C-1 of its token (C = ceil(experts/32) <= 8).  Otherwise
 // (topk_kernel): one wave per token, lane l holding experts l*C .. l*C+C-1
 // (C = ceil(experts/64) <= 8).  Either way a group of experts is a block of
-// consecutive lanes and lane order is index order.
+// consecutive lanes and lane order is index order.  When a token's kept
+// groups fit 16 lanes of the two-token layout (at most 8 groups, k <= 16;
+// 256 experts in 8 groups keeping 4, for one), topk_quad_kernel ranks the
+// groups first, moves the kept lanes into one 16-lane row per token and
+// runs steps 1 and 3 on four tokens per wave.
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -259,34 +263,12 @@ __device__ __forceinline__ uint32_t half_umax_at_ends(uint32_t v)
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
 }
 
-template <int C, bool FULL, bool K8>
-__global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __restrict__ scores, uint32_t tokens,
-                                                             uint32_t experts, uint32_t k, uint32_t n_group,
-                                                             uint32_t topk_group, uint32_t gl_log2, int normalise,
-                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+// A lane's C candidates sorted best first by (key, smaller slot); idx[j] is
+// 7 - slot of entry j, so that as a low word beside the key it breaks ties
+// toward the smaller index.
+template <int C>
+__device__ __forceinline__ void sort_lane(uint32_t (&key)[C], uint32_t (&idx)[C])
 {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t t0 = 2u * __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
-    if (t0 >= tokens)
-        return;
-    const bool hi = lane >= 32u;
-    const uint32_t hl = lane & 31u;
-    const uint32_t t = t0 + (hi ? 1u : 0u);
-    // a wave past an odd last token repeats that token in its high half and stores nothing from it
-    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
-
-    // ---- 1. this lane's candidates, sorted best first.  The slot of entry j
-    // is kept as 7 - j, so that as a low word beside the key it breaks ties
-    // toward the smaller index.
-    // (FULL: experts == 32*C, every slot holds an expert)
-    uint32_t key[C], idx[C];
-    float v[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-        v[j] = FULL ? s_row[hl * C + j] : s_row[min(hl * C + j, experts - 1u)];
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-        key[j] = (FULL || hl * C + j < experts) ? ordered(v[j]) : 0u;
     if constexpr (C == 8) {
         // 19-comparator network on (key, 7 - slot): every pair of entries is
         // strictly ordered, so the network's lack of stability does not matter
@@ -328,51 +310,93 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
             }
         }
     }
+}
+
+// The rank of this lane's group among its token's groups in the two-token
+// layout (a group is 2^gl_log2 <= 32 lanes inside its half), from the lane's
+// two best keys a1 >= a2 (0 = none); 0 is the best group.
+__device__ __forceinline__ uint32_t pair_group_rank(uint32_t a1, uint32_t a2, uint32_t lane, uint32_t gl_log2,
+                                                    uint32_t n_group)
+{
+    const bool hi = lane >= 32u;
+    const uint32_t hl = lane & 31u;
+    if (gl_log2 >= 1)
+        merge_top2<0xB1>(a1, a2);
+    if (gl_log2 >= 2)
+        merge_top2<0x4E>(a1, a2);
+    if (gl_log2 >= 3)
+        merge_top2<0x141>(a1, a2);
+    if (gl_log2 >= 4)
+        merge_top2<0x140>(a1, a2);
+    if (gl_log2 >= 5)
+        merge_top2_from(a1, a2, (uint32_t)__shfl_xor((int)a1, 16), (uint32_t)__shfl_xor((int)a2, 16));
+    float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
+    if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf
+        gsum = -INFINITY;
+    const uint32_t my_g = hl >> gl_log2;
+    uint32_t rank = 0;
+    if (n_group <= 8) {
+        // one ballot per token: lane 8h + h' compares that token's group
+        // h' against its group h; group h's rank is the count of set bits
+        // in byte h
+        const uint32_t h = lane >> 3, h2 = lane & 7u;
+        const uint32_t in = (uint32_t)(max(h, h2) < n_group);
+        const uint32_t lt = (uint32_t)(h2 < h);
+        uint64_t m[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t base = 32u * p;
+            const float g_h = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)((base + (min(h, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
+            const float g_h2 = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)((base + (min(h2, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
+            const uint32_t b = in & ((uint32_t)(g_h2 > g_h) | ((uint32_t)(g_h2 == g_h) & lt));
+            m[p] = __builtin_amdgcn_ballot_w64(b != 0u);
+        }
+        rank = (uint32_t)__builtin_popcountll(((hi ? m[1] : m[0]) >> (8u * my_g)) & 0xFFull);
+    } else {
+        for (uint32_t hh = 0; hh < n_group; ++hh) {
+            const float g0 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), hh << gl_log2));
+            const float g1 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), 32u + (hh << gl_log2)));
+            rank += beats(hi ? g1 : g0, hh, gsum, my_g) ? 1u : 0u;
+        }
+    }
+    return rank;
+}
+
+template <int C, bool FULL, bool K8>
+__global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, uint32_t n_group,
+                                                             uint32_t topk_group, uint32_t gl_log2, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t t0 = 2u * __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
+    if (t0 >= tokens)
+        return;
+    const bool hi = lane >= 32u;
+    const uint32_t hl = lane & 31u;
+    const uint32_t t = t0 + (hi ? 1u : 0u);
+    // a wave past an odd last token repeats that token in its high half and stores nothing from it
+    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
+
+    // ---- 1. this lane's candidates, sorted best first.  The slot of entry j
+    // is kept as 7 - j, so that as a low word beside the key it breaks ties
+    // toward the smaller index.
+    // (FULL: experts == 32*C, every slot holds an expert)
+    uint32_t key[C], idx[C];
+    float v[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        v[j] = FULL ? s_row[hl * C + j] : s_row[min(hl * C + j, experts - 1u)];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        key[j] = (FULL || hl * C + j < experts) ? ordered(v[j]) : 0u;
+    sort_lane<C>(key, idx);
 
     // ---- 2. group selection, per half (a group is 2^gl_log2 <= 32 lanes)
     if (n_group > 1) {
-        uint32_t a1 = key[0], a2 = C > 1 ? key[C > 1 ? 1 : 0] : 0u;
-        if (gl_log2 >= 1)
-            merge_top2<0xB1>(a1, a2);
-        if (gl_log2 >= 2)
-            merge_top2<0x4E>(a1, a2);
-        if (gl_log2 >= 3)
-            merge_top2<0x141>(a1, a2);
-        if (gl_log2 >= 4)
-            merge_top2<0x140>(a1, a2);
-        if (gl_log2 >= 5)
-            merge_top2_from(a1, a2, (uint32_t)__shfl_xor((int)a1, 16), (uint32_t)__shfl_xor((int)a2, 16));
-        float gsum = (a1 ? unordered(a1) : -INFINITY) + (a2 ? unordered(a2) : -INFINITY);
-        if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf
-            gsum = -INFINITY;
-        const uint32_t my_g = hl >> gl_log2;
-        uint32_t rank = 0;
-        if (n_group <= 8) {
-            // one ballot per token: lane 8h + h' compares that token's group
-            // h' against its group h; group h's rank is the count of set bits
-            // in byte h
-            const uint32_t h = lane >> 3, h2 = lane & 7u;
-            const uint32_t in = (uint32_t)(max(h, h2) < n_group);
-            const uint32_t lt = (uint32_t)(h2 < h);
-            uint64_t m[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const uint32_t base = 32u * p;
-                const float g_h = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
-                    (int)((base + (min(h, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
-                const float g_h2 = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute(
-                    (int)((base + (min(h2, n_group - 1u) << gl_log2)) << 2), (int)fbits(gsum)));
-                const uint32_t b = in & ((uint32_t)(g_h2 > g_h) | ((uint32_t)(g_h2 == g_h) & lt));
-                m[p] = __builtin_amdgcn_ballot_w64(b != 0u);
-            }
-            rank = (uint32_t)__builtin_popcountll(((hi ? m[1] : m[0]) >> (8u * my_g)) & 0xFFull);
-        } else {
-            for (uint32_t hh = 0; hh < n_group; ++hh) {
-                const float g0 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), hh << gl_log2));
-                const float g1 = ffrom(__builtin_amdgcn_readlane(fbits(gsum), 32u + (hh << gl_log2)));
-                rank += beats(hi ? g1 : g0, hh, gsum, my_g) ? 1u : 0u;
-            }
-        }
+        const uint32_t rank = pair_group_rank(key[0], C > 1 ? key[C > 1 ? 1 : 0] : 0u, lane, gl_log2, n_group);
         if (rank >= topk_group) {
 #pragma unroll
             for (int j = 0; j < C; ++j)
@@ -456,6 +480,176 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
     }
 }
 
+// Four tokens per wave, for shapes of the two-token layout whose kept groups
+// fill at most 16 lanes of a token (topk_group * 2^gl_log2 <= 16; with 256
+// experts: 8 groups keep up to 4, 4 keep up to 2, 2 keep 1) and k <= 16.
+// Groups are ranked first, from each lane's two best keys; then the lanes of
+// the kept groups move through LDS, in group order, into one 16-lane row per
+// token, so that lane order in a row is still index order.  The sort and the
+// k rounds then run on those rows: a round's maximum is a DPP maximum inside
+// each 16-lane row (every lane of the row ends with it, so no lane reads),
+// and one round serves four tokens instead of two.  A round's winners write
+// their expert index into LDS at the round's position; output lane j of a
+// row reads pick j from there.
+template <int C, bool FULL, bool K8>
+__global__ __launch_bounds__(kThreads) void topk_quad_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, uint32_t n_group,
+                                                             uint32_t topk_group, uint32_t gl_log2, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kWords = C > 4 ? 2 : 1; // 16-byte words of a lane's candidate keys
+    __shared__ uint4 s_keys[kWaves][kWords][kWave];
+    __shared__ uint32_t s_src[kWaves][kWave];
+    __shared__ int32_t s_pick[kWaves][kWave]; // [row * 16 + round]
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    if (t0 >= tokens)
+        return;
+    const bool hi = lane >= 32u;
+    const uint32_t hl = lane & 31u;
+    const uint32_t gmask = (1u << gl_log2) - 1u;
+
+    // ---- 1. the two-token layout twice: tokens t0 + 2p (lanes 0-31) and
+    // t0 + 2p + 1 (lanes 32-63); a wave past the last token repeats it and
+    // stores nothing from it.  Both passes' loads are issued first.
+    float v[2][C];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float* s_row = scores + (size_t)min(t0 + 2u * p + (hi ? 1u : 0u), tokens - 1u) * experts;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            v[p][j] = FULL ? s_row[hl * C + j] : s_row[min(hl * C + j, experts - 1u)];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        uint32_t key[C + (C % 4 ? 4 - C % 4 : 0)];
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            key[j] = (FULL || hl * C + j < experts) ? ordered(v[p][j]) : 0u;
+#pragma unroll
+        for (int j = C; j < (int)(sizeof(key) / sizeof(key[0])); ++j)
+            key[j] = 0u;
+        // the lane's two best keys, unsorted
+        uint32_t a1 = key[0], a2 = 0u;
+        if constexpr (C > 1) {
+            a1 = max(key[0], key[1]);
+            a2 = min(key[0], key[1]);
+#pragma unroll
+            for (int j = 2; j < C; ++j) {
+                a2 = max(a2, min(a1, key[j]));
+                a1 = max(a1, key[j]);
+            }
+        }
+        const uint32_t rank = pair_group_rank(a1, a2, lane, gl_log2, n_group);
+        const bool kept = (hl >> gl_log2) < n_group && rank < topk_group;
+        // kept groups below this lane's own: the last lanes of kept groups below it in its half
+        const uint64_t last = __builtin_amdgcn_ballot_w64(kept && (hl & gmask) == gmask);
+        const uint32_t below = hi ? __builtin_amdgcn_mbcnt_hi((uint32_t)(last >> 32), 0u)
+                                  : __builtin_amdgcn_mbcnt_lo((uint32_t)last, 0u);
+        if (kept) {
+            const uint32_t d = 16u * (2u * p + (hi ? 1u : 0u)) + ((below << gl_log2) | (hl & gmask));
+#pragma unroll
+            for (int w = 0; w < kWords; ++w)
+                s_keys[wv][w][d] = make_uint4(key[4 * w], key[4 * w + 1], key[4 * w + 2], key[4 * w + 3]);
+            s_src[wv][d] = hl;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 2. row r = lane / 16 holds token t0 + r: its kept lanes, then empty ones
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
+    const bool filled = q < (topk_group << gl_log2);
+    uint32_t key[C], idx[C];
+    {
+        uint32_t w8[4 * kWords];
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) {
+            const uint4 x = s_keys[wv][w][lane];
+            w8[4 * w] = x.x;
+            w8[4 * w + 1] = x.y;
+            w8[4 * w + 2] = x.z;
+            w8[4 * w + 3] = x.w;
+        }
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            key[j] = filled ? w8[j] : 0u;
+    }
+    // the expert index of this lane's first slot (an empty lane's picks
+    // never happen, since k is at most the candidates; it points at expert 0)
+    const uint32_t base = filled ? (s_src[wv][lane] & 31u) * C : 0u;
+    sort_lane<C>(key, idx);
+    // slot lists, head lowest, 3 bits each: the slots themselves (7 - idx)
+    uint32_t slots = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        slots |= idx[j] << (3 * j);
+    slots ^= 0xFFFFFFu;
+
+    // ---- 3. k rounds, four tokens at once
+    int32_t* pick_row = &s_pick[wv][row << 4];
+    auto round = [&](uint32_t it, uint32_t depth) {
+        uint32_t m = key[0];
+        m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
+        m = dpp_umax<0x4E>(m);  // quad_perm [2,3,0,1]
+        m = dpp_umax<0x141>(m); // row_half_mirror
+        m = dpp_umax<0x140>(m); // row_mirror: every lane holds its row's maximum
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == m);
+        // the lowest set bit of each row's 16 bits (every row has one: its
+        // maximum is some lane's head, so no borrow crosses a row)
+        const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
+        if (__builtin_amdgcn_inverse_ballot_w64(win)) {
+            pick_row[it] = (int32_t)(C == 8 ? (base | (slots & 7u)) : (base + (slots & 7u)));
+#pragma unroll
+            for (int j = 0; j + 1 < C; ++j)
+                if (j + 1u < depth)
+                    key[j] = key[j + 1];
+            if (depth > (uint32_t)C)
+                key[C - 1] = 0u;
+            slots >>= 3;
+        }
+    };
+    if constexpr (K8) {
+#pragma unroll
+        for (uint32_t it = 0; it < 8; ++it)
+            round(it, 8u - it);
+    } else {
+        uint32_t it = 0;
+        for (; it + 1 < k; it += 2) {
+            round(it, 64u);
+            round(it + 1, 64u);
+        }
+        if (it < k)
+            round(it, 64u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 4. output lane q of row r: pick q of token t0 + r
+    const uint32_t t = t0 + row;
+    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
+    const int32_t my_idx = q < k ? s_pick[wv][lane] : 0;
+    const float my_w = q < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
+    float sum = 0.0f;
+    if (normalise) {
+        // running sum in pick order inside each row (row_shr:1 reads 0 into a
+        // row's first lane): lane k-1 ends with 0 + w[0] + ... + w[k-1]
+        float run = 0.0f;
+        for (uint32_t it = 0; it < k; ++it)
+            run = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(run), 0x111, 0xF, 0xF, true)) + my_w;
+        sum = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute((int)(((row << 4) + k - 1u) << 2), (int)fbits(run)));
+    }
+    if (q < k && t < tokens) {
+        idx_out[(size_t)t * k + q] = my_idx;
+        w_out[(size_t)t * k + q] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
+    }
+}
+
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
 {
     if (!a || !b || an == 0 || bn == 0)
@@ -515,12 +709,19 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
         return TK_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (C2) {
-        const uint32_t tpb = 2 * (kThreads / kWave);
+        // four tokens per wave when each token's kept groups fit one 16-lane row
+        const bool quad = n_group >= 2 && n_group <= 8 && (topk_group << gl2) <= 16 && k <= 16;
+        const uint32_t tpb = (quad ? 4 : 2) * (kThreads / kWave);
         const uint32_t pblocks = (uint32_t)((tokens + tpb - 1) / tpb);
 #define TK_TOPK2_LAUNCH(CC, FULL, K8)                                                                         \
-    hipLaunchKernelGGL((topk_pair_kernel<CC, FULL, K8>), dim3(pblocks), dim3(kThreads), 0, s, scores,         \
-                       (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group, (uint32_t)topk_group, \
-                       gl2, normalise, topk_idx, topk_weight)
+    if (quad)                                                                                                 \
+        hipLaunchKernelGGL((topk_quad_kernel<CC, FULL, K8>), dim3(pblocks), dim3(kThreads), 0, s, scores,     \
+                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,               \
+                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight);                      \
+    else                                                                                                      \
+        hipLaunchKernelGGL((topk_pair_kernel<CC, FULL, K8>), dim3(pblocks), dim3(kThreads), 0, s, scores,     \
+                           (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, (uint32_t)n_group,               \
+                           (uint32_t)topk_group, gl2, normalise, topk_idx, topk_weight)
 #define TK_TOPK2(CC)                                                                                          \
     if (experts == 32 * (CC)) {                                                                               \
         if (k == 8)                                                                                           \

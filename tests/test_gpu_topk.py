@@ -61,6 +61,11 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     # 96 / 4: 3 per lane, 8 lanes), groups that need more experts per lane than the minimum (120 / 6 and
     # 100 / 5: 5 per lane, 4 lanes), and a shape no layout holds (9 experts per group)
     (160, 6, 8, 3), (96, 4, 4, 2), (120, 6, 6, 2), (100, 5, 5, 2), (72, 4, 8, 2),
+    # four tokens per wave (kept groups within 16 lanes of the two-token layout, at most 8 groups,
+    # k <= 16): every row filled, part-filled rows, 8 / 4 / 2 groups, k = 1 and 16, 2 to 8 experts
+    # per lane; and its neighbours that stay two to a wave (20 kept lanes, k = 17, 16 groups)
+    (256, 16, 8, 4), (256, 8, 8, 3), (256, 1, 8, 1), (256, 8, 4, 2), (256, 4, 2, 1), (192, 8, 8, 4),
+    (64, 6, 8, 4), (128, 8, 8, 4), (256, 8, 8, 5), (256, 17, 8, 4), (256, 8, 16, 8),
 ]
 
 
@@ -88,6 +93,23 @@ def test_topk_matches_oracle(shape, normalise):
     bad = np.argwhere(gi != oi)
     assert bad.size == 0, f"indices differ at {bad[:4].tolist()}: {gi[bad[0][0]]} vs {oi[bad[0][0]]}"
     assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), np.argwhere(gw.view(np.uint32) != ow.view(np.uint32))[:4]
+
+
+@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (64, 3, 8, 2)], ids=str)
+def test_topk_last_wave_partly_past_the_tokens(shape):
+    """Token counts around the four-tokens-per-wave grid: a last wave with 1,
+    2 or 3 real tokens repeats the last one in its other rows and stores
+    nothing from them (the canaries past the outputs stay)."""
+    E, k, ng, tg = shape
+    for T in (1, 2, 3, 4, 5, 6, 7, 63, 65, 66, 67):
+        print("[gpu-case] topk tail", shape, T, flush=True)
+        u = wl.uniform(wl.stream_key("topk_test", E * 1000 + k * 10 + T, "tail"), 0, T * E).reshape(T, E)
+        s = (np.floor(u * 16) / 16).astype(np.float32)  # many ties
+        for normalise in (0, 1):
+            gi, gw = run(s, k, ng, tg, normalise)
+            oi, ow = oracle.topk_gate(s, k, ng, tg, bool(normalise))
+            assert np.array_equal(gi, oi), (T, normalise, np.argwhere(gi != oi)[:4])
+            assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), (T, normalise)
 
 
 def test_topk_deepseek_shape_full_size():
