@@ -49,9 +49,9 @@ KERNELS = {
     "fused": (("tk_swiglu_cast.hip", "tk_quant.h"), r"\bswiglu_cast_kernel<", "swiglu_cast_kernel"),
     "cast": (("tk_cast.hip", "tk_quant.h"), r"\bcast_kernel<", "cast_kernel"),
     "reduce": (("tk_reduce.hip",), r"\bmoe_reduce_kernel<", "moe_reduce_kernel"),
-    # (topk_quad_kernel serves the gating workload's shape: 256 experts, 8
+    # (topk_row_kernel serves the gating workload's shape: 256 experts, 8
     # groups keep 4, top-8)
-    "topk": (("tk_topk.hip",), r"\btopk_(?:pair_|quad_)?kernel<", "topk_quad_kernel"),
+    "topk": (("tk_topk.hip",), r"\btopk_(?:pair_|quad_|row_)?kernel<", "topk_row_kernel"),
 }
 
 

@@ -17,9 +17,12 @@
 // (C = ceil(experts/64) <= 8).  Either way a group of experts is a block of
 // consecutive lanes and lane order is index order.  When a token's kept
 // groups fit 16 lanes of the two-token layout (at most 8 groups, k <= 16;
-// 256 experts in 8 groups keeping 4, for one), topk_quad_kernel ranks the
-// groups first, moves the kept lanes into one 16-lane row per token and
-// runs steps 1 and 3 on four tokens per wave.
+// 256 experts in 8 groups keeping 4, for one), the groups are ranked first,
+// the kept lanes move into one 16-lane row per token and steps 1 and 3 run
+// on four tokens per wave: topk_row_kernel for 128 or 256 experts (one token
+// per 16-lane row from the start, group ranks by row broadcasts),
+// topk_quad_kernel for the other such shapes (two passes of the two-token
+// layout).
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -480,6 +483,110 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
     }
 }
 
+// The part of the four-tokens-per-wave kernels after the kept lanes have been
+// written to LDS: row r = lane / 16 holds token t0 + r, its `filled_lanes`
+// first lanes a kept lane's C keys each (index order along the row) and
+// s_src the expert index of each lane's first key.  Each lane sorts its keys,
+// the k rounds run on the rows (a DPP maximum inside each 16-lane row, so one
+// round serves four tokens; a round's winners write their pick into s_pick at
+// the round's position), and output lane q of row r stores pick q.
+template <int C, bool K8>
+__device__ __forceinline__ void quad_rows_finish(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
+                                                 uint32_t k, uint32_t filled_lanes, int normalise,
+                                                 int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                 uint32_t t0, uint32_t lane, const uint4 (*s_keys)[kWave],
+                                                 const uint32_t* s_src, int32_t* s_pick)
+{
+    constexpr int kWords = C > 4 ? 2 : 1;
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
+    const bool filled = q < filled_lanes;
+    uint32_t key[C], idx[C];
+    {
+        uint32_t w8[4 * kWords];
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) {
+            const uint4 x = s_keys[w][lane];
+            w8[4 * w] = x.x;
+            w8[4 * w + 1] = x.y;
+            w8[4 * w + 2] = x.z;
+            w8[4 * w + 3] = x.w;
+        }
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            key[j] = filled ? w8[j] : 0u;
+    }
+    // the expert index of this lane's first slot (an empty lane's picks
+    // never happen, since k is at most the candidates; it points at expert 0)
+    const uint32_t base = filled ? s_src[lane] : 0u;
+    sort_lane<C>(key, idx);
+    // slot lists, head lowest, 3 bits each: the slots themselves (7 - idx)
+    uint32_t slots = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        slots |= idx[j] << (3 * j);
+    slots ^= 0xFFFFFFu;
+
+    // ---- k rounds, four tokens at once
+    int32_t* pick_row = &s_pick[row << 4];
+    auto round = [&](uint32_t it, uint32_t depth) {
+        uint32_t m = key[0];
+        m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
+        m = dpp_umax<0x4E>(m);  // quad_perm [2,3,0,1]
+        m = dpp_umax<0x141>(m); // row_half_mirror
+        m = dpp_umax<0x140>(m); // row_mirror: every lane holds its row's maximum
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == m);
+        // the lowest set bit of each row's 16 bits (every row has one: its
+        // maximum is some lane's head, so no borrow crosses a row)
+        const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
+        if (__builtin_amdgcn_inverse_ballot_w64(win)) {
+            pick_row[it] = (int32_t)(C == 8 ? (base | (slots & 7u)) : (base + (slots & 7u)));
+#pragma unroll
+            for (int j = 0; j + 1 < C; ++j)
+                if (j + 1u < depth)
+                    key[j] = key[j + 1];
+            if (depth > (uint32_t)C)
+                key[C - 1] = 0u;
+            slots >>= 3;
+        }
+    };
+    if constexpr (K8) {
+#pragma unroll
+        for (uint32_t it = 0; it < 8; ++it)
+            round(it, 8u - it);
+    } else {
+        uint32_t it = 0;
+        for (; it + 1 < k; it += 2) {
+            round(it, 64u);
+            round(it + 1, 64u);
+        }
+        if (it < k)
+            round(it, 64u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- output lane q of row r: pick q of token t0 + r
+    const uint32_t t = t0 + row;
+    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
+    const int32_t my_idx = q < k ? s_pick[lane] : 0;
+    const float my_w = q < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
+    float sum = 0.0f;
+    if (normalise) {
+        // running sum in pick order inside each row (row_shr:1 reads 0 into a
+        // row's first lane): lane k-1 ends with 0 + w[0] + ... + w[k-1]
+        float run = 0.0f;
+        for (uint32_t it = 0; it < k; ++it)
+            run = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(run), 0x111, 0xF, 0xF, true)) + my_w;
+        sum = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute((int)(((row << 4) + k - 1u) << 2), (int)fbits(run)));
+    }
+    if (q < k && t < tokens) {
+        idx_out[(size_t)t * k + q] = my_idx;
+        w_out[(size_t)t * k + q] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
+    }
+}
+
 // Four tokens per wave, for shapes of the two-token layout whose kept groups
 // fill at most 16 lanes of a token (topk_group * 2^gl_log2 <= 16; with 256
 // experts: 8 groups keep up to 4, 4 keep up to 2, 2 keep 1) and k <= 16.
@@ -553,101 +660,112 @@ __global__ __launch_bounds__(kThreads) void topk_quad_kernel(const float* __rest
 #pragma unroll
             for (int w = 0; w < kWords; ++w)
                 s_keys[wv][w][d] = make_uint4(key[4 * w], key[4 * w + 1], key[4 * w + 2], key[4 * w + 3]);
-            s_src[wv][d] = hl;
+            s_src[wv][d] = hl * C;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- 2. row r = lane / 16 holds token t0 + r: its kept lanes, then empty ones
+    quad_rows_finish<C, K8>(scores, tokens, experts, k, topk_group << gl_log2, normalise, idx_out, w_out, t0, lane,
+                            s_keys[wv], s_src[wv], s_pick[wv]);
+}
+
+// Group ranks within 16-lane rows (one token per row, 16 >> GL groups of
+// 2^GL lanes): group H's sum reaches every lane of the row by row_newbcast
+// from the group's first lane, and a lane counts the groups that beat its own
+// ("a beats b": larger sum, or equal sums and the smaller group index).
+template <int GL, int H = 0>
+__device__ __forceinline__ void row_group_rank(float gsum, uint32_t& rank)
+{
+    if constexpr ((H << GL) < 16) {
+        const float gh = ffrom((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(gsum), 0x150 + (H << GL), 0xF, 0xF, false));
+        // the lanes of groups above H, whose equal sums lose to group H: a constant lane mask
+        constexpr uint64_t kAbove = (uint64_t)(0xFFFFu & ~((1u << ((H + 1) << GL)) - 1u)) * 0x0001000100010001ull;
+        const bool loses_tie = __builtin_amdgcn_inverse_ballot_w64(kAbove);
+        rank += (gh > gsum || (gh == gsum && loses_tie)) ? 1u : 0u;
+        row_group_rank<GL, H + 1>(gsum, rank);
+    }
+}
+
+// Four tokens per wave in one pass, for 128 or 256 experts in 2, 4 or 8
+// groups (C16 = 8 or 16 experts per lane, 16 lanes per token, 16 >> GL groups
+// of 2^GL lanes) whose kept groups fill at most 8 lanes, and k <= 16: lane q of
+// row r holds experts q*C16 .. +C16-1 of token 4w + r.  Each row ranks its
+// groups with row broadcasts (no LDS), and a kept lane writes the two halves
+// of its keys to two lanes of its own row, in group order, so that lane
+// order in the row is still index order; then the rows go on as in
+// topk_quad_kernel.
+template <int C16, bool K8, int GL>
+__global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                            uint32_t k, uint32_t topk_group, int normalise,
+                                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    constexpr uint32_t kExperts = 16 * C16;
+    constexpr int C = C16 / 2; // keys per row lane after the move
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kWords = C > 4 ? 2 : 1;
+    constexpr uint32_t kGMask = (1u << GL) - 1u;
+    static_assert(C16 == 8 || C16 == 16, "8 or 16 experts per lane");
+    __shared__ uint4 s_keys[kWaves][kWords][kWave];
+    __shared__ uint32_t s_src[kWaves][kWave];
+    __shared__ int32_t s_pick[kWaves][kWave]; // [row * 16 + round]
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    if (t0 >= tokens)
+        return;
     const uint32_t q = lane & 15u;
     const uint32_t row = lane >> 4;
-    const bool filled = q < (topk_group << gl_log2);
-    uint32_t key[C], idx[C];
-    {
-        uint32_t w8[4 * kWords];
+    // a wave past the last token repeats it in its other rows and stores nothing from them
+    const float* s_row = scores + (size_t)min(t0 + row, tokens - 1u) * kExperts;
+    uint32_t key[C16];
 #pragma unroll
-        for (int w = 0; w < kWords; ++w) {
-            const uint4 x = s_keys[wv][w][lane];
-            w8[4 * w] = x.x;
-            w8[4 * w + 1] = x.y;
-            w8[4 * w + 2] = x.z;
-            w8[4 * w + 3] = x.w;
-        }
+    for (int j = 0; j < C16; ++j)
+        key[j] = ordered(s_row[q * C16 + j]);
+    // the lane's two best keys, unsorted, then the group's over its 2^GL lanes
+    uint32_t a1 = max(key[0], key[1]), a2 = min(key[0], key[1]);
 #pragma unroll
-        for (int j = 0; j < C; ++j)
-            key[j] = filled ? w8[j] : 0u;
+    for (int j = 2; j < C16; ++j) {
+        a2 = max(a2, min(a1, key[j]));
+        a1 = max(a1, key[j]);
     }
-    // the expert index of this lane's first slot (an empty lane's picks
-    // never happen, since k is at most the candidates; it points at expert 0)
-    const uint32_t base = filled ? (s_src[wv][lane] & 31u) * C : 0u;
-    sort_lane<C>(key, idx);
-    // slot lists, head lowest, 3 bits each: the slots themselves (7 - idx)
-    uint32_t slots = 0;
+    if constexpr (GL >= 1)
+        merge_top2<0xB1>(a1, a2); // quad_perm [1,0,3,2]
+    if constexpr (GL >= 2)
+        merge_top2<0x4E>(a1, a2); // quad_perm [2,3,0,1]
+    if constexpr (GL >= 3)
+        merge_top2<0x141>(a1, a2); // row_half_mirror
+    float gsum = unordered(a1) + unordered(a2);
+    if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf
+        gsum = -INFINITY;
+    uint32_t rank = 0;
+    row_group_rank<GL>(gsum, rank);
+    const bool kept = rank < topk_group;
+    // kept groups below this lane's own in its row: the last lanes of kept
+    // groups below it, counted over the wave and less those of the rows above
+    const uint64_t last = __builtin_amdgcn_ballot_w64(kept && (q & kGMask) == kGMask);
+    const uint32_t below_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(last >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)last, 0u));
+    const uint32_t above = row == 0 ? 0u
+                           : (uint32_t)__builtin_popcountll(last & (row == 1 ? 0xFFFFull : row == 2 ? 0xFFFFFFFFull
+                                                                                                      : 0xFFFFFFFFFFFFull));
+    const uint32_t below = below_wave - above;
+    if (kept) {
+        const uint32_t d = (row << 4) + 2u * ((below << GL) | (q & kGMask));
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-        slots |= idx[j] << (3 * j);
-    slots ^= 0xFFFFFFu;
-
-    // ---- 3. k rounds, four tokens at once
-    int32_t* pick_row = &s_pick[wv][row << 4];
-    auto round = [&](uint32_t it, uint32_t depth) {
-        uint32_t m = key[0];
-        m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
-        m = dpp_umax<0x4E>(m);  // quad_perm [2,3,0,1]
-        m = dpp_umax<0x141>(m); // row_half_mirror
-        m = dpp_umax<0x140>(m); // row_mirror: every lane holds its row's maximum
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == m);
-        // the lowest set bit of each row's 16 bits (every row has one: its
-        // maximum is some lane's head, so no borrow crosses a row)
-        const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
-        if (__builtin_amdgcn_inverse_ballot_w64(win)) {
-            pick_row[it] = (int32_t)(C == 8 ? (base | (slots & 7u)) : (base + (slots & 7u)));
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int j = 0; j + 1 < C; ++j)
-                if (j + 1u < depth)
-                    key[j] = key[j + 1];
-            if (depth > (uint32_t)C)
-                key[C - 1] = 0u;
-            slots >>= 3;
+            for (int w = 0; w < kWords; ++w)
+                s_keys[wv][w][d + h] = make_uint4(key[h * C + 4 * w], key[h * C + 4 * w + 1], key[h * C + 4 * w + 2],
+                                                  key[h * C + 4 * w + 3]);
+            s_src[wv][d + h] = q * C16 + h * C;
         }
-    };
-    if constexpr (K8) {
-#pragma unroll
-        for (uint32_t it = 0; it < 8; ++it)
-            round(it, 8u - it);
-    } else {
-        uint32_t it = 0;
-        for (; it + 1 < k; it += 2) {
-            round(it, 64u);
-            round(it + 1, 64u);
-        }
-        if (it < k)
-            round(it, 64u);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- 4. output lane q of row r: pick q of token t0 + r
-    const uint32_t t = t0 + row;
-    const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
-    const int32_t my_idx = q < k ? s_pick[wv][lane] : 0;
-    const float my_w = q < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
-    float sum = 0.0f;
-    if (normalise) {
-        // running sum in pick order inside each row (row_shr:1 reads 0 into a
-        // row's first lane): lane k-1 ends with 0 + w[0] + ... + w[k-1]
-        float run = 0.0f;
-        for (uint32_t it = 0; it < k; ++it)
-            run = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(run), 0x111, 0xF, 0xF, true)) + my_w;
-        sum = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute((int)(((row << 4) + k - 1u) << 2), (int)fbits(run)));
-    }
-    if (q < k && t < tokens) {
-        idx_out[(size_t)t * k + q] = my_idx;
-        w_out[(size_t)t * k + q] = (normalise && sum != 0.0f) ? my_w / sum : my_w;
-    }
+    quad_rows_finish<C, K8>(scores, tokens, kExperts, k, 2u * (topk_group << GL), normalise, idx_out, w_out, t0, lane,
+                            s_keys[wv], s_src[wv], s_pick[wv]);
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
@@ -708,6 +826,31 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
     if (tokens == 0)
         return TK_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // one token per 16-lane row in one pass: 128 or 256 experts (8 or 16 per
+    // lane) in 2, 4 or 8 groups of 2^GL lanes, kept groups within 8 lanes
+    if ((experts == 128 || experts == 256) && (n_group == 2 || n_group == 4 || n_group == 8) && k <= 16) {
+        const uint32_t GLr = (uint32_t)__builtin_ctzll((unsigned long long)(16 / n_group));
+        if (2 * (topk_group << GLr) <= 16) {
+            const uint32_t tpb = 4 * (kThreads / kWave);
+            const uint32_t rblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+#define TK_TOPKR_LAUNCH(C16, K8, GL)                                                                          \
+    hipLaunchKernelGGL((topk_row_kernel<C16, K8, GL>), dim3(rblocks), dim3(kThreads), 0, s, scores,           \
+                       (uint32_t)tokens, (uint32_t)k, (uint32_t)topk_group, normalise, topk_idx, topk_weight)
+#define TK_TOPKR(C16, GL)                                                                                     \
+    if (k == 8)                                                                                               \
+        TK_TOPKR_LAUNCH(C16, true, GL);                                                                       \
+    else                                                                                                      \
+        TK_TOPKR_LAUNCH(C16, false, GL);
+            if (experts == 256) {
+                if (GLr == 1) { TK_TOPKR(16, 1) } else if (GLr == 2) { TK_TOPKR(16, 2) } else { TK_TOPKR(16, 3) }
+            } else {
+                if (GLr == 1) { TK_TOPKR(8, 1) } else if (GLr == 2) { TK_TOPKR(8, 2) } else { TK_TOPKR(8, 3) }
+            }
+#undef TK_TOPKR
+#undef TK_TOPKR_LAUNCH
+            return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+        }
+    }
     if (C2) {
         // four tokens per wave when each token's kept groups fit one 16-lane row
         const bool quad = n_group >= 2 && n_group <= 8 && (topk_group << gl2) <= 16 && k <= 16;

@@ -63,9 +63,11 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     (160, 6, 8, 3), (96, 4, 4, 2), (120, 6, 6, 2), (100, 5, 5, 2), (72, 4, 8, 2),
     # four tokens per wave (kept groups within 16 lanes of the two-token layout, at most 8 groups,
     # k <= 16): every row filled, part-filled rows, 8 / 4 / 2 groups, k = 1 and 16, 2 to 8 experts
-    # per lane; and its neighbours that stay two to a wave (20 kept lanes, k = 17, 16 groups)
+    # per lane (128 and 256 experts take the one-pass row layout, the others two passes); and its
+    # neighbours that stay two to a wave (20 kept lanes, k = 17, 16 groups)
     (256, 16, 8, 4), (256, 8, 8, 3), (256, 1, 8, 1), (256, 8, 4, 2), (256, 4, 2, 1), (192, 8, 8, 4),
-    (64, 6, 8, 4), (128, 8, 8, 4), (256, 8, 8, 5), (256, 17, 8, 4), (256, 8, 16, 8),
+    (64, 6, 8, 4), (128, 8, 8, 4), (128, 4, 4, 2), (128, 3, 2, 1), (128, 16, 8, 1), (256, 8, 8, 5),
+    (256, 17, 8, 4), (256, 8, 16, 8),
 ]
 
 
