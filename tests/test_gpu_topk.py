@@ -114,6 +114,30 @@ def test_topk_last_wave_partly_past_the_tokens(shape):
             assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), (T, normalise)
 
 
+@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (256, 8, 8, 5), (512, 8, 8, 4)],
+                         ids=str)
+def test_topk_scores_only_4_byte_aligned(shape):
+    """Scores at an address that is 4 bytes past a 16-byte boundary (the
+    interface asks for 4-byte alignment only): every layout's loads still
+    read the right scores."""
+    E, k, ng, tg = shape
+    T = 37
+    print("[gpu-case] topk scores 4-byte aligned", shape, flush=True)
+    u = wl.uniform(wl.stream_key("topk_test", E * 1000 + k, "align"), 0, T * E).reshape(T, E).astype(np.float32)
+    flat = torch.zeros(T * E + 4, dtype=torch.float32, device=DEV)
+    flat[1:1 + T * E] = torch.from_numpy(u.reshape(-1)).to(DEV)
+    assert (flat.data_ptr() + 4) % 16 == 4
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), -7.0, dtype=torch.float32, device=DEV)
+    for normalise in (0, 1):
+        rc = tk.tk_topk_gate(flat.data_ptr() + 4, T, E, k, ng, tg, normalise, idx, w)
+        assert rc == tk.TkStatus.TK_OK, tk.tk_status_str(rc)
+        torch.cuda.synchronize()
+        oi, ow = oracle.topk_gate(u, k, ng, tg, bool(normalise))
+        assert np.array_equal(idx.cpu().numpy(), oi)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+
+
 def test_topk_deepseek_shape_full_size():
     """16384 tokens x 256 experts, 8 groups keep 4, top-8, normalised."""
     T, E = 16384, 256
