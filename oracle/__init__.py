@@ -64,6 +64,8 @@ def _load():
         lib.oracle_topk_gate.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int64, c.c_int64,
                                          c.c_int, c.c_void_p, c.c_void_p]
         lib.oracle_moe_reduce.restype = c.c_int
+        lib.oracle_topk_to_pos.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p]
+        lib.oracle_topk_to_pos.restype = c.c_int
         lib.oracle_moe_reduce.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_float, c.c_int64,
                                           c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_void_p]
         lib.oracle_swiglu_cast.restype = c.c_int
@@ -251,3 +253,16 @@ def moe_reduce(x: np.ndarray, pos: np.ndarray, w: np.ndarray, row_scale: Optiona
     if rc:
         raise ValueError(f"oracle_moe_reduce failed ({rc})")
     return out
+
+
+def topk_to_pos(idx: np.ndarray, experts: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Token/top-k -> expert-row map (oracle.c: oracle_topk_to_pos):
+    (pos int32 [tokens, k], -1 for absent slots; offsets int32 [experts + 1])."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    tokens, k = idx.shape
+    pos = np.empty((tokens, k), dtype=np.int32)
+    off = np.empty((experts + 1,), dtype=np.int32)
+    rc = _load().oracle_topk_to_pos(idx.ctypes.data, tokens, k, experts, pos.ctypes.data, off.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_topk_to_pos failed ({rc})")
+    return pos, off

@@ -7,7 +7,8 @@
  * an abs-max per token or per column group, and the cast to FP8 E4M3 or
  * FP4 E2M1 codes with an fp32 or UE8M0 (power-of-two) scale; the same cast
  * on its own; the deterministic top-k gating that produces the routing
- * weights; and the weighted top-k reduce of the experts' output rows.
+ * weights; the map from each token's top-k slots to its expert rows; and the
+ * weighted top-k reduce of the experts' output rows.
  *
  * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  The GPU library never calls it, and the two share no
@@ -551,5 +552,63 @@ int oracle_moe_reduce(const uint16_t* x, const float* row_scale, const int32_t* 
                 ((float*)out)[t * hidden + c] = o;
         }
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The token/top-k -> position map of "【DeepSeek】TileKernels从入门到精通" ch.3,
+ * section "动态寻址": the table that tells the reduce where each token's j-th
+ * expert output sits.  The pages do not fix the layout of the expanded rows;
+ * the reading here is the plainest one a grouped expert GEMM consumes: the
+ * rows of expert 0 first, then expert 1, ..., and within an expert in token
+ * order.
+ *   Slot (t, j) is present when 0 <= e = idx[t,j] < experts and no earlier
+ *   slot of the same token names e; other slots get pos = -1.
+ *   offsets[e] = number of present slots naming an expert below e
+ *   (offsets[experts] = all present slots);
+ *   pos[t,j] = offsets[e] + number of tokens t' < t with a present slot
+ *   naming e.
+ * ------------------------------------------------------------------------- */
+int oracle_topk_to_pos(const int32_t* idx, int64_t tokens, int64_t k, int64_t experts, int32_t* pos,
+                       int32_t* offsets)
+{
+    if (tokens < 0 || k <= 0 || experts <= 0)
+        return 1;
+    int64_t* count = (int64_t*)calloc((size_t)experts, sizeof(int64_t));
+    if (!count)
+        return 2;
+    /* which slots are present: a valid expert not named earlier in its token */
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int64_t j = 0; j < k; ++j) {
+            const int32_t e = idx[t * k + j];
+            int present = e >= 0 && e < experts;
+            for (int64_t i = 0; present && i < j; ++i)
+                if (idx[t * k + i] == e)
+                    present = 0;
+            pos[t * k + j] = present ? 0 : -1;
+            if (present)
+                count[e] += 1;
+        }
+    }
+    /* expert e's rows start after every row of the experts below it */
+    int64_t run = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        offsets[e] = (int32_t)run;
+        run += count[e];
+    }
+    offsets[experts] = (int32_t)run;
+    /* then the tokens in order: each takes the next row of each of its experts */
+    for (int64_t e = 0; e < experts; ++e)
+        count[e] = 0;
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int64_t j = 0; j < k; ++j) {
+            if (pos[t * k + j] < 0)
+                continue;
+            const int32_t e = idx[t * k + j];
+            pos[t * k + j] = (int32_t)(offsets[e] + count[e]);
+            count[e] += 1;
+        }
+    }
+    free(count);
     return 0;
 }

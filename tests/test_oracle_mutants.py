@@ -73,6 +73,14 @@ MUTANTS = [
      "row[j] = bf16_to_float((uint16_t)(x[r * hidden + j] & 0xFFFEu));"),
     ("cast_bf16_scale_stride", "(uint8_t*)scales + (size_t)(r * groups) * scale_bytes);",
      "(uint8_t*)scales + (size_t)r * scale_bytes);"),
+    # the token/top-k -> position map
+    ("pos_repeat_kept", "if (idx[t * k + i] == e)\n                    present = 0;", "if (0)\n                    present = 0;"),
+    ("pos_offsets_inclusive", "offsets[e] = (int32_t)run;\n        run += count[e];",
+     "run += count[e];\n        offsets[e] = (int32_t)run;"),
+    ("pos_expert_zero_absent", "int present = e >= 0 && e < experts;", "int present = e > 0 && e < experts;"),
+    ("pos_tokens_reversed",
+     "for (int64_t t = 0; t < tokens; ++t) {\n        for (int64_t j = 0; j < k; ++j) {\n            if (pos[t * k + j] < 0)",
+     "for (int64_t t = tokens - 1; t >= 0; --t) {\n        for (int64_t j = 0; j < k; ++j) {\n            if (pos[t * k + j] < 0)"),
 ]
 
 

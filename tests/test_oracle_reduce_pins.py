@@ -176,3 +176,71 @@ def test_routing_generator_structure():
     for t in range(pos.shape[0]):
         q = pos[t][pos[t] >= 0]
         assert len(set(q.tolist())) == len(q)
+
+
+# ---- the token/top-k -> position map ("动态寻址")
+
+def test_topk_to_pos_hand_cases():
+    """Hand-worked cases (tests/golden/topk_to_pos.json): repeated, negative
+    and out-of-range experts, an expert nobody picks, slot order unlike expert
+    order, one expert, no present slot."""
+    import json
+    import os
+    d = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "topk_to_pos.json")))
+    for c in d["cases"]:
+        pos, off = oracle.topk_to_pos(np.array(c["idx"], dtype=np.int32), c["experts"])
+        assert pos.tolist() == c["pos"], c["name"]
+        assert off.tolist() == c["offsets"], c["name"]
+
+
+def _pos_by_sorting(idx: np.ndarray, experts: int):
+    """The same map by a different route: list the present slots as (expert,
+    token, slot), sort them, and number them in that order."""
+    tokens, k = idx.shape
+    present = []
+    for t in range(tokens):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if 0 <= e < experts and e not in seen:
+                present.append((e, t, j))
+            seen.add(e)
+    pos = np.full((tokens, k), -1, dtype=np.int64)
+    for row, (e, t, j) in enumerate(sorted(present)):
+        pos[t, j] = row
+    experts_of_rows = np.array([e for e, _, _ in sorted(present)], dtype=np.int64)
+    off = np.searchsorted(experts_of_rows, np.arange(experts + 1), side="left")
+    return pos, off
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_to_pos_matches_a_stable_sort(seed):
+    rng = np.random.default_rng(seed)
+    tokens, k, experts = int(rng.integers(0, 40)), int(rng.integers(1, 6)), int(rng.integers(1, 9))
+    idx = rng.integers(-2, experts + 2, size=(tokens, k)).astype(np.int32)  # repeats, -1/-2, past the end
+    pos, off = oracle.topk_to_pos(idx, experts)
+    want_pos, want_off = _pos_by_sorting(idx, experts)
+    assert np.array_equal(pos, want_pos)
+    assert np.array_equal(off, want_off)
+
+
+def test_topk_to_pos_invariants():
+    """On a top-k shaped routing (distinct experts per token, a few dropped
+    slots): the present slots take every row in [0, total) once, expert e's
+    rows are [offsets[e], offsets[e+1]) and hold its tokens in increasing
+    order, and absent slots are -1."""
+    rng = np.random.default_rng(5)
+    tokens, k, experts = 3000, 8, 256
+    idx = np.stack([rng.choice(experts, size=k, replace=False) for _ in range(tokens)]).astype(np.int32)
+    idx[rng.random((tokens, k)) < 0.05] = -1
+    pos, off = oracle.topk_to_pos(idx, experts)
+    present = idx >= 0
+    assert (pos[~present] == -1).all()
+    total = int(present.sum())
+    assert off[0] == 0 and off[-1] == total and (np.diff(off) >= 0).all()
+    assert np.array_equal(np.sort(pos[present]), np.arange(total))
+    for e in range(experts):
+        t_of = np.nonzero((idx == e).any(axis=1))[0]
+        rows = pos[idx == e]
+        assert np.array_equal(rows, np.arange(off[e], off[e + 1]))
+        assert len(t_of) == off[e + 1] - off[e]
