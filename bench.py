@@ -1,7 +1,7 @@
 """Benchmark of the fused SwiGLU + top-k weight + FP8/FP4 cast on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-python bench.py --kernel cast|topk|reduce   (the next-row kernels, each on its own workload)
+python bench.py --kernel cast|topk|reduce|pos   (the next-row kernels, each on its own workload)
 python bench.py --suite [--record FILE] [--baseline FILE]
     (every workload of every kernel, one JSON record per case; a case more
     than 15% slower than its committed baseline record is a regression and
@@ -49,6 +49,8 @@ KERNELS = {
     "fused": (("tk_swiglu_cast.hip", "tk_quant.h"), r"\bswiglu_cast_kernel<", "swiglu_cast_kernel"),
     "cast": (("tk_cast.hip", "tk_quant.h"), r"\bcast_kernel<", "cast_kernel"),
     "reduce": (("tk_reduce.hip",), r"\bmoe_reduce_kernel<", "moe_reduce_kernel"),
+    # (three launches per call; the line names the last, which writes the map)
+    "pos": (("tk_pos.hip",), r"\bpos_(?:count|scan|write)_kernel", "pos_write_kernel"),
     # (topk_row_kernel serves the gating workload's shape: 256 experts, 8
     # groups keep 4, top-8)
     "topk": (("tk_topk.hip",), r"\btopk_(?:pair_|quad_|row_)?kernel<", "topk_row_kernel"),
@@ -118,6 +120,9 @@ def aux_workload(kernel: str, wl, seed: int):
         r = wl.REDUCE_WORKLOADS[wl.REDUCE_HEADLINE]
         pos, _, _, _ = wl.make_routing(r, seed)
         return r.name, r.algorithmic_bytes(pos)
+    if kernel == "pos":
+        T, E, k = POS_SHAPE
+        return f"topk_to_pos_t{T}_k{k}_e{E}", T * k * 8 + (E + 1) * 4
     T, E, k, ng, tg = TOPK_SHAPE
     return f"topk_gate_t{T}_e{E}_g{ng}_keep{tg}_top{k}", T * (4 * E + 8 * k)
 
@@ -486,6 +491,7 @@ def _timed(torch, stream, fn, steps, warmup):
 
 CAST_TOKENS, CAST_HIDDEN, CAST_GROUP = 32768, 2048, 128
 TOPK_SHAPE = (16384, 256, 8, 8, 4)  # tokens, experts, k, groups, groups kept
+POS_SHAPE = (16384, 256, 8)  # tokens, experts, k: the gating workload's indices
 
 
 def aux_setup(kernel, torch, np, tk, wl, seed, sets, dev, sh):
@@ -535,6 +541,23 @@ def aux_setup(kernel, torch, np, tk, wl, seed, sets, dev, sh):
                   "n_rows": n_rows, "row_scale": r.row_scale, "global_scale": r.global_scale, "out": "bf16",
                   "layout": "rows grouped by expert, tokens in order within an expert"}
         rows = r.tokens
+    elif kernel == "pos":
+        T, E, k = POS_SHAPE
+        # k distinct experts per token, drawn from the seeded uniform stream
+        u = wl.uniform(wl.stream_key("topk_to_pos", seed, "experts"), 0, T * E).reshape(T, E)
+        ih = np.ascontiguousarray(np.argsort(u, axis=1)[:, :k].astype(np.int32))
+        ids = [torch.from_numpy(ih).to(dev) for _ in range(sets)]
+        ps = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(sets)]
+        offs = [torch.empty((E + 1,), dtype=torch.int32, device=dev) for _ in range(sets)]
+
+        def step(i, stream_handle=sh):
+            j = i % sets
+            rc = tk.tk_topk_to_pos(ids[j], T, k, E, ps[j], offs[j], stream_handle)
+            assert rc == tk.TkStatus.TK_OK, rc
+        metric = "token/top-k -> expert-row map tokens/s and HBM GB/s at 1 MI355X"
+        config = {"workload": name, "tokens": T, "experts": E, "k": k,
+                  "routing": "k distinct experts per token, uniform", "launches_per_call": 3}
+        rows = T
     else:
         T, E, k, ng, tg = TOPK_SHAPE
         key = wl.stream_key("topk_gate", seed, "scores")
@@ -639,8 +662,9 @@ def fused_setup(torch, np, tk, wl, name, seed, nsets, dev, sh):
 # more than the threshold (15% there).
 BASELINES = os.path.join(ROOT, "profiles", "bench_baselines.jsonl")
 REGRESSION_THRESHOLD = 0.15
-SUITE_AUX = ("cast", "reduce", "topk")
-SUITE_OPS = {"fused": "swiglu_cast", "cast": "cast", "reduce": "moe_reduce", "topk": "topk_gate"}
+SUITE_AUX = ("cast", "reduce", "topk", "pos")
+SUITE_OPS = {"fused": "swiglu_cast", "cast": "cast", "reduce": "moe_reduce", "topk": "topk_gate",
+             "pos": "topk_to_pos"}
 
 
 def case_key(kernel: str, params: dict) -> str:
@@ -761,9 +785,9 @@ def main():
                     help="skip the 30 single launches after a 1 GiB cache flush each (protocol_flush30)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the K launches captured in one HIP graph (reported as graph_replay)")
-    ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce"], default="fused",
+    ap.add_argument("--kernel", choices=["fused", "cast", "topk", "reduce", "pos"], default="fused",
                     help="fused (default): the fused SwiGLU + cast; cast: the stand-alone cast; topk: the gating; "
-                         "reduce: the weighted top-k reduce")
+                         "reduce: the weighted top-k reduce; pos: the token/top-k -> expert-row map")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload of every kernel, one JSON record per case, and compare with "
                          "--baseline (exit code 1 when a case is more than --threshold slower)")

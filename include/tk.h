@@ -268,6 +268,39 @@ tk_status tk_moe_reduce(const void* x, const float* row_scale, const int32_t* po
                         float global_scale, int64_t tokens, int64_t k, int64_t hidden, int64_t n_rows,
                         tk_dtype out_dtype, void* out, void* stream);
 
+/*
+ * tk_topk_to_pos: the token/top-k -> expert-row map that tk_moe_reduce gathers
+ * through -- the position map of "【DeepSeek】TileKernels从入门到精通" ch.3, section
+ * "动态寻址".  The expanded rows are laid out as a grouped expert GEMM reads
+ * them: expert 0's rows first, then expert 1's, ...; within an expert, in
+ * token order.
+ *
+ *   Slot (t, j) is present when 0 <= e = topk_idx[t,j] < experts and no earlier
+ *   slot of token t names e (a top-k never repeats an expert; a repeat, like a
+ *   negative entry for a dropped slot, is absent).
+ *   expert_offsets[e] = the number of present slots naming an expert below e;
+ *   expert_offsets[experts] = the number of present slots (rows in all).
+ *   pos[t,j] = expert_offsets[e] + the number of tokens t' < t with a present
+ *   slot naming e, for a present slot; -1 otherwise.
+ *
+ *  topk_idx        int32 [tokens, k] (device), 4-byte aligned.
+ *  tokens          0 <= tokens < 2^31, with tokens * k < 2^31.
+ *  k               1..32 (k > 32: TK_ERR_UNSUPPORTED).
+ *  experts         1..512 (more: TK_ERR_UNSUPPORTED).
+ *  pos             int32 [tokens, k] (device), 4-byte aligned; also the call's
+ *                  working storage (each block of 1024 tokens keeps its
+ *                  per-expert counts there until it writes its rows).
+ *  expert_offsets  int32 [experts + 1] (device), 4-byte aligned; also working
+ *                  storage during the call.  All zero when tokens == 0.
+ * The three buffers must not overlap.  Three kernel launches on `stream`
+ * (one when tokens == 0); the call keeps no pointer after it returns and
+ * allocates nothing.  Returns TK_ERR_INVALID_ARG for violated preconditions,
+ * overlapping buffers or misaligned pointers (before any HIP call), TK_ERR_HIP
+ * if a launch fails.
+ */
+tk_status tk_topk_to_pos(const int32_t* topk_idx, int64_t tokens, int64_t k, int64_t experts, int32_t* pos,
+                         int32_t* expert_offsets, void* stream);
+
 /* tk_status_str: a static, human-readable name for a status code. */
 const char* tk_status_str(tk_status status);
 

@@ -66,6 +66,8 @@ SIGNATURES = {
     "tk_moe_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "tk_topk_to_pos": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tk_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -165,6 +167,12 @@ def tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens, k, hidde
     """See tk_moe_reduce in include/tk.h."""
     return _STATUS[(_ext or load_extension()).tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens,
                                                               k, hidden, n_rows, out_dtype, out, stream)]
+
+
+def tk_topk_to_pos(topk_idx, tokens, k, experts, pos, expert_offsets, stream=None) -> TkStatus:
+    """See tk_topk_to_pos in include/tk.h."""
+    return _STATUS[(_ext or load_extension()).tk_topk_to_pos(topk_idx, tokens, k, experts, pos, expert_offsets,
+                                                               stream)]
 
 
 def tk_status_str(status: int) -> str:

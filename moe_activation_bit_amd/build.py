@@ -35,7 +35,7 @@ def _run(cmd):
 
 
 OBJ_DIR = os.path.join(HERE, "_build")
-TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip", "tk_topk.hip", "tk_reduce.hip"]
+TK_SOURCES = ["tk_swiglu_cast.hip", "tk_cast.hip", "tk_topk.hip", "tk_reduce.hip", "tk_pos.hip"]
 
 
 def _hip_object(src):

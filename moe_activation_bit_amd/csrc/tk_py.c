@@ -208,6 +208,21 @@ static PyObject* py_tk_topk_gate(PyObject* self, PyObject* args)
     return status(rc);
 }
 
+static PyObject* py_tk_topk_to_pos(PyObject* self, PyObject* args)
+{
+    (void)self;
+    void *idx, *pos, *off, *stream = NULL;
+    long long tokens, k, experts;
+    PyObject* so = Py_None;
+    if (!PyArg_ParseTuple(args, "O&LLLO&O&|O", as_ptr, &idx, &tokens, &k, &experts, as_ptr, &pos, as_ptr, &off, &so))
+        return NULL;
+    if (!as_stream(so, &stream))
+        return NULL;
+    tk_status rc;
+    TK_CALL(rc, tk_topk_to_pos((const int32_t*)idx, tokens, k, experts, (int32_t*)pos, (int32_t*)off, stream));
+    return status(rc);
+}
+
 static PyObject* py_tk_moe_reduce(PyObject* self, PyObject* args)
 {
     (void)self;
@@ -248,6 +263,8 @@ static PyMethodDef kMethods[] = {
     {"tk_moe_reduce", py_tk_moe_reduce, METH_VARARGS,
      "tk_moe_reduce(x, row_scale, pos, topk_weight, global_scale, tokens, k, hidden, n_rows, out_dtype, out, "
      "stream=None)"},
+    {"tk_topk_to_pos", py_tk_topk_to_pos, METH_VARARGS,
+     "tk_topk_to_pos(topk_idx, tokens, k, experts, pos, expert_offsets, stream=None)"},
     {NULL, NULL, 0, NULL},
 };
 

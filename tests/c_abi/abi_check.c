@@ -35,6 +35,8 @@ int oracle_moe_reduce(const uint16_t* x, const float* row_scale, const int32_t* 
                       void* out);
 int oracle_topk_gate(const float* scores, int64_t tokens, int64_t experts, int64_t k, int64_t n_group,
                      int64_t topk_group, int normalise, int32_t* idx_out, float* w_out);
+int oracle_topk_to_pos(const int32_t* idx, int64_t tokens, int64_t k, int64_t experts, int32_t* pos,
+                       int32_t* offsets);
 
 static int failures = 0;
 
@@ -108,6 +110,12 @@ static void check_validation(void)
                          TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_INVALID_ARG, "infinite global scale");
     EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), 1.0f, 4, 33, 7168, 32,
                          TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_UNSUPPORTED, "k above 32");
+
+    /* position map */
+    EXPECT(tk_topk_to_pos((const int32_t*)FAKE(0), 4, 33, 256, (int32_t*)FAKE(1), (int32_t*)FAKE(2), NULL) ==
+               TK_ERR_UNSUPPORTED, "position map: k above 32");
+    EXPECT(tk_topk_to_pos((const int32_t*)FAKE(0), 4, 8, 256, (int32_t*)FAKE(0), (int32_t*)FAKE(2), NULL) ==
+               TK_ERR_INVALID_ARG, "position map: pos aliases topk_idx");
 }
 
 static void* dev_copy(const void* host, size_t bytes)
@@ -242,6 +250,23 @@ static void check_topk(void)
     EXPECT(oracle_topk_gate(s, tokens, experts, k, 8, 4, 1, i_ref, w_ref) == 0, "topk: oracle");
     EXPECT(memcmp(i_gpu, i_ref, (size_t)(tokens * k) * 4) == 0, "topk: indices differ");
     EXPECT(memcmp(w_gpu, w_ref, (size_t)(tokens * k) * 4) == 0, "topk: weights differ");
+    /* the gating's indices straight into the position map */
+    int32_t *p_gpu = malloc((size_t)(tokens * k) * 4), *p_ref = malloc((size_t)(tokens * k) * 4);
+    int32_t o_gpu[257], o_ref[257];
+    void* dp = dev_copy(NULL, (size_t)(tokens * k) * 4);
+    void* doff = dev_copy(NULL, 257 * 4);
+    st = tk_topk_to_pos((const int32_t*)di, tokens, k, experts, (int32_t*)dp, (int32_t*)doff, NULL);
+    EXPECT(st == TK_OK, "position map: status %s", tk_status_str(st));
+    HIP_OK(hipDeviceSynchronize());
+    from_dev(p_gpu, dp, (size_t)(tokens * k) * 4);
+    from_dev(o_gpu, doff, 257 * 4);
+    EXPECT(oracle_topk_to_pos(i_ref, tokens, k, experts, p_ref, o_ref) == 0, "position map: oracle");
+    EXPECT(memcmp(p_gpu, p_ref, (size_t)(tokens * k) * 4) == 0, "position map: positions differ");
+    EXPECT(memcmp(o_gpu, o_ref, 257 * 4) == 0, "position map: offsets differ");
+    HIP_OK(hipFree(dp));
+    HIP_OK(hipFree(doff));
+    free(p_gpu);
+    free(p_ref);
     HIP_OK(hipFree(ds));
     HIP_OK(hipFree(di));
     HIP_OK(hipFree(dw));

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["tk_init", "tk_status_str", "tk_swiglu_cast_fp4", "tk_swiglu_cast_fp8",
                                          "tk_swiglu_forward", "tk_cast_fp8", "tk_cast_fp4", "tk_topk_gate",
-                                         "tk_moe_reduce"])
+                                         "tk_moe_reduce", "tk_topk_to_pos"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -207,6 +207,27 @@ def test_moe_reduce_unsupported_and_empty():
     assert reduce(tokens=0, x=None, pos=None, topk_weight=None, out=None) == OK
     # n_rows == 0 lets x be NULL (nothing can be read); with no tokens nothing launches
     assert reduce(tokens=0, n_rows=0, x=None) == OK
+
+
+def to_pos(**kw):
+    a = dict(topk_idx=X, tokens=4, k=8, experts=256, pos=C, expert_offsets=S, stream=0)
+    a.update(kw)
+    return tk.tk_topk_to_pos(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tokens=-1), dict(tokens=2 ** 31), dict(k=0), dict(k=-1), dict(experts=0), dict(experts=-4),
+    dict(tokens=2 ** 28), dict(topk_idx=None), dict(pos=None), dict(expert_offsets=None), dict(topk_idx=X + 2),
+    dict(pos=C + 1), dict(expert_offsets=S + 3), dict(pos=X + 64), dict(expert_offsets=C + 4), dict(expert_offsets=X),
+], ids=str)
+def test_topk_to_pos_invalid_arguments(kw):
+    # (an empty call is not made here: it launches a kernel to zero the offsets)
+    assert to_pos(**kw) == INVALID
+
+
+def test_topk_to_pos_unsupported():
+    assert to_pos(k=33) == UNSUPPORTED
+    assert to_pos(experts=513) == UNSUPPORTED
 
 
 class _FakeTensor:

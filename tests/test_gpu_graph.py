@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture: they allocate nothing, record no
 memset and query nothing that capture forbids, so a caller can capture them
 once and replay.  One graph holds a fused FP8 launch (with the clamp counter),
-an FP4 launch, a stand-alone cast, the gating, the reduce, three launches
+an FP4 launch, a stand-alone cast, the gating and the position map of its
+indices (three launches), the reduce, three launches
 of long rows (groups shared by two waves, and 16 streamed steps), segmented
 groups of 96 columns (fused and cast) and two-pass groups of 8704 columns;
 small launches among them read the 16 KiB table; it is replayed
@@ -63,6 +64,8 @@ def test_capture_and_replay_matches_eager():
         cscales=torch.empty((2 * n, 16), dtype=torch.uint8, device=DEV),
         idx=torch.empty((300, 8), dtype=torch.int32, device=DEV),
         gw=torch.empty((300, 8), dtype=torch.float32, device=DEV),
+        pos=torch.empty((300, 8), dtype=torch.int32, device=DEV),
+        poff=torch.empty((257,), dtype=torch.int32, device=DEV),
         red=torch.empty((r.tokens, r.hidden), dtype=torch.bfloat16, device=DEV),
         lcodes=torch.empty((nl, hl), dtype=torch.uint8, device=DEV),
         lscales=torch.empty((nl, 1), dtype=torch.float32, device=DEV),
@@ -87,6 +90,7 @@ def test_capture_and_replay_matches_eager():
         assert tk.tk_cast_fp8(x, tk.TK_DTYPE_BF16, 2 * n, 2048, 128, tk.TK_SCALE_UE8M0, outs["ccodes"],
                               outs["cscales"], s) == OK
         assert tk.tk_topk_gate(scores, 300, 256, 8, 8, 4, 1, outs["idx"], outs["gw"], s) == OK
+        assert tk.tk_topk_to_pos(outs["idx"], 300, 8, 256, outs["pos"], outs["poff"], s) == OK
         assert tk.tk_moe_reduce(xr, rsd, pd, rwd, r.global_scale, r.tokens, r.k, r.hidden, n_rows,
                                 tk.TK_DTYPE_BF16, outs["red"], s) == OK
         assert tk.tk_swiglu_cast_fp8(xl, None, nl, hl, 0, math.inf, tk.TK_SCALE_FP32, outs["lcodes"],
