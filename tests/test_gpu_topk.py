@@ -205,3 +205,42 @@ def test_topk_nan_group_sums(ng, tg):
     oi, ow = oracle.topk_gate(s, k, ng, tg, False)
     assert np.array_equal(gi, oi), np.argwhere(gi != oi)[:4]
     assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32))
+
+
+def _random_shape(rng):
+    """A valid gating shape: experts up to 512, a group count dividing them
+    with at least 2 experts per group, topk_group groups kept, k at most the
+    candidates and at most 64.  A third of the draws are 128 or 256 experts
+    in 2, 4 or 8 groups whose kept groups fit half a 16-lane row."""
+    if rng.random() < 1 / 3:
+        E = int(rng.choice([128, 256]))
+        ng = int(rng.choice([2, 4, 8]))
+        tg = int(rng.integers(1, max(1, ng // 4) + 1))
+        k = int(rng.integers(1, min(16, tg * (E // ng)) + 1))
+        return E, k, ng, tg
+    while True:
+        E = int(rng.choice([8, 16, 32, 48, 64, 96, 100, 128, 160, 192, 200, 224, 256, 320, 384, 448, 512]))
+        divisors = [g for g in range(1, 33) if E % g == 0 and (g == 1 or E // g >= 2)]
+        ng = int(rng.choice(divisors))
+        tg = int(rng.integers(1, ng + 1))
+        k = int(rng.integers(1, min(64, tg * (E // ng)) + 1))
+        if layout_supported(E, k, ng):
+            return E, k, ng, tg
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_topk_random_shapes(seed):
+    """Seeded random shapes and token counts (every layout the library picks:
+    one token per 16-lane row, four tokens in two passes, two tokens, one
+    token per wave), scores with ties on a third of the rows."""
+    rng = np.random.default_rng(1000 + seed)
+    E, k, ng, tg = _random_shape(rng)
+    T = int(rng.integers(1, 700))
+    normalise = int(rng.integers(0, 2))
+    print("[gpu-case] topk random", seed, (E, k, ng, tg), T, normalise, flush=True)
+    u = wl.uniform(wl.stream_key("topk_random", seed, "scores"), 0, T * E).reshape(T, E)
+    s = np.where(np.arange(T)[:, None] % 3 == 0, np.floor(u * 8) / 8, u - 0.5).astype(np.float32)
+    gi, gw = run(s, k, ng, tg, normalise)
+    oi, ow = oracle.topk_gate(s, k, ng, tg, bool(normalise))
+    assert np.array_equal(gi, oi), np.argwhere(gi != oi)[:4]
+    assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32))
