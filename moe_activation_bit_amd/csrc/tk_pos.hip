@@ -47,13 +47,22 @@ constexpr int kScanThreads = 1024;
 // This token's present slots: slot j is present when its expert is in range
 // and no earlier slot names it.  KMAX bounds k at compile time so that the
 // slot list stays in registers.
-template <int KMAX>
+// VEC (k == 8, idx 16-byte aligned): the token's 8 slots as two 16-byte loads.
+template <int KMAX, bool VEC>
 __device__ __forceinline__ void load_slots(const int32_t* __restrict__ idx, uint32_t t, uint32_t k, uint32_t experts,
                                            int32_t (&e)[KMAX], bool (&present)[KMAX])
 {
+    if constexpr (VEC) {
+        static_assert(KMAX == 8, "vector slots are 8 per token");
+        const int4* p = reinterpret_cast<const int4*>(idx + (size_t)t * 8);
+        const int4 a = p[0], b = p[1];
+        e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
+        e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        e[j] = (uint32_t)j < k ? idx[(size_t)t * k + j] : -1;
+        for (int j = 0; j < KMAX; ++j)
+            e[j] = (uint32_t)j < k ? idx[(size_t)t * k + j] : -1;
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         bool p = (uint32_t)j < k && e[j] >= 0 && (uint32_t)e[j] < experts;
@@ -129,27 +138,36 @@ __device__ __forceinline__ uint32_t bitmap_prefix(Bitmap<B>& bm, uint32_t expert
     return run; // this block's count of the expert
 }
 
-template <int B, int KMAX>
+// VEC (k == 8, pos 16-byte aligned): the token's 8 rows as two 16-byte stores.
+template <int B, int KMAX, bool VEC>
 __device__ __forceinline__ void write_rows(const Bitmap<B>& bm, uint32_t experts, uint32_t tl, size_t t, uint32_t k,
                                            const int32_t* off, const int32_t* base, const int32_t (&e)[KMAX],
                                            const bool (&present)[KMAX], int32_t* pos)
 {
+    int32_t p[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        if ((uint32_t)j >= k)
-            break;
-        int32_t p = -1;
+        p[j] = -1;
         if (present[j]) {
             const uint32_t i = (tl >> 5) * experts + e[j];
-            p = off[e[j]] + base[e[j]] + (int32_t)bm.before[i] +
-                (int32_t)__builtin_popcount(bm.bits[i] & ((1u << (tl & 31u)) - 1u));
+            p[j] = off[e[j]] + base[e[j]] + (int32_t)bm.before[i] +
+                   (int32_t)__builtin_popcount(bm.bits[i] & ((1u << (tl & 31u)) - 1u));
         }
-        pos[t * k + j] = p;
+    }
+    if constexpr (VEC) {
+        int4* q = reinterpret_cast<int4*>(pos + t * 8);
+        q[0] = make_int4(p[0], p[1], p[2], p[3]);
+        q[1] = make_int4(p[4], p[5], p[6], p[7]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if ((uint32_t)j < k)
+                pos[t * k + j] = p[j];
     }
 }
 
 // All tokens in one block (tokens <= B).
-template <int B, int KMAX>
+template <int B, int KMAX, bool VEC>
 __global__ __launch_bounds__(B) void pos_single_kernel(const int32_t* __restrict__ idx, uint32_t tokens, uint32_t k,
                                                        uint32_t experts, int32_t* __restrict__ pos,
                                                        int32_t* __restrict__ offsets)
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(B) void pos_single_kernel(const int32_t* __restrict
     bool present[KMAX];
     const bool has = tl < tokens;
     if (has)
-        load_slots<KMAX>(idx, tl, k, experts, e, present);
+        load_slots<KMAX, VEC>(idx, tl, k, experts, e, present);
     __syncthreads();
     bitmap_fill<B, KMAX>(bm, experts, tl, has, e, present);
     __syncthreads();
@@ -192,10 +210,10 @@ __global__ __launch_bounds__(B) void pos_single_kernel(const int32_t* __restrict
     for (uint32_t x = tl; x <= experts; x += B)
         offsets[x] = off[x];
     if (has)
-        write_rows<B, KMAX>(bm, experts, tl, tl, k, off, zero, e, present, pos);
+        write_rows<B, KMAX, VEC>(bm, experts, tl, tl, k, off, zero, e, present, pos);
 }
 
-template <int B, int KMAX>
+template <int B, int KMAX, bool VEC>
 __global__ __launch_bounds__(B) void pos_count_kernel(const int32_t* __restrict__ idx, uint32_t tokens, uint32_t k,
                                                       uint32_t experts, int32_t* pos, int32_t* offsets)
 {
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(B) void pos_count_kernel(const int32_t* __restrict_
     if (t < tokens) {
         int32_t e[KMAX];
         bool present[KMAX];
-        load_slots<KMAX>(idx, t, k, experts, e, present);
+        load_slots<KMAX, VEC>(idx, t, k, experts, e, present);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (present[j])
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(kScanThreads) void pos_scan_kernel(uint32_t blocks,
         offsets[experts] = (int32_t)all;
 }
 
-template <int B, int KMAX>
+template <int B, int KMAX, bool VEC>
 __global__ __launch_bounds__(B) void pos_write_kernel(const int32_t* __restrict__ idx, uint32_t tokens, uint32_t k,
                                                       uint32_t experts, const int32_t* __restrict__ offsets,
                                                       int32_t* pos)
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(B) void pos_write_kernel(const int32_t* __restrict_
     bool present[KMAX];
     const bool has = t < tokens;
     if (has)
-        load_slots<KMAX>(idx, t, k, experts, e, present);
+        load_slots<KMAX, VEC>(idx, t, k, experts, e, present);
     __syncthreads();
     bitmap_fill<B, KMAX>(bm, experts, tl, has, e, present);
     __syncthreads();
@@ -340,7 +358,7 @@ __global__ __launch_bounds__(B) void pos_write_kernel(const int32_t* __restrict_
     }
     __syncthreads();
     if (has)
-        write_rows<B, KMAX>(bm, experts, tl, t, k, off, base, e, present, pos);
+        write_rows<B, KMAX, VEC>(bm, experts, tl, t, k, off, base, e, present, pos);
 }
 
 __global__ void zero_offsets_kernel(int32_t* offsets, uint32_t n)
@@ -358,7 +376,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn)
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-template <int B, int KMAX>
+template <int B, int KMAX, bool VEC>
 void launch_blocks(const int32_t* idx, uint32_t tokens, uint32_t k, uint32_t experts, int32_t* pos, int32_t* offsets,
                    hipStream_t s)
 {
@@ -366,15 +384,15 @@ void launch_blocks(const int32_t* idx, uint32_t tokens, uint32_t k, uint32_t exp
     uint32_t lanes = 1;
     while (lanes * 2 * experts <= (uint32_t)kScanThreads)
         lanes *= 2;
-    hipLaunchKernelGGL((pos_count_kernel<B, KMAX>), dim3(blocks), dim3(B), 0, s, idx, tokens, k, experts, pos,
+    hipLaunchKernelGGL((pos_count_kernel<B, KMAX, VEC>), dim3(blocks), dim3(B), 0, s, idx, tokens, k, experts, pos,
                        offsets);
     hipLaunchKernelGGL(pos_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blocks, (size_t)B * k, experts, lanes,
                        pos, offsets);
-    hipLaunchKernelGGL((pos_write_kernel<B, KMAX>), dim3(blocks), dim3(B), 0, s, idx, tokens, k, experts, offsets,
-                       pos);
+    hipLaunchKernelGGL((pos_write_kernel<B, KMAX, VEC>), dim3(blocks), dim3(B), 0, s, idx, tokens, k, experts,
+                       offsets, pos);
 }
 
-template <int KMAX>
+template <int KMAX, bool VEC>
 void launch_pos(const int32_t* idx, uint32_t tokens, uint32_t k, uint32_t experts, int32_t* pos, int32_t* offsets,
                 hipStream_t s)
 {
@@ -383,20 +401,20 @@ void launch_pos(const int32_t* idx, uint32_t tokens, uint32_t k, uint32_t expert
     // (a full block must have room for its parked counts), or 1024 from
     // 65536 tokens on (fewer blocks for the one-workgroup scan)
     if (tokens <= 256)
-        hipLaunchKernelGGL((pos_single_kernel<256, KMAX>), dim3(1), dim3(256), 0, s, idx, tokens, k, experts, pos,
+        hipLaunchKernelGGL((pos_single_kernel<256, KMAX, VEC>), dim3(1), dim3(256), 0, s, idx, tokens, k, experts, pos,
                            offsets);
     else if (tokens <= 512)
-        hipLaunchKernelGGL((pos_single_kernel<512, KMAX>), dim3(1), dim3(512), 0, s, idx, tokens, k, experts, pos,
+        hipLaunchKernelGGL((pos_single_kernel<512, KMAX, VEC>), dim3(1), dim3(512), 0, s, idx, tokens, k, experts, pos,
                            offsets);
     else if (tokens <= 1024)
-        hipLaunchKernelGGL((pos_single_kernel<1024, KMAX>), dim3(1), dim3(1024), 0, s, idx, tokens, k, experts, pos,
+        hipLaunchKernelGGL((pos_single_kernel<1024, KMAX, VEC>), dim3(1), dim3(1024), 0, s, idx, tokens, k, experts, pos,
                            offsets);
     else if (tokens >= 65536)
-        launch_blocks<1024, KMAX>(idx, tokens, k, experts, pos, offsets, s);
+        launch_blocks<1024, KMAX, VEC>(idx, tokens, k, experts, pos, offsets, s);
     else if (256u * k >= experts)
-        launch_blocks<256, KMAX>(idx, tokens, k, experts, pos, offsets, s);
+        launch_blocks<256, KMAX, VEC>(idx, tokens, k, experts, pos, offsets, s);
     else
-        launch_blocks<512, KMAX>(idx, tokens, k, experts, pos, offsets, s);
+        launch_blocks<512, KMAX, VEC>(idx, tokens, k, experts, pos, offsets, s);
 }
 
 } // namespace
@@ -424,9 +442,12 @@ extern "C" tk_status tk_topk_to_pos(const int32_t* topk_idx, int64_t tokens, int
                            expert_offsets, (uint32_t)(experts + 1));
         return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
     }
-    if (k <= 8)
-        launch_pos<8>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
+    // k == 8 with both arrays 16-byte aligned: each token's slots in two 16-byte loads and stores
+    if (k == 8 && ((uintptr_t)topk_idx & 15) == 0 && ((uintptr_t)pos & 15) == 0)
+        launch_pos<8, true>(topk_idx, (uint32_t)tokens, 8u, (uint32_t)experts, pos, expert_offsets, s);
+    else if (k <= 8)
+        launch_pos<8, false>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
     else
-        launch_pos<32>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
+        launch_pos<32, false>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
     return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
 }

@@ -121,3 +121,25 @@ def test_gating_then_map_then_reduce():
     torch.cuda.synchronize()
     want = oracle.moe_reduce(xb, op, ow, None, 1.0, True)
     assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("tokens", [300, 5000])
+def test_topk_to_pos_k8_unaligned(tokens):
+    """k = 8 with the index and position arrays 4 bytes past a 16-byte
+    boundary: the per-slot loads and stores (16-byte aligned arrays take
+    two 16-byte accesses per token) give the same map."""
+    print("[gpu-case] topk_to_pos k=8 unaligned", tokens, flush=True)
+    E, k = 256, 8
+    idx = routing(tokens, k, E, seed=tokens + 77, drop=0.05, noise=True)
+    di = torch.zeros(tokens * k + 4, dtype=torch.int32, device=DEV)
+    di[1:1 + tokens * k] = torch.from_numpy(idx.reshape(-1)).to(DEV)
+    dp = torch.full((tokens * k + 4,), 99, dtype=torch.int32, device=DEV)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    assert (di.data_ptr() + 4) % 16 == 4 and (dp.data_ptr() + 4) % 16 == 4
+    assert tk.tk_topk_to_pos(di.data_ptr() + 4, tokens, k, E, dp.data_ptr() + 4, off) == OK
+    torch.cuda.synchronize()
+    op, oo = oracle.topk_to_pos(idx, E)
+    p = dp.cpu().numpy()
+    assert p[0] == 99 and (p[1 + tokens * k:] == 99).all()
+    assert np.array_equal(p[1:1 + tokens * k].reshape(tokens, k), op)
+    assert np.array_equal(off.cpu().numpy(), oo)
