@@ -41,7 +41,8 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and return after the launch is enqueued.
  *  - Outputs must not overlap inputs.
- *  - n == 0 returns TK_OK and launches nothing.
+ *  - n == 0 (tokens == 0) returns TK_OK and launches nothing; the one
+ *    exception is tk_topk_to_pos, which still writes its all-zero offsets.
  *  - Errors are returned, never thrown; on any error nothing is launched
  *    except for TK_ERR_HIP, which reports a failed launch or device query.
  *  - Inputs are expected to be finite.  A NaN or infinite input gives codes
