@@ -250,8 +250,9 @@ tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t experts, int
  *               be NULL when n_rows == 0.
  *  row_scale    fp32 [n_rows] (device), 4-byte aligned, or NULL.
  *  pos          int32 [tokens, k] (device), 4-byte aligned: the row of each
- *               (token, slot).  Entries are range-checked on the device, so a
- *               bad entry drops its slot instead of reading out of bounds.
+ *               (token, slot), as tk_topk_to_pos builds it from top-k indices.
+ *               Entries are range-checked on the device, so a bad entry drops
+ *               its slot instead of reading out of bounds.
  *  topk_weight  fp32 [tokens, k] (device), 4-byte aligned.
  *  global_scale a finite fp32 factor applied once to each sum.
  *  tokens       0 <= tokens < 2^31;  k: 1..32 (k > 32: TK_ERR_UNSUPPORTED).
