@@ -207,7 +207,8 @@ tk_status tk_cast_fp4(const void* x, tk_dtype in_dtype, int64_t n, int64_t hidde
  *   is RN(best + second best) of its members; only the topk_group best groups'
  *   members are candidates.  Then k times: the best remaining candidate.
  *
- *  scores       fp32 [tokens, experts], row-major, 4-byte aligned (device).
+ *  scores       fp32 [tokens, experts], row-major, 4-byte aligned (device);
+ *               +-inf allowed, NaN not (a NaN score's rank is unspecified).
  *  tokens       0 <= tokens < 2^31.
  *  experts      1..512;  k: 1..64 and at most the number of candidates.
  *  n_group      divides experts (1 = no groups); topk_group in 1..n_group;

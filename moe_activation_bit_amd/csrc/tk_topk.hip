@@ -43,7 +43,13 @@
 //      wave-wide instructions serves both tokens.
 //      Output lane j then re-reads pick j's own score, and the
 //      normalising sum adds those k values in pick order after the rounds.
-// No LDS traffic beyond the two lane shuffles of the group rank.
+//      In the four-token kernels a pick's weight is its key's value instead
+//      (one read again only for a zero key, whose sign the key does not keep).
+// The one- and two-token kernels use no LDS beyond the two lane shuffles of
+// the group rank.  topk_row_kernel takes each group's two best on the scores
+// themselves (v_med3_f32) and maps to keys only the kept lanes, after the
+// move.  Scores are taken to be non-NaN: a NaN score may be ranked
+// differently by different kernels.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -117,6 +123,36 @@ __device__ __forceinline__ void merge_top2(uint32_t& a1, uint32_t& a2)
     const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a1, CTRL, 0xF, 0xF, false);
     const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a2, CTRL, 0xF, 0xF, false);
     merge_top2_from(a1, a2, b1, b2);
+}
+
+// +inf or -inf in a scalar register whose value the compiler does not see:
+// a median against it stays one v_med3_f32 (against a known infinity the
+// compiler turns it into an IEEE max or min, which first quiets each loaded
+// operand with an instruction of its own)
+__device__ __forceinline__ float opaque_inf(bool negative)
+{
+    uint32_t b;
+    if (negative)
+        asm volatile("s_mov_b32 %0, 0xff800000" : "=s"(b));
+    else
+        asm volatile("s_mov_b32 %0, 0x7f800000" : "=s"(b));
+    return ffrom(b);
+}
+
+// max / min of two non-NaN floats, as a median against an infinity
+__device__ __forceinline__ float fmax2(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+__device__ __forceinline__ float fmin2(float a, float b, float ninf) { return __builtin_amdgcn_fmed3f(a, b, ninf); }
+
+// (a1, a2) <- the two largest of (a1, a2) and the pair CTRL brings from
+// another lane, each pair ordered: the second is the median of the two
+// firsts and the larger second
+template <int CTRL>
+__device__ __forceinline__ void merge_top2f(float& a1, float& a2, float pinf)
+{
+    const float b1 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a1), CTRL, 0xF, 0xF, false));
+    const float b2 = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(a2), CTRL, 0xF, 0xF, false));
+    a2 = __builtin_amdgcn_fmed3f(a1, b1, fmax2(a2, b2, pinf));
+    a1 = fmax2(a1, b1, pinf);
 }
 
 template <int C>
@@ -485,17 +521,19 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
 
 // The part of the four-tokens-per-wave kernels after the kept lanes have been
 // written to LDS: row r = lane / 16 holds token t0 + r, its `filled_lanes`
-// first lanes a kept lane's C keys each (index order along the row) and
-// s_src the expert index of each lane's first key.  Each lane sorts its keys,
-// the k rounds run on the rows (a DPP maximum inside each 16-lane row, so one
-// round serves four tokens; a round's winners write their pick into s_pick at
-// the round's position), and output lane q of row r stores pick q.
-template <int C, bool K8>
+// first lanes a kept lane's C keys each (index order along the row; RAW: the
+// scores themselves, mapped to keys here) and s_src the expert index of each
+// lane's first key.  Each lane sorts its keys, the k rounds run on the rows (a
+// DPP maximum inside each 16-lane row, so one round serves four tokens; a
+// round's winners write their pick and its key into s_pick at the round's
+// position), and output lane q of row r stores pick q, its weight the key's
+// value.
+template <int C, bool K8, bool RAW>
 __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
                                                  uint32_t k, uint32_t filled_lanes, int normalise,
                                                  int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                  uint32_t t0, uint32_t lane, const uint4 (*s_keys)[kWave],
-                                                 const uint32_t* s_src, int32_t* s_pick)
+                                                 const uint32_t* s_src, uint2* s_pick)
 {
     constexpr int kWords = C > 4 ? 2 : 1;
     const uint32_t q = lane & 15u;
@@ -514,12 +552,15 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
         }
 #pragma unroll
         for (int j = 0; j < C; ++j)
-            key[j] = filled ? w8[j] : 0u;
+            key[j] = RAW ? ordered(ffrom(w8[j])) : w8[j];
     }
-    // the expert index of this lane's first slot (an empty lane's picks
-    // never happen, since k is at most the candidates; it points at expert 0)
-    const uint32_t base = filled ? s_src[lane] : 0u;
+    // the expert index of this lane's first slot (read by every lane: an
+    // empty lane never wins, since k is at most the candidates)
+    const uint32_t base = s_src[lane];
     sort_lane<C>(key, idx);
+    // a lane past the row's filled ones sorts whatever its LDS words hold; an
+    // empty head keeps it from ever winning, so its other keys are never read
+    key[0] = filled ? key[0] : 0u;
     // slot lists, head lowest, 3 bits each: the slots themselves (7 - idx)
     uint32_t slots = 0;
 #pragma unroll
@@ -528,7 +569,7 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
     slots ^= 0xFFFFFFu;
 
     // ---- k rounds, four tokens at once
-    int32_t* pick_row = &s_pick[row << 4];
+    uint2* pick_row = &s_pick[row << 4];
     auto round = [&](uint32_t it, uint32_t depth) {
         uint32_t m = key[0];
         m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
@@ -540,7 +581,7 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
         // maximum is some lane's head, so no borrow crosses a row)
         const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
         if (__builtin_amdgcn_inverse_ballot_w64(win)) {
-            pick_row[it] = (int32_t)(C == 8 ? (base | (slots & 7u)) : (base + (slots & 7u)));
+            pick_row[it] = make_uint2(C == 8 ? (base | (slots & 7u)) : (base + (slots & 7u)), key[0]);
 #pragma unroll
             for (int j = 0; j + 1 < C; ++j)
                 if (j + 1u < depth)
@@ -570,15 +611,30 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
     // ---- output lane q of row r: pick q of token t0 + r
     const uint32_t t = t0 + row;
     const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
-    const int32_t my_idx = q < k ? s_pick[lane] : 0;
-    const float my_w = q < k ? s_row[min((uint32_t)my_idx, experts - 1u)] : 0.0f;
+    const uint2 pk = s_pick[lane];
+    const int32_t my_idx = q < k ? (int32_t)pk.x : 0;
+    const uint32_t my_key = pk.y;
+    // the pick's score is its key's value; a zero key stands for either sign
+    // of zero, so only then is the score read again
+    float my_w = q < k ? unordered(my_key) : 0.0f;
+    if (q < k && my_key == 0x80000000u)
+        my_w = s_row[min((uint32_t)my_idx, experts - 1u)];
     float sum = 0.0f;
     if (normalise) {
         // running sum in pick order inside each row (row_shr:1 reads 0 into a
         // row's first lane): lane k-1 ends with 0 + w[0] + ... + w[k-1]
         float run = 0.0f;
-        for (uint32_t it = 0; it < k; ++it)
+        auto add_step = [&]() {
             run = ffrom((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(run), 0x111, 0xF, 0xF, true)) + my_w;
+        };
+        if constexpr (K8) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+                add_step();
+        } else {
+            for (uint32_t it = 0; it < k; ++it)
+                add_step();
+        }
         sum = ffrom((uint32_t)__builtin_amdgcn_ds_bpermute((int)(((row << 4) + k - 1u) << 2), (int)fbits(run)));
     }
     if (q < k && t < tokens) {
@@ -608,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void topk_quad_kernel(const float* __rest
     constexpr int kWords = C > 4 ? 2 : 1; // 16-byte words of a lane's candidate keys
     __shared__ uint4 s_keys[kWaves][kWords][kWave];
     __shared__ uint32_t s_src[kWaves][kWave];
-    __shared__ int32_t s_pick[kWaves][kWave]; // [row * 16 + round]
+    __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wv = threadIdx.x / kWave;
     const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
@@ -667,24 +723,27 @@ __global__ __launch_bounds__(kThreads) void topk_quad_kernel(const float* __rest
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    quad_rows_finish<C, K8>(scores, tokens, experts, k, topk_group << gl_log2, normalise, idx_out, w_out, t0, lane,
+    quad_rows_finish<C, K8, false>(scores, tokens, experts, k, topk_group << gl_log2, normalise, idx_out, w_out, t0, lane,
                             s_keys[wv], s_src[wv], s_pick[wv]);
 }
 
 // Group ranks within 16-lane rows (one token per row, 16 >> GL groups of
-// 2^GL lanes): group H's sum reaches every lane of the row by row_newbcast
-// from the group's first lane, and a lane counts the groups that beat its own
-// ("a beats b": larger sum, or equal sums and the smaller group index).
+// 2^GL lanes): group H's sum, as an order-preserving key, reaches every lane
+// of the row by row_newbcast from the group's first lane, and a lane counts
+// the groups that beat its own ("a beats b": larger sum, or equal sums and the
+// smaller group index): a group below its own by a key at least its own
+// (above gkey_less = gkey - 1), one above it by a larger key.
 template <int GL, int H = 0>
-__device__ __forceinline__ void row_group_rank(float gsum, uint32_t& rank)
+__device__ __forceinline__ void row_group_rank(uint32_t gkey, uint32_t gkey_less, uint32_t& rank)
 {
     if constexpr ((H << GL) < 16) {
-        const float gh = ffrom((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(gsum), 0x150 + (H << GL), 0xF, 0xF, false));
-        // the lanes of groups above H, whose equal sums lose to group H: a constant lane mask
+        const uint32_t gh = (uint32_t)__builtin_amdgcn_mov_dpp((int)gkey, 0x150 + (H << GL), 0xF, 0xF, false);
+        // the lanes of groups above H, whose equal sums lose to group H (a
+        // constant lane mask), count group H when its key is at least theirs
         constexpr uint64_t kAbove = (uint64_t)(0xFFFFu & ~((1u << ((H + 1) << GL)) - 1u)) * 0x0001000100010001ull;
-        const bool loses_tie = __builtin_amdgcn_inverse_ballot_w64(kAbove);
-        rank += (gh > gsum || (gh == gsum && loses_tie)) ? 1u : 0u;
-        row_group_rank<GL, H + 1>(gsum, rank);
+        const uint32_t thr = __builtin_amdgcn_inverse_ballot_w64(kAbove) ? gkey_less : gkey;
+        rank += gh > thr ? 1u : 0u;
+        row_group_rank<GL, H + 1>(gkey, gkey_less, rank);
     }
 }
 
@@ -709,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     static_assert(C16 == 8 || C16 == 16, "8 or 16 experts per lane");
     __shared__ uint4 s_keys[kWaves][kWords][kWave];
     __shared__ uint32_t s_src[kWaves][kWave];
-    __shared__ int32_t s_pick[kWaves][kWave]; // [row * 16 + round]
+    __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wv = threadIdx.x / kWave;
     const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
@@ -719,28 +778,35 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     const uint32_t row = lane >> 4;
     // a wave past the last token repeats it in its other rows and stores nothing from them
     const float* s_row = scores + (size_t)min(t0 + row, tokens - 1u) * kExperts;
-    uint32_t key[C16];
+    float x[C16];
 #pragma unroll
     for (int j = 0; j < C16; ++j)
-        key[j] = ordered(s_row[q * C16 + j]);
-    // the lane's two best keys, unsorted, then the group's over its 2^GL lanes
-    uint32_t a1 = max(key[0], key[1]), a2 = min(key[0], key[1]);
+        x[j] = s_row[q * C16 + j];
+    // the lane's two best scores, then the group's over its 2^GL lanes (as
+    // values: the sign of a zero does not change a sum's comparisons)
+    const float pinf = opaque_inf(false);
+    float a1 = fmax2(x[0], x[1], pinf), a2 = fmin2(x[0], x[1], opaque_inf(true));
 #pragma unroll
     for (int j = 2; j < C16; ++j) {
-        a2 = max(a2, min(a1, key[j]));
-        a1 = max(a1, key[j]);
+        a2 = __builtin_amdgcn_fmed3f(a1, a2, x[j]);
+        a1 = fmax2(a1, x[j], pinf);
     }
     if constexpr (GL >= 1)
-        merge_top2<0xB1>(a1, a2); // quad_perm [1,0,3,2]
+        merge_top2f<0xB1>(a1, a2, pinf); // quad_perm [1,0,3,2]
     if constexpr (GL >= 2)
-        merge_top2<0x4E>(a1, a2); // quad_perm [2,3,0,1]
+        merge_top2f<0x4E>(a1, a2, pinf); // quad_perm [2,3,0,1]
     if constexpr (GL >= 3)
-        merge_top2<0x141>(a1, a2); // row_half_mirror
-    float gsum = unordered(a1) + unordered(a2);
+        merge_top2f<0x141>(a1, a2, pinf); // row_half_mirror
+    float gsum = a1 + a2;
     if (gsum != gsum) // +inf + -inf: a NaN group score ranks as -inf
         gsum = -INFINITY;
     uint32_t rank = 0;
-    row_group_rank<GL>(gsum, rank);
+    // the sums as keys (above 0, -0 == +0), so that one unsigned compare per
+    // group decides it
+    const uint32_t gkey = ordered(gsum);
+    uint32_t gkey_less = gkey - 1u; // opaque to the compiler, so each group's threshold stays one select
+    asm volatile("" : "+v"(gkey_less));
+    row_group_rank<GL>(gkey, gkey_less, rank);
     const bool kept = rank < topk_group;
     // kept groups below this lane's own in its row: the last lanes of kept
     // groups below it, counted over the wave and less those of the rows above
@@ -756,15 +822,15 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int w = 0; w < kWords; ++w)
-                s_keys[wv][w][d + h] = make_uint4(key[h * C + 4 * w], key[h * C + 4 * w + 1], key[h * C + 4 * w + 2],
-                                                  key[h * C + 4 * w + 3]);
+                s_keys[wv][w][d + h] = make_uint4(fbits(x[h * C + 4 * w]), fbits(x[h * C + 4 * w + 1]),
+                                                  fbits(x[h * C + 4 * w + 2]), fbits(x[h * C + 4 * w + 3]));
             s_src[wv][d + h] = q * C16 + h * C;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    quad_rows_finish<C, K8>(scores, tokens, kExperts, k, 2u * (topk_group << GL), normalise, idx_out, w_out, t0, lane,
+    quad_rows_finish<C, K8, true>(scores, tokens, kExperts, k, 2u * (topk_group << GL), normalise, idx_out, w_out, t0, lane,
                             s_keys[wv], s_src[wv], s_pick[wv]);
 }
 
