@@ -362,6 +362,58 @@ def stream_ceiling(torch, dev, rows: int, hidden: int, reps: int = 10, rounds: i
     return res
 
 
+# The next-row kernels' read:write mixes for the plain-stream probe: 16-byte
+# vectors read and bytes written per probe thread (the cast: 16 bytes of bf16
+# in, 8 code bytes out; the gating: 64 bytes of scores in, 4 bytes of indices
+# and weights out).  The scale bytes the cast also writes (1/256 of its
+# traffic) are left out.
+STREAM_MIX = {"cast": (1, 8), "topk": (4, 4)}
+
+
+def stream_mix(torch, dev, in_bytes: int, rv: int, wb: int, sets: int, reps: int = 200, rounds: int = 3):
+    """GB/s of a plain non-temporal stream with a kernel's read:write mix:
+    in_bytes read and in_bytes * wb / (16 * rv) written per launch, no
+    arithmetic, over `sets` rotating buffer sets like the kernel's own line;
+    median of `rounds` rounds of `reps` launches."""
+    import ctypes
+    import statistics
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_activation_bit_amd", "libstreamceil.so"))
+    lib.stream_read_n_write.restype = ctypes.c_int
+    lib.stream_read_n_write.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                        ctypes.c_uint32, ctypes.c_void_p]
+    n = in_bytes // (16 * rv)
+    assert n * 16 * rv == in_bytes and n > 0
+    out_bytes = n * wb
+    ins = [torch.ones(in_bytes // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
+    outs = [torch.empty((out_bytes + 3) // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+
+    def launch(i):
+        assert lib.stream_read_n_write(ins[i % sets].data_ptr(), outs[i % sets].data_ptr(), n, rv, wb, sh) == 0
+
+    for i in range(max(50, sets)):
+        launch(i)
+    times = []
+    for _ in range(rounds):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            launch(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / 1e3 / reps)
+    t = statistics.median(times)
+    del ins, outs
+    torch.cuda.empty_cache()
+    return {"stream_GBs": round((in_bytes + out_bytes) / t / 1e9, 1), "us_per_launch": round(t * 1e6, 3),
+            "bytes_per_launch": in_bytes + out_bytes,
+            "kernel": f"read_n_write_kernel<{rv}, {wb}>: {n} threads, {16 * rv} bytes read and {wb} written "
+                      f"each, non-temporal, non-persistent; {sets} rotating sets; median of {rounds} rounds of "
+                      f"{reps} launches"}
+
+
 def cpu_baseline(w, seed: int, rows: int, single_rows: int = 1024):
     """The oracle on `rows` rows of the workload, split over host threads (the
     reported value), and on `single_rows` of them on one thread."""
@@ -611,9 +663,17 @@ def bench_aux(args, torch, np, tk, wl):
                         "avg_launch_us": round(avg * 1e6, 3)},
            "regime": regime(nbytes, sets, avg),
            "cpu_baseline": None}
+    if args.kernel in STREAM_MIX and not args.no_ceiling:
+        # what a plain stream with the kernel's own read:write mix reaches
+        rv, wb = STREAM_MIX[args.kernel]
+        in_bytes = (CAST_TOKENS * 2 * CAST_HIDDEN * 2 if args.kernel == "cast"
+                    else TOPK_SHAPE[0] * TOPK_SHAPE[1] * 4)
+        ceil = stream_mix(torch, dev, in_bytes, rv, wb, sets)
+        out["roofline"]["measured_ceiling"] = ceil
+        out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["stream_GBs"], 4)
     if args.kernel == "topk":
-        # the gating is bound by VALU issue, not by its bytes: VALU instructions
-        # per launch (counter record) against the chip's issue rate
+        # the gating's VALU instructions per launch (counter record) against
+        # the chip's issue rate, beside its bytes
         v = valu_for(name, "topk")
         out["valu_issue"] = None if v is None else {
             "insts_per_launch": round(v), "achieved": round(v / avg / 1e9, 2), "peak": VALU_PEAK_INSTS_PER_S / 1e9,

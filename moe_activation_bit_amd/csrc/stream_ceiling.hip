@@ -17,8 +17,13 @@
 //                 16: sc1, sums of these); the grid is either one unit of SPU
 //                 steps per wave (non-persistent) or a persistent grid of
 //                 blocks_per_cu 256-thread workgroups per CU striding over the
-//                 units in the XCD-contiguous order the fused kernel uses.
-// The benchmark times them with HIP events beside the fused kernel.
+//                 units in the XCD-contiguous order the fused kernel uses;
+//   read_n_write: another kernel's read:write mix without its arithmetic:
+//                 each of n threads reads RV 16-byte vectors (vector j of
+//                 thread i at j*n + i, so each load instruction of a wave is
+//                 one contiguous KiB) and writes WB bytes at i*WB;
+//                 non-persistent, non-temporal loads and stores.
+// The benchmark times them with HIP events beside the kernels they bound.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,6 +53,42 @@ __global__ __launch_bounds__(256) void read_only_kernel(const v4u* __restrict__ 
     const v4u a = __builtin_nontemporal_load(in + i);
     if ((a.x ^ a.y ^ a.z ^ a.w) == 0x9E3779B9u) // practically never: keeps the load alive
         sink[0] = a.x;
+}
+
+template <int RV, int WB>
+__global__ __launch_bounds__(256) void read_n_write_kernel(const v4u* __restrict__ in, char* __restrict__ out,
+                                                           uint64_t n)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n)
+        return;
+    v4u a[RV];
+#pragma unroll
+    for (int j = 0; j < RV; ++j)
+        a[j] = __builtin_nontemporal_load(in + (uint64_t)j * n + i);
+#pragma unroll
+    for (int j = 1; j < RV; ++j)
+        a[0] ^= a[j];
+    if constexpr (WB == 4) {
+        __builtin_nontemporal_store(a[0].x ^ a[0].y ^ a[0].z ^ a[0].w, reinterpret_cast<uint32_t*>(out) + i);
+    } else if constexpr (WB == 8) {
+        const v2u o = {a[0].x ^ a[0].y, a[0].z ^ a[0].w};
+        __builtin_nontemporal_store(o, reinterpret_cast<v2u*>(out) + i);
+    } else {
+        static_assert(WB == 16, "4, 8 or 16 bytes out per thread");
+        __builtin_nontemporal_store(a[0], reinterpret_cast<v4u*>(out) + i);
+    }
+}
+
+template <int RV>
+bool launch_read_n(uint32_t wb, dim3 grid, hipStream_t s, const v4u* in, char* out, uint64_t n)
+{
+    switch (wb) {
+    case 4: hipLaunchKernelGGL((read_n_write_kernel<RV, 4>), grid, dim3(256), 0, s, in, out, n); return true;
+    case 8: hipLaunchKernelGGL((read_n_write_kernel<RV, 8>), grid, dim3(256), 0, s, in, out, n); return true;
+    case 16: hipLaunchKernelGGL((read_n_write_kernel<RV, 16>), grid, dim3(256), 0, s, in, out, n); return true;
+    default: return false;
+    }
 }
 
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
@@ -182,6 +223,33 @@ int stream_probe_4to1(const void* x, void* out, uint64_t rows, uint32_t hidden, 
     case 2: ok = probe_store<2>(store_pol, spu, grid, s, xi, o, hidden, (uint32_t)upr, (uint32_t)units, xcd); break;
     case 16: ok = probe_store<16>(store_pol, spu, grid, s, xi, o, hidden, (uint32_t)upr, (uint32_t)units, xcd); break;
     case 17: ok = probe_store<17>(store_pol, spu, grid, s, xi, o, hidden, (uint32_t)upr, (uint32_t)units, xcd); break;
+    default: ok = false;
+    }
+    if (!ok)
+        return 1;
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Another kernel's read:write mix: in holds n * rv * 16 readable bytes, out
+// n * wb writable bytes, both 16-byte aligned; rv 1, 2, 4 or 8, wb 4, 8 or 16.
+// Returns 0, or 1 on a bad argument or a failed launch.
+int stream_read_n_write(const void* in, void* out, uint64_t n, uint32_t rv, uint32_t wb, void* stream)
+{
+    if (!in || !out || n == 0 || ((uintptr_t)in & 15u) || ((uintptr_t)out & 15u))
+        return 1;
+    const uint64_t blocks = (n + 255) / 256;
+    if (blocks >= (1ull << 31) || n > (1ull << 40))
+        return 1;
+    const dim3 grid((uint32_t)blocks);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const v4u* vin = static_cast<const v4u*>(in);
+    char* o = static_cast<char*>(out);
+    bool ok;
+    switch (rv) {
+    case 1: ok = launch_read_n<1>(wb, grid, s, vin, o, n); break;
+    case 2: ok = launch_read_n<2>(wb, grid, s, vin, o, n); break;
+    case 4: ok = launch_read_n<4>(wb, grid, s, vin, o, n); break;
+    case 8: ok = launch_read_n<8>(wb, grid, s, vin, o, n); break;
     default: ok = false;
     }
     if (!ok)
