@@ -256,7 +256,7 @@ tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t experts, int
  *               its slot instead of reading out of bounds.
  *  topk_weight  fp32 [tokens, k] (device), 4-byte aligned.
  *  global_scale a finite fp32 factor applied once to each sum.
- *  tokens       0 <= tokens < 2^31;  k: 1..32 (k > 32: TK_ERR_UNSUPPORTED).
+ *  tokens       0 <= tokens < 2^31;  k: 1..64 (k > 64: TK_ERR_UNSUPPORTED).
  *  hidden       a positive multiple of 8, at most (2^31-1)/8.
  *  n_rows       0 <= n_rows < 2^31.
  *  out_dtype    TK_DTYPE_BF16 or TK_DTYPE_FP32.
@@ -288,7 +288,7 @@ tk_status tk_moe_reduce(const void* x, const float* row_scale, const int32_t* po
  *
  *  topk_idx        int32 [tokens, k] (device), 4-byte aligned.
  *  tokens          0 <= tokens < 2^31, with tokens * k < 2^31.
- *  k               1..32 (k > 32: TK_ERR_UNSUPPORTED).
+ *  k               1..64 (k > 64: TK_ERR_UNSUPPORTED).
  *  experts         1..512 (more: TK_ERR_UNSUPPORTED).
  *  pos             int32 [tokens, k] (device), 4-byte aligned; also the call's
  *                  working storage (each block of 1024 tokens keeps its

@@ -41,7 +41,7 @@
 namespace {
 
 constexpr int kMaxExperts = 512;
-constexpr int kMaxK = 32;
+constexpr int kMaxK = 64;
 constexpr int kScanThreads = 1024;
 
 // This token's present slots: slot j is present when its expert is in range
@@ -447,7 +447,9 @@ extern "C" tk_status tk_topk_to_pos(const int32_t* topk_idx, int64_t tokens, int
         launch_pos<8, true>(topk_idx, (uint32_t)tokens, 8u, (uint32_t)experts, pos, expert_offsets, s);
     else if (k <= 8)
         launch_pos<8, false>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
-    else
+    else if (k <= 32)
         launch_pos<32, false>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
+    else
+        launch_pos<64, false>(topk_idx, (uint32_t)tokens, (uint32_t)k, (uint32_t)experts, pos, expert_offsets, s);
     return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
 }

@@ -23,7 +23,9 @@
 //      the loads below are only for rows that contribute).
 //   2. All KT x SPU row loads of the unit are issued before the first use
 //      (16 bytes per lane, non-temporal: nothing is re-read), row base in
-//      scalar registers, lane offset in 32 bits.
+//      scalar registers, lane offset in 32 bits.  Above 32 slots per token
+//      (up to 64, one per lane for step 1) moe_reduce_wide_kernel takes the
+//      present slots 32 at a time through steps 2 and 3, the sum carried over.
 //   3. fp32 multiply and add in slot order (no contraction), the global scale,
 //      then v_cvt_pk_bf16_f32 (round to nearest even) and 16-byte
 //      non-temporal stores.
@@ -39,7 +41,8 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr uint32_t kSlotBytes = 16;   // 8 bf16 columns per lane per step
-constexpr int64_t kMaxK = 32;
+constexpr int64_t kMaxK = 64; // one slot per lane for the metadata
+constexpr int kWideKT = 32;   // rows whose loads a wave holds at once above 32 slots
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -163,6 +166,89 @@ __global__ __launch_bounds__(THREADS) void moe_reduce_kernel(ReduceParams p)
     }
 }
 
+// k in 33..64: moe_reduce_kernel's steps with one 512-column step per unit,
+// the present slots taken kWideKT at a time (their loads in flight together),
+// the sum carried from one batch to the next in slot order.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void moe_reduce_wide_kernel(ReduceParams p)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t u = __builtin_amdgcn_readfirstlane(blockIdx.x * (256 / kWave) + threadIdx.x / kWave);
+    if (u >= p.units)
+        return;
+    const uint32_t t = u / p.upt;
+    const uint32_t step0 = u - t * p.upt;
+
+    uint32_t q = 0xFFFFFFFFu;
+    float f = 0.0f;
+    if (lane < p.k) {
+        const size_t i = (size_t)t * p.k + lane;
+        q = (uint32_t)p.pos[i];
+        const float wj = p.w[i];
+        if (q < p.n_rows)
+            f = p.row_scale ? wj * p.row_scale[q] : wj;
+    }
+    uint64_t mask = __builtin_amdgcn_ballot_w64(lane < p.k && q < p.n_rows);
+    const uint32_t count = (uint32_t)__builtin_popcountll(mask);
+    const uint32_t off = min((step0 * kWave + lane) * kSlotBytes, (p.slots - 1u) * kSlotBytes);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.0f;
+    for (uint32_t done = 0; done < count; done += kWideKT) {
+        const uint32_t n = min(count - done, (uint32_t)kWideKT);
+        uint32_t row[kWideKT];
+        float fm[kWideKT];
+#pragma unroll
+        for (int m = 0; m < kWideKT; ++m) {
+            const uint32_t l = mask ? (uint32_t)__builtin_ctzll(mask) : 0u;
+            row[m] = __builtin_amdgcn_readlane(q, l);
+            fm[m] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, f), l));
+            mask &= mask - 1;
+        }
+        u32x4 raw[kWideKT];
+#pragma unroll
+        for (int m = 0; m < kWideKT; ++m)
+            if ((uint32_t)m < n)
+                raw[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.x + (size_t)row[m] * p.row_bytes + off));
+#pragma unroll
+        for (int m = 0; m < kWideKT; ++m) {
+            if ((uint32_t)m < n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = acc[2 * e] + fm[m] * bf16_lo(raw[m][e]);
+                    acc[2 * e + 1] = acc[2 * e + 1] + fm[m] * bf16_hi(raw[m][e]);
+                }
+            }
+        }
+    }
+    constexpr uint32_t kOutSlot = OUT_BF16 ? 16u : 32u;
+    const uint32_t slot = step0 * kWave + lane;
+    if (slot < p.slots) {
+        char* dst = p.out + ((size_t)t * p.slots + slot) * kOutSlot;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o[e] = acc[e] * p.gscale;
+        if constexpr (OUT_BF16) {
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x2 pr = {o[2 * e], o[2 * e + 1]};
+                v[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+            }
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        } else {
+            const u32x4 a = {__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
+                             __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3])};
+            const u32x4 b = {__builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]),
+                             __builtin_bit_cast(uint32_t, o[6]), __builtin_bit_cast(uint32_t, o[7])};
+            __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(dst));
+            __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(dst) + 1);
+        }
+    }
+}
+
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
 {
     if (!a || !b || an == 0 || bn == 0)
@@ -238,7 +324,7 @@ extern "C" tk_status tk_moe_reduce(const void* x, const float* row_scale, const 
         return TK_ERR_UNSUPPORTED;
     const uint32_t slots = (uint32_t)(hidden / 8);
     const uint32_t steps_row = (slots + kWave - 1) / kWave;
-    const uint32_t kt = k <= 1 ? 1u : k <= 2 ? 2u : k <= 4 ? 4u : k <= 8 ? 8u : k <= 16 ? 16u : 32u;
+    const uint32_t kt = k <= 1 ? 1u : k <= 2 ? 2u : k <= 4 ? 4u : k <= 8 ? 8u : k <= 16 ? 16u : k <= 32 ? 32u : 64u;
     const uint32_t spu_max = kt <= 2 ? 4u : kt <= 4 ? 2u : 1u;
     uint32_t spu = spu_max;
     while (steps_row % spu != 0)
@@ -271,7 +357,15 @@ extern "C" tk_status tk_moe_reduce(const void* x, const float* row_scale, const 
     case 4: launch_spu<4>(spu, bf16_out, p, s); break;
     case 8: launch_spu<8>(spu, bf16_out, p, s); break;
     case 16: launch_spu<16>(spu, bf16_out, p, s); break;
-    default: launch_spu<32>(spu, bf16_out, p, s); break;
+    case 32: launch_spu<32>(spu, bf16_out, p, s); break;
+    default: { // k in 33..64: one step per unit (spu is 1 for kt above 4)
+        const uint32_t blocks = (p.units + 3u) / 4u;
+        if (bf16_out)
+            hipLaunchKernelGGL(moe_reduce_wide_kernel<true>, dim3(blocks), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(moe_reduce_wide_kernel<false>, dim3(blocks), dim3(256), 0, s, p);
+        break;
+    }
     }
     return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
 }

@@ -108,12 +108,12 @@ static void check_validation(void)
                          TK_DTYPE_BF16, FAKE(0), NULL) == TK_ERR_INVALID_ARG, "reduce output aliases x");
     EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), INFINITY, 4, 8, 7168, 32,
                          TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_INVALID_ARG, "infinite global scale");
-    EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), 1.0f, 4, 33, 7168, 32,
-                         TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_UNSUPPORTED, "k above 32");
+    EXPECT(tk_moe_reduce(FAKE(0), NULL, (const int32_t*)FAKE(1), (const float*)FAKE(2), 1.0f, 4, 65, 7168, 32,
+                         TK_DTYPE_BF16, FAKE(3), NULL) == TK_ERR_UNSUPPORTED, "k above 64");
 
     /* position map */
-    EXPECT(tk_topk_to_pos((const int32_t*)FAKE(0), 4, 33, 256, (int32_t*)FAKE(1), (int32_t*)FAKE(2), NULL) ==
-               TK_ERR_UNSUPPORTED, "position map: k above 32");
+    EXPECT(tk_topk_to_pos((const int32_t*)FAKE(0), 4, 65, 256, (int32_t*)FAKE(1), (int32_t*)FAKE(2), NULL) ==
+               TK_ERR_UNSUPPORTED, "position map: k above 64");
     EXPECT(tk_topk_to_pos((const int32_t*)FAKE(0), 4, 8, 256, (int32_t*)FAKE(0), (int32_t*)FAKE(2), NULL) ==
                TK_ERR_INVALID_ARG, "position map: pos aliases topk_idx");
 }

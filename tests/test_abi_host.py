@@ -201,8 +201,8 @@ def test_moe_reduce_invalid_arguments(kw):
 
 
 def test_moe_reduce_unsupported_and_empty():
-    assert reduce(k=33) == UNSUPPORTED
-    assert reduce(k=64) == UNSUPPORTED
+    assert reduce(k=65) == UNSUPPORTED
+    assert reduce(k=1000) == UNSUPPORTED
     assert reduce(tokens=0) == OK
     assert reduce(tokens=0, x=None, pos=None, topk_weight=None, out=None) == OK
     # n_rows == 0 lets x be NULL (nothing can be read); with no tokens nothing launches
@@ -226,7 +226,7 @@ def test_topk_to_pos_invalid_arguments(kw):
 
 
 def test_topk_to_pos_unsupported():
-    assert to_pos(k=33) == UNSUPPORTED
+    assert to_pos(k=65) == UNSUPPORTED
     assert to_pos(experts=513) == UNSUPPORTED
 
 

@@ -54,6 +54,9 @@ CASES = [  # (tokens, k, experts, drop, noise)
     (1024, 8, 256, 0.0, False), (1025, 8, 256, 0.05, False), (2048, 8, 256, 0.0, True), (4096, 8, 256, 0.0, False),
     (3000, 6, 160, 0.1, True), (2049, 1, 512, 0.0, False), (777, 32, 512, 0.0, True), (777, 32, 64, 0.0, True),
     (5000, 9, 100, 0.0, True), (1500, 2, 2, 0.0, True), (65536, 8, 256, 0.02, False), (40000, 16, 384, 0.0, True),
+    # k above 32 (up to 64): one-workgroup calls, blocks of 256 and 1024 tokens, more slots than experts
+    (200, 64, 512, 0.0, True), (700, 48, 256, 0.1, True), (200, 64, 32, 0.0, False), (3000, 40, 64, 0.0, True),
+    (1100, 64, 512, 0.05, True), (66000, 33, 256, 0.0, False),
 ]
 
 
@@ -92,23 +95,25 @@ def test_topk_to_pos_no_tokens_zeroes_the_offsets():
     assert (o[:257] == 0).all() and (o[257:] == 99).all() and (pos.cpu().numpy() == 5).all()
 
 
-def test_gating_then_map_then_reduce():
+@pytest.mark.parametrize("k,ng,tg", [(8, 8, 4), (48, 1, 1), (64, 8, 6)], ids=str)
+def test_gating_then_map_then_reduce(k, ng, tg):
     """The gating's indices go straight into the map, and the map into the
     reduce: expert rows laid out by the map and reduced through it give, bit
     for bit, the oracle's reduce over the oracle's map of the oracle's
-    gating."""
-    print("[gpu-case] gating -> map -> reduce", flush=True)
-    T, E, k, hidden = 1500, 256, 8, 1024
+    gating (k = 8 with groups, and k above 32, which the one-token gating
+    kernel, the 64-slot map and the reduce's 32-row batches serve)."""
+    print("[gpu-case] gating -> map -> reduce", k, ng, tg, flush=True)
+    T, E, hidden = 1500, 256, (1024 if k <= 8 else 256)
     s = wl.uniform(wl.stream_key("pos_test", 0, "scores"), 0, T * E).reshape(T, E).astype(np.float32)
     sd = torch.from_numpy(s).to(DEV)
     idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, k), dtype=torch.float32, device=DEV)
-    assert tk.tk_topk_gate(sd, T, E, k, 8, 4, 1, idx, w) == OK
+    assert tk.tk_topk_gate(sd, T, E, k, ng, tg, 1, idx, w) == OK
     pos = torch.empty((T, k), dtype=torch.int32, device=DEV)
     off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
     assert tk.tk_topk_to_pos(idx, T, k, E, pos, off) == OK
     torch.cuda.synchronize()
-    oi, ow = oracle.topk_gate(s, k, 8, 4, True)
+    oi, ow = oracle.topk_gate(s, k, ng, tg, True)
     op, oo = oracle.topk_to_pos(oi, E)
     assert np.array_equal(idx.cpu().numpy(), oi) and np.array_equal(pos.cpu().numpy(), op)
     assert np.array_equal(off.cpu().numpy(), oo)

@@ -74,14 +74,14 @@ def test_random_standalone_cast_case(i):
 
 @pytest.mark.parametrize("i", range(32))
 def test_random_reduce_case(i):
-    """tk_moe_reduce on a random draw: tokens, k (1 .. 32), width, position
+    """tk_moe_reduce on a random draw: tokens, k (1 .. 64), width, position
     map with repeated rows, dropped (-1) and out-of-range entries, weights
     with zeros and negatives, optional per-row scales, global scale of
     either sign and tiny magnitude, bf16 or fp32 output."""
     from test_gpu_reduce import run_reduce, same as same_reduce
     rng = np.random.default_rng(30_000 + i)
     tokens = int(rng.choice([1, 7, 64, 200]))
-    k = int(rng.choice([1, 2, 3, 5, 8, 9, 12, 16, 24, 32]))
+    k = int(rng.choice([1, 2, 3, 5, 8, 9, 12, 16, 24, 32, 40, 64]))
     hidden = int(rng.choice([8, 24, 64, 520, 1024, 2056, 7168]))
     n_rows = int(rng.integers(1, 3 * tokens * k // 2 + 2))
     pos = rng.integers(0, n_rows, size=(tokens, k)).astype(np.int32)

@@ -83,7 +83,7 @@ def random_case(seed, tokens, k, hidden, n_rows, drop=0.1, bad=0.05):
     return x, pos, w, rs
 
 
-KS = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 24, 32]
+KS = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 24, 32, 33, 40, 48, 63, 64]  # above 32: batches of 32 rows
 
 
 @pytest.mark.parametrize("k", KS)
