@@ -19,10 +19,10 @@
 // groups fit 16 lanes of the two-token layout (at most 8 groups, k <= 16;
 // 256 experts in 8 groups keeping 4, for one), the groups are ranked first,
 // the kept lanes move into one 16-lane row per token and steps 1 and 3 run
-// on four tokens per wave: topk_row_kernel for 128 or 256 experts (one token
-// per 16-lane row from the start, group ranks by row broadcasts),
-// topk_quad_kernel for the other such shapes (two passes of the two-token
-// layout).
+// on four tokens per wave: topk_row_kernel for a multiple of 32 experts from
+// 64 to 256 in 2, 4 or 8 groups (one token per 16-lane row from the start,
+// 4 to 16 experts per lane, group ranks by row broadcasts), topk_quad_kernel
+// for the other such shapes (two passes of the two-token layout).
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -747,8 +747,8 @@ __device__ __forceinline__ void row_group_rank(uint32_t gkey, uint32_t gkey_less
     }
 }
 
-// Four tokens per wave in one pass, for 128 or 256 experts in 2, 4 or 8
-// groups (C16 = 8 or 16 experts per lane, 16 lanes per token, 16 >> GL groups
+// Four tokens per wave in one pass, for 16 * C16 experts (C16 even, 4 to 16
+// experts per lane, 16 lanes per token) in 2, 4 or 8 groups (16 >> GL groups
 // of 2^GL lanes) whose kept groups fill at most 8 lanes, and k <= 16: lane q of
 // row r holds experts q*C16 .. +C16-1 of token 4w + r.  Each row ranks its
 // groups with row broadcasts (no LDS), and a kept lane writes the two halves
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     constexpr int kWaves = kThreads / kWave;
     constexpr int kWords = C > 4 ? 2 : 1;
     constexpr uint32_t kGMask = (1u << GL) - 1u;
-    static_assert(C16 == 8 || C16 == 16, "8 or 16 experts per lane");
+    static_assert(C16 % 2 == 0 && C16 >= 4 && C16 <= 16, "an even count of 4 to 16 experts per lane");
     __shared__ uint4 s_keys[kWaves][kWords][kWave];
     __shared__ uint32_t s_src[kWaves][kWave];
     __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
@@ -821,9 +821,11 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int w = 0; w < kWords; ++w)
-                s_keys[wv][w][d + h] = make_uint4(fbits(x[h * C + 4 * w]), fbits(x[h * C + 4 * w + 1]),
-                                                  fbits(x[h * C + 4 * w + 2]), fbits(x[h * C + 4 * w + 3]));
+            for (int w = 0; w < kWords; ++w) {
+                // the half's C scores, then zeros up to the words' 4 * kWords slots
+                auto at = [&](int i) { return i < C ? fbits(x[h * C + i]) : 0u; };
+                s_keys[wv][w][d + h] = make_uint4(at(4 * w), at(4 * w + 1), at(4 * w + 2), at(4 * w + 3));
+            }
             s_src[wv][d + h] = q * C16 + h * C;
         }
     }
@@ -892,9 +894,10 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
     if (tokens == 0)
         return TK_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // one token per 16-lane row in one pass: 128 or 256 experts (8 or 16 per
-    // lane) in 2, 4 or 8 groups of 2^GL lanes, kept groups within 8 lanes
-    if ((experts == 128 || experts == 256) && (n_group == 2 || n_group == 4 || n_group == 8) && k <= 16) {
+    // one token per 16-lane row in one pass: 16 * C16 experts (C16 even, 4 to
+    // 16 per lane) in 2, 4 or 8 groups of 2^GL lanes, kept groups within 8 lanes
+    if (experts % 32 == 0 && experts >= 64 && experts <= 256 && (n_group == 2 || n_group == 4 || n_group == 8) &&
+        k <= 16) {
         const uint32_t GLr = (uint32_t)__builtin_ctzll((unsigned long long)(16 / n_group));
         if (2 * (topk_group << GLr) <= 16) {
             const uint32_t tpb = 4 * (kThreads / kWave);
@@ -902,15 +905,24 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
 #define TK_TOPKR_LAUNCH(C16, K8, GL)                                                                          \
     hipLaunchKernelGGL((topk_row_kernel<C16, K8, GL>), dim3(rblocks), dim3(kThreads), 0, s, scores,           \
                        (uint32_t)tokens, (uint32_t)k, (uint32_t)topk_group, normalise, topk_idx, topk_weight)
-#define TK_TOPKR(C16, GL)                                                                                     \
-    if (k == 8)                                                                                               \
-        TK_TOPKR_LAUNCH(C16, true, GL);                                                                       \
-    else                                                                                                      \
-        TK_TOPKR_LAUNCH(C16, false, GL);
-            if (experts == 256) {
-                if (GLr == 1) { TK_TOPKR(16, 1) } else if (GLr == 2) { TK_TOPKR(16, 2) } else { TK_TOPKR(16, 3) }
-            } else {
-                if (GLr == 1) { TK_TOPKR(8, 1) } else if (GLr == 2) { TK_TOPKR(8, 2) } else { TK_TOPKR(8, 3) }
+#define TK_TOPKR(C16)                                                                                         \
+    case C16:                                                                                                 \
+        if (GLr == 1) {                                                                                       \
+            if (k == 8) TK_TOPKR_LAUNCH(C16, true, 1); else TK_TOPKR_LAUNCH(C16, false, 1);                   \
+        } else if (GLr == 2) {                                                                                \
+            if (k == 8) TK_TOPKR_LAUNCH(C16, true, 2); else TK_TOPKR_LAUNCH(C16, false, 2);                   \
+        } else {                                                                                              \
+            if (k == 8) TK_TOPKR_LAUNCH(C16, true, 3); else TK_TOPKR_LAUNCH(C16, false, 3);                   \
+        }                                                                                                     \
+        break;
+            switch (experts / 16) {
+                TK_TOPKR(4)
+                TK_TOPKR(6)
+                TK_TOPKR(8)
+                TK_TOPKR(10)
+                TK_TOPKR(12)
+                TK_TOPKR(14)
+                TK_TOPKR(16)
             }
 #undef TK_TOPKR
 #undef TK_TOPKR_LAUNCH

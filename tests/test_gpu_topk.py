@@ -63,11 +63,12 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     (160, 6, 8, 3), (96, 4, 4, 2), (120, 6, 6, 2), (100, 5, 5, 2), (72, 4, 8, 2),
     # four tokens per wave (kept groups within 16 lanes of the two-token layout, at most 8 groups,
     # k <= 16): every row filled, part-filled rows, 8 / 4 / 2 groups, k = 1 and 16, 2 to 8 experts
-    # per lane (128 and 256 experts take the one-pass row layout, the others two passes); and its
-    # neighbours that stay two to a wave (20 kept lanes, k = 17, 16 groups)
+    # per lane (experts a multiple of 32 from 64 to 256 in 2, 4 or 8 groups take the one-pass row
+    # layout with 4 to 16 experts per lane, the others two passes); and its neighbours that stay two
+    # to a wave (20 kept lanes, k = 17, 16 groups)
     (256, 16, 8, 4), (256, 8, 8, 3), (256, 1, 8, 1), (256, 8, 4, 2), (256, 4, 2, 1), (192, 8, 8, 4),
     (64, 6, 8, 4), (128, 8, 8, 4), (128, 4, 4, 2), (128, 3, 2, 1), (128, 16, 8, 1), (256, 8, 8, 5),
-    (256, 17, 8, 4), (256, 8, 16, 8),
+    (256, 17, 8, 4), (256, 8, 16, 8), (224, 7, 8, 3), (160, 16, 8, 4), (96, 8, 2, 1), (64, 16, 4, 2),
 ]
 
 
@@ -210,12 +211,13 @@ def test_topk_nan_group_sums(ng, tg):
 def _random_shape(rng):
     """A valid gating shape: experts up to 512, a group count dividing them
     with at least 2 experts per group, topk_group groups kept, k at most the
-    candidates and at most 64.  A third of the draws are 128 or 256 experts
-    in 2, 4 or 8 groups whose kept groups fit half a 16-lane row."""
+    candidates and at most 64.  A third of the draws are the one-pass row
+    layout's shapes: a multiple of 32 experts from 64 to 256 in 2, 4 or 8
+    groups whose kept groups fit half a 16-lane row."""
     if rng.random() < 1 / 3:
-        E = int(rng.choice([128, 256]))
+        E = int(rng.choice([64, 96, 128, 160, 192, 224, 256]))
         ng = int(rng.choice([2, 4, 8]))
-        tg = int(rng.integers(1, max(1, ng // 4) + 1))
+        tg = int(rng.integers(1, ng // 2 + 1))
         k = int(rng.integers(1, min(16, tg * (E // ng)) + 1))
         return E, k, ng, tg
     while True:
