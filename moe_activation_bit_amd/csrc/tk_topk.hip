@@ -22,7 +22,9 @@
 // on four tokens per wave: topk_row_kernel for a multiple of 32 experts from
 // 64 to 256 in 2, 4 or 8 groups (one token per 16-lane row from the start,
 // 4 to 16 experts per lane, group ranks by row broadcasts), topk_quad_kernel
-// for the other such shapes (two passes of the two-token layout).
+// for the other such shapes (two passes of the two-token layout).  Without
+// groups, up to 128 experts and k <= 16, topk_row1_kernel puts one token in
+// each 16-lane row and goes straight to steps 1 and 3.
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -528,6 +530,12 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
 // round's winners write their pick and its key into s_pick at the round's
 // position), and output lane q of row r stores pick q, its weight the key's
 // value.
+template <int C, bool K8>
+__device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, bool filled,
+                                            const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
+                                            uint32_t k, int normalise, int32_t* __restrict__ idx_out,
+                                            float* __restrict__ w_out, uint32_t t0, uint32_t lane, uint2* s_pick);
+
 template <int C, bool K8, bool RAW>
 __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
                                                  uint32_t k, uint32_t filled_lanes, int normalise,
@@ -537,9 +545,8 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
 {
     constexpr int kWords = C > 4 ? 2 : 1;
     const uint32_t q = lane & 15u;
-    const uint32_t row = lane >> 4;
     const bool filled = q < filled_lanes;
-    uint32_t key[C], idx[C];
+    uint32_t key[C];
     {
         uint32_t w8[4 * kWords];
 #pragma unroll
@@ -556,10 +563,30 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
     }
     // the expert index of this lane's first slot (read by every lane: an
     // empty lane never wins, since k is at most the candidates)
-    const uint32_t base = s_src[lane];
+    rows_select<C, K8>(key, s_src[lane], filled, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane,
+                       s_pick);
+}
+
+// The steps of the four-tokens-per-wave kernels from the sort on: row r =
+// lane / 16 holds token t0 + r, lane q of a row C keys of that token (lane
+// order in the row is index order, `base` the expert index of the lane's first
+// key; a lane that is not `filled` holds no candidate).  Each lane sorts its
+// keys, the k rounds run on the rows (a DPP maximum inside each 16-lane row,
+// so one round serves four tokens; a round's winners write their pick and its
+// key into s_pick at the round's position), and output lane q of row r stores
+// pick q, its weight the key's value.
+template <int C, bool K8>
+__device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, bool filled,
+                                            const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
+                                            uint32_t k, int normalise, int32_t* __restrict__ idx_out,
+                                            float* __restrict__ w_out, uint32_t t0, uint32_t lane, uint2* s_pick)
+{
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
+    uint32_t idx[C];
     sort_lane<C>(key, idx);
-    // a lane past the row's filled ones sorts whatever its LDS words hold; an
-    // empty head keeps it from ever winning, so its other keys are never read
+    // a lane past the row's filled ones sorts whatever it was given; an empty
+    // head keeps it from ever winning, so its other keys are never read
     key[0] = filled ? key[0] : 0u;
     // slot lists, head lowest, 3 bits each: the slots themselves (7 - idx)
     uint32_t slots = 0;
@@ -725,6 +752,36 @@ __global__ __launch_bounds__(kThreads) void topk_quad_kernel(const float* __rest
 
     quad_rows_finish<C, K8, false>(scores, tokens, experts, k, topk_group << gl_log2, normalise, idx_out, w_out, t0, lane,
                             s_keys[wv], s_src[wv], s_pick[wv]);
+}
+
+// Four tokens per wave without groups, up to 128 experts and k <= 16: lane q
+// of row r holds experts q*C .. +C-1 of token 4w + r (C = ceil(experts / 16);
+// without FULL, slots past the last expert are empty), each lane's keys go
+// straight to the sort, and the rows go on as in topk_quad_kernel.
+template <int C, bool K8, bool FULL>
+__global__ __launch_bounds__(kThreads) void topk_row1_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    constexpr int kWaves = kThreads / kWave;
+    __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    if (t0 >= tokens)
+        return;
+    const uint32_t q = lane & 15u;
+    // a wave past the last token repeats it in its other rows and stores nothing from them
+    const float* s_row = scores + (size_t)min(t0 + (lane >> 4), tokens - 1u) * experts;
+    float v[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        v[j] = FULL ? s_row[q * C + j] : s_row[min(q * C + j, experts - 1u)];
+    uint32_t key[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        key[j] = (FULL || q * C + j < experts) ? ordered(v[j]) : 0u;
+    rows_select<C, K8>(key, q * C, true, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
 }
 
 // Group ranks within 16-lane rows (one token per row, 16 >> GL groups of
@@ -894,6 +951,35 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
     if (tokens == 0)
         return TK_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // no groups, up to 128 experts, k <= 16: one token per 16-lane row
+    if (n_group == 1 && experts <= 128 && k <= 16) {
+        const uint32_t tpb = 4 * (kThreads / kWave);
+        const uint32_t rblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+#define TK_TOPK1_LAUNCH(CC, K8, FULL)                                                                         \
+    hipLaunchKernelGGL((topk_row1_kernel<CC, K8, FULL>), dim3(rblocks), dim3(kThreads), 0, s, scores,         \
+                       (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, normalise, topk_idx, topk_weight)
+#define TK_TOPK1(CC)                                                                                          \
+    case CC:                                                                                                  \
+        if (experts == 16 * (CC)) {                                                                           \
+            if (k == 8) TK_TOPK1_LAUNCH(CC, true, true); else TK_TOPK1_LAUNCH(CC, false, true);               \
+        } else {                                                                                              \
+            if (k == 8) TK_TOPK1_LAUNCH(CC, true, false); else TK_TOPK1_LAUNCH(CC, false, false);             \
+        }                                                                                                     \
+        break;
+        switch ((experts + 15) / 16) {
+            TK_TOPK1(1)
+            TK_TOPK1(2)
+            TK_TOPK1(3)
+            TK_TOPK1(4)
+            TK_TOPK1(5)
+            TK_TOPK1(6)
+            TK_TOPK1(7)
+            TK_TOPK1(8)
+        }
+#undef TK_TOPK1
+#undef TK_TOPK1_LAUNCH
+        return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+    }
     // one token per 16-lane row in one pass: 16 * C16 experts (C16 even, 4 to
     // 16 per lane) in 2, 4 or 8 groups of 2^GL lanes, kept groups within 8 lanes
     if (experts % 32 == 0 && experts >= 64 && experts <= 256 && (n_group == 2 || n_group == 4 || n_group == 8) &&

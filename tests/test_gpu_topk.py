@@ -69,6 +69,10 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     (256, 16, 8, 4), (256, 8, 8, 3), (256, 1, 8, 1), (256, 8, 4, 2), (256, 4, 2, 1), (192, 8, 8, 4),
     (64, 6, 8, 4), (128, 8, 8, 4), (128, 4, 4, 2), (128, 3, 2, 1), (128, 16, 8, 1), (256, 8, 8, 5),
     (256, 17, 8, 4), (256, 8, 16, 8), (224, 7, 8, 3), (160, 16, 8, 4), (96, 8, 2, 1), (64, 16, 4, 2),
+    # no groups, up to 128 experts and k <= 16: one token per 16-lane row, 1 to 8 experts per lane,
+    # the last lanes part-filled or empty when experts is not a multiple of 16; k = 17 stays two to a wave
+    (128, 8, 1, 1), (128, 16, 1, 1), (60, 4, 1, 1), (112, 9, 1, 1), (16, 16, 1, 1), (120, 5, 1, 1),
+    (17, 3, 1, 1), (128, 17, 1, 1),
 ]
 
 
@@ -98,7 +102,8 @@ def test_topk_matches_oracle(shape, normalise):
     assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), np.argwhere(gw.view(np.uint32) != ow.view(np.uint32))[:4]
 
 
-@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (64, 3, 8, 2)], ids=str)
+@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (64, 3, 8, 2), (100, 8, 1, 1)],
+                         ids=str)
 def test_topk_last_wave_partly_past_the_tokens(shape):
     """Token counts around the four-tokens-per-wave grid: a last wave with 1,
     2 or 3 real tokens repeats the last one in its other rows and stores
@@ -115,7 +120,8 @@ def test_topk_last_wave_partly_past_the_tokens(shape):
             assert np.array_equal(gw.view(np.uint32), ow.view(np.uint32)), (T, normalise)
 
 
-@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (256, 8, 8, 5), (512, 8, 8, 4)],
+@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (128, 16, 4, 2), (160, 6, 8, 3), (256, 8, 8, 5), (512, 8, 8, 4),
+                                   (128, 8, 1, 1), (60, 4, 1, 1)],
                          ids=str)
 def test_topk_scores_only_4_byte_aligned(shape):
     """Scores at an address that is 4 bytes past a 16-byte boundary (the
@@ -211,9 +217,13 @@ def test_topk_nan_group_sums(ng, tg):
 def _random_shape(rng):
     """A valid gating shape: experts up to 512, a group count dividing them
     with at least 2 experts per group, topk_group groups kept, k at most the
-    candidates and at most 64.  A third of the draws are the one-pass row
+    candidates and at most 64.  A sixth of the draws have no groups, up to
+    128 experts and k <= 16; a third of the rest are the one-pass row
     layout's shapes: a multiple of 32 experts from 64 to 256 in 2, 4 or 8
     groups whose kept groups fit half a 16-lane row."""
+    if rng.random() < 1 / 6:  # no groups, up to 128 experts, k <= 16: one token per 16-lane row
+        E = int(rng.integers(1, 129))
+        return E, int(rng.integers(1, min(16, E) + 1)), 1, 1
     if rng.random() < 1 / 3:
         E = int(rng.choice([64, 96, 128, 160, 192, 224, 256]))
         ng = int(rng.choice([2, 4, 8]))
