@@ -23,8 +23,9 @@
 // 64 to 256 in 2, 4 or 8 groups (one token per 16-lane row from the start,
 // 4 to 16 experts per lane, group ranks by row broadcasts), topk_quad_kernel
 // for the other such shapes (two passes of the two-token layout).  Without
-// groups, up to 128 experts and k <= 16, topk_row1_kernel puts one token in
-// each 16-lane row and goes straight to steps 1 and 3.
+// groups and k <= 16, one token per 16-lane row goes straight to steps 1 and
+// 3: topk_row1_kernel up to 128 experts (one list per lane), topk_row2_kernel
+// from 129 to 256 (two lists per lane, a round taking the larger head).
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -536,6 +537,12 @@ __device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, b
                                             uint32_t k, int normalise, int32_t* __restrict__ idx_out,
                                             float* __restrict__ w_out, uint32_t t0, uint32_t lane, uint2* s_pick);
 
+template <bool K8>
+__device__ __forceinline__ void rows_store(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
+                                           uint32_t k, int normalise, int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out, uint32_t t0, uint32_t lane,
+                                           const uint2* s_pick);
+
 template <int C, bool K8, bool RAW>
 __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
                                                  uint32_t k, uint32_t filled_lanes, int normalise,
@@ -631,11 +638,24 @@ __device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, b
         if (it < k)
             round(it, 64u);
     }
+    rows_store<K8>(scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick);
+}
+
+// After the rounds of a four-tokens-per-wave kernel (s_pick[r * 16 + q] holds
+// row r's pick q and its key): output lane q of row r stores pick q of token
+// t0 + r, its weight the key's value, normalised by the running sum in pick
+// order.
+template <bool K8>
+__device__ __forceinline__ void rows_store(const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
+                                           uint32_t k, int normalise, int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out, uint32_t t0, uint32_t lane,
+                                           const uint2* s_pick)
+{
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- output lane q of row r: pick q of token t0 + r
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
     const uint32_t t = t0 + row;
     const float* s_row = scores + (size_t)min(t, tokens - 1u) * experts;
     const uint2 pk = s_pick[lane];
@@ -782,6 +802,97 @@ __global__ __launch_bounds__(kThreads) void topk_row1_kernel(const float* __rest
     for (int j = 0; j < C; ++j)
         key[j] = (FULL || q * C + j < experts) ? ordered(v[j]) : 0u;
     rows_select<C, K8>(key, q * C, true, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
+}
+
+// Four tokens per wave without groups, 129 to 256 experts and k <= 16: lane q
+// of row r holds experts q*2C .. +2C-1 of token 4w + r (C = ceil(experts / 32);
+// without FULL, slots past the last expert are empty) as two lists of C, each
+// sorted on its own.  A round's row maximum is taken over the lanes' larger
+// heads; a winning lane pops the list that holds it (the first list on equal
+// keys: its experts have the smaller indices).
+template <int C, bool K8, bool FULL>
+__global__ __launch_bounds__(kThreads) void topk_row2_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    constexpr int kWaves = kThreads / kWave;
+    __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    if (t0 >= tokens)
+        return;
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
+    // a wave past the last token repeats it in its other rows and stores nothing from them
+    const float* s_row = scores + (size_t)min(t0 + row, tokens - 1u) * experts;
+    float v[2 * C];
+#pragma unroll
+    for (int j = 0; j < 2 * C; ++j)
+        v[j] = FULL ? s_row[q * (2 * C) + j] : s_row[min(q * (2 * C) + j, experts - 1u)];
+    uint32_t ka[C], kb[C], ia[C], ib[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        ka[j] = (FULL || q * (2 * C) + j < experts) ? ordered(v[j]) : 0u;
+        kb[j] = (FULL || q * (2 * C) + C + j < experts) ? ordered(v[C + j]) : 0u;
+    }
+    sort_lane<C>(ka, ia);
+    sort_lane<C>(kb, ib);
+    // slot lists, head lowest, 3 bits each
+    uint32_t sa = 0, sb = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        sa |= ia[j] << (3 * j);
+        sb |= ib[j] << (3 * j);
+    }
+    sa ^= 0xFFFFFFu;
+    sb ^= 0xFFFFFFu;
+    const uint32_t base = q * (2 * C);
+
+    uint2* pick_row = &s_pick[wv][row << 4];
+    // a pop as selects on the lane's condition (as branches on the list the
+    // compiler would address the lists through memory)
+    auto pop = [&](uint32_t (&key)[C], uint32_t& slots, uint32_t depth, bool p) {
+#pragma unroll
+        for (int j = 0; j + 1 < C; ++j)
+            if (j + 1u < depth)
+                key[j] = p ? key[j + 1] : key[j];
+        if (depth > (uint32_t)C)
+            key[C - 1] = p ? 0u : key[C - 1];
+        slots = p ? slots >> 3 : slots;
+    };
+    auto round = [&](uint32_t it, uint32_t depth) {
+        const uint32_t h = max(ka[0], kb[0]);
+        uint32_t m = h;
+        m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
+        m = dpp_umax<0x4E>(m);  // quad_perm [2,3,0,1]
+        m = dpp_umax<0x141>(m); // row_half_mirror
+        m = dpp_umax<0x140>(m); // row_mirror: every lane holds its row's maximum
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(h == m);
+        // the lowest set bit of each row's 16 bits (every row has one)
+        const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
+        const bool w = __builtin_amdgcn_inverse_ballot_w64(win);
+        const bool from_a = ka[0] >= kb[0];
+        const uint2 pick = make_uint2(from_a ? base + (sa & 7u) : base + C + (sb & 7u), h);
+        pop(ka, sa, depth, w && from_a);
+        pop(kb, sb, depth, w && !from_a);
+        if (w)
+            pick_row[it] = pick;
+    };
+    if constexpr (K8) {
+#pragma unroll
+        for (uint32_t it = 0; it < 8; ++it)
+            round(it, 8u - it);
+    } else {
+        uint32_t it = 0;
+        for (; it + 1 < k; it += 2) {
+            round(it, 64u);
+            round(it + 1, 64u);
+        }
+        if (it < k)
+            round(it, 64u);
+    }
+    rows_store<K8>(scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
 }
 
 // Group ranks within 16-lane rows (one token per row, 16 >> GL groups of
@@ -978,6 +1089,31 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
         }
 #undef TK_TOPK1
 #undef TK_TOPK1_LAUNCH
+        return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+    }
+    // no groups, 129 to 256 experts, k <= 16: one token per 16-lane row, two lists per lane
+    if (n_group == 1 && experts > 128 && experts <= 256 && k <= 16) {
+        const uint32_t tpb = 4 * (kThreads / kWave);
+        const uint32_t rblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+#define TK_TOPK2L_LAUNCH(CC, K8, FULL)                                                                        \
+    hipLaunchKernelGGL((topk_row2_kernel<CC, K8, FULL>), dim3(rblocks), dim3(kThreads), 0, s, scores,         \
+                       (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, normalise, topk_idx, topk_weight)
+#define TK_TOPK2L(CC)                                                                                         \
+    case CC:                                                                                                  \
+        if (experts == 32 * (CC)) {                                                                           \
+            if (k == 8) TK_TOPK2L_LAUNCH(CC, true, true); else TK_TOPK2L_LAUNCH(CC, false, true);             \
+        } else {                                                                                              \
+            if (k == 8) TK_TOPK2L_LAUNCH(CC, true, false); else TK_TOPK2L_LAUNCH(CC, false, false);           \
+        }                                                                                                     \
+        break;
+        switch ((experts + 31) / 32) {
+            TK_TOPK2L(5)
+            TK_TOPK2L(6)
+            TK_TOPK2L(7)
+            TK_TOPK2L(8)
+        }
+#undef TK_TOPK2L
+#undef TK_TOPK2L_LAUNCH
         return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
     }
     // one token per 16-lane row in one pass: 16 * C16 experts (C16 even, 4 to
