@@ -25,7 +25,8 @@
 // for the other such shapes (two passes of the two-token layout).  Without
 // groups and k <= 16, one token per 16-lane row goes straight to steps 1 and
 // 3: topk_row1_kernel up to 128 experts (one list per lane), topk_row2_kernel
-// from 129 to 256 (two lists per lane, a round taking the larger head).
+// from 129 to 256 (two lists per lane, a round taking the larger head),
+// topk_rowl_kernel from 257 to 512 (three or four lists per lane).
 //   1. Each lane sorts its C candidates once, best first, by the key (score
 //      in an order-preserving uint32 map, -0 == +0; then smaller index).
 //   2. Groups: each lane's two best, merged over the group's lanes (DPP
@@ -895,6 +896,109 @@ __global__ __launch_bounds__(kThreads) void topk_row2_kernel(const float* __rest
     rows_store<K8>(scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
 }
 
+// Four tokens per wave without groups, 257 to 512 experts and k <= 16: the
+// layout of topk_row2_kernel with L = 3 or 4 lists of C per lane (lane q of
+// row r holds experts q*L*C .. +L*C-1; without FULL, slots past the last
+// expert are empty).  A round's row maximum is taken over each lane's largest
+// head; a winning lane pops the first list that holds it.
+template <int C, int L, bool K8, bool FULL>
+__global__ __launch_bounds__(kThreads) void topk_rowl_kernel(const float* __restrict__ scores, uint32_t tokens,
+                                                             uint32_t experts, uint32_t k, int normalise,
+                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+{
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kLane = L * C; // experts per lane
+    __shared__ uint2 s_pick[kWaves][kWave]; // [row * 16 + round]: (expert, key)
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t t0 = 4u * __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    if (t0 >= tokens)
+        return;
+    const uint32_t q = lane & 15u;
+    const uint32_t row = lane >> 4;
+    // a wave past the last token repeats it in its other rows and stores nothing from them
+    const float* s_row = scores + (size_t)min(t0 + row, tokens - 1u) * experts;
+    const uint32_t base = q * kLane;
+    float v[kLane];
+#pragma unroll
+    for (int j = 0; j < kLane; ++j)
+        v[j] = FULL ? s_row[base + j] : s_row[min(base + j, experts - 1u)];
+    uint32_t key[L][C], sl[L];
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+        uint32_t id[C];
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            key[l][j] = (FULL || base + l * C + j < experts) ? ordered(v[l * C + j]) : 0u;
+        sort_lane<C>(key[l], id);
+        // slot list, head lowest, 3 bits each
+        sl[l] = 0;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            sl[l] |= id[j] << (3 * j);
+        sl[l] ^= 0xFFFFFFu;
+    }
+
+    uint2* pick_row = &s_pick[wv][row << 4];
+    // a pop as selects on the lane's condition (as branches on the list the
+    // compiler would address the lists through memory)
+    auto pop = [&](uint32_t (&kl)[C], uint32_t& slots, uint32_t depth, bool p) {
+#pragma unroll
+        for (int j = 0; j + 1 < C; ++j)
+            if (j + 1u < depth)
+                kl[j] = p ? kl[j + 1] : kl[j];
+        if (depth > (uint32_t)C)
+            kl[C - 1] = p ? 0u : kl[C - 1];
+        slots = p ? slots >> 3 : slots;
+    };
+    auto round = [&](uint32_t it, uint32_t depth) {
+        uint32_t h = key[0][0];
+#pragma unroll
+        for (int l = 1; l < L; ++l)
+            h = max(h, key[l][0]);
+        uint32_t m = h;
+        m = dpp_umax<0xB1>(m);  // quad_perm [1,0,3,2]
+        m = dpp_umax<0x4E>(m);  // quad_perm [2,3,0,1]
+        m = dpp_umax<0x141>(m); // row_half_mirror
+        m = dpp_umax<0x140>(m); // row_mirror: every lane holds its row's maximum
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(h == m);
+        // the lowest set bit of each row's 16 bits (every row has one)
+        const uint64_t win = hit & ~(hit - 0x0001000100010001ull);
+        const bool w = __builtin_amdgcn_inverse_ballot_w64(win);
+        // the first list whose head is the lane's head (equal keys: the
+        // earlier list's experts have the smaller indices)
+        bool taken = false;
+        uint32_t pick = 0;
+        bool p[L];
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const bool is_l = !taken && key[l][0] == h;
+            pick = is_l ? base + l * C + (sl[l] & 7u) : pick;
+            taken = taken || is_l;
+            p[l] = w && is_l;
+        }
+#pragma unroll
+        for (int l = 0; l < L; ++l)
+            pop(key[l], sl[l], depth, p[l]);
+        if (w)
+            pick_row[it] = make_uint2(pick, h);
+    };
+    if constexpr (K8) {
+#pragma unroll
+        for (uint32_t it = 0; it < 8; ++it)
+            round(it, 8u - it);
+    } else {
+        uint32_t it = 0;
+        for (; it + 1 < k; it += 2) {
+            round(it, 64u);
+            round(it + 1, 64u);
+        }
+        if (it < k)
+            round(it, 64u);
+    }
+    rows_store<K8>(scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
+}
+
 // Group ranks within 16-lane rows (one token per row, 16 >> GL groups of
 // 2^GL lanes): group H's sum, as an order-preserving key, reaches every lane
 // of the row by row_newbcast from the group's first lane, and a lane counts
@@ -1115,6 +1219,32 @@ extern "C" tk_status tk_topk_gate(const float* scores, int64_t tokens, int64_t e
 #undef TK_TOPK2L
 #undef TK_TOPK2L_LAUNCH
         return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;
+    }
+    // no groups, 257 to 512 experts, k <= 16: one token per 16-lane row, L = 3 or 4 lists per lane
+    if (n_group == 1 && experts > 256 && k <= 16) {
+        const uint32_t tpb = 4 * (kThreads / kWave);
+        const uint32_t rblocks = (uint32_t)((tokens + tpb - 1) / tpb);
+        const uint32_t L = (uint32_t)((experts + 127) / 128), Cl = (uint32_t)((experts + 16 * L - 1) / (16 * L));
+        const bool full = experts == (int64_t)(16 * L * Cl);
+#define TK_TOPKL_LAUNCH(CC, LL, K8, FULL)                                                                     \
+    hipLaunchKernelGGL((topk_rowl_kernel<CC, LL, K8, FULL>), dim3(rblocks), dim3(kThreads), 0, s, scores,     \
+                       (uint32_t)tokens, (uint32_t)experts, (uint32_t)k, normalise, topk_idx, topk_weight)
+#define TK_TOPKL(CC, LL)                                                                                      \
+    if (Cl == (CC) && L == (LL)) {                                                                            \
+        if (full) {                                                                                           \
+            if (k == 8) TK_TOPKL_LAUNCH(CC, LL, true, true); else TK_TOPKL_LAUNCH(CC, LL, false, true);       \
+        } else {                                                                                              \
+            if (k == 8) TK_TOPKL_LAUNCH(CC, LL, true, false); else TK_TOPKL_LAUNCH(CC, LL, false, false);     \
+        }                                                                                                     \
+        return hipGetLastError() == hipSuccess ? TK_OK : TK_ERR_HIP;                                          \
+    }
+        TK_TOPKL(6, 3)
+        TK_TOPKL(7, 3)
+        TK_TOPKL(8, 3)
+        TK_TOPKL(7, 4)
+        TK_TOPKL(8, 4)
+#undef TK_TOPKL
+#undef TK_TOPKL_LAUNCH
     }
     // one token per 16-lane row in one pass: 16 * C16 experts (C16 even, 4 to
     // 16 per lane) in 2, 4 or 8 groups of 2^GL lanes, kept groups within 8 lanes

@@ -73,8 +73,10 @@ SHAPES = [  # (experts, k, n_group, topk_group)
     # the last lanes part-filled or empty when experts is not a multiple of 16; k = 17 stays two to a wave
     (128, 8, 1, 1), (128, 16, 1, 1), (60, 4, 1, 1), (112, 9, 1, 1), (16, 16, 1, 1), (120, 5, 1, 1),
     (17, 3, 1, 1), (128, 17, 1, 1),
-    # no groups, 129 to 256 experts and k <= 16: two lists of 5 to 8 experts per lane
+    # no groups, 129 to 256 experts and k <= 16: two lists of 5 to 8 experts per lane; 257 to 512:
+    # three or four lists of 6 to 8
     (160, 8, 1, 1), (256, 16, 1, 1), (129, 3, 1, 1), (250, 10, 1, 1), (192, 1, 1, 1), (224, 6, 1, 1),
+    (384, 8, 1, 1), (512, 10, 1, 1), (320, 7, 1, 1), (448, 16, 1, 1), (257, 3, 1, 1), (500, 9, 1, 1),
 ]
 
 
@@ -220,11 +222,11 @@ def _random_shape(rng):
     """A valid gating shape: experts up to 512, a group count dividing them
     with at least 2 experts per group, topk_group groups kept, k at most the
     candidates and at most 64.  A sixth of the draws have no groups, up to
-    256 experts and k <= 16; a third of the rest are the one-pass row
+    512 experts and k <= 16; a third of the rest are the one-pass row
     layout's shapes: a multiple of 32 experts from 64 to 256 in 2, 4 or 8
     groups whose kept groups fit half a 16-lane row."""
-    if rng.random() < 1 / 6:  # no groups, up to 256 experts, k <= 16: one token per 16-lane row
-        E = int(rng.integers(1, 257))
+    if rng.random() < 1 / 6:  # no groups, up to 512 experts, k <= 16: one token per 16-lane row
+        E = int(rng.integers(1, 513))
         return E, int(rng.integers(1, min(16, E) + 1)), 1, 1
     if rng.random() < 1 / 3:
         E = int(rng.choice([64, 96, 128, 160, 192, 224, 256]))
