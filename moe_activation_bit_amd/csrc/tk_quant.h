@@ -44,6 +44,7 @@ struct Params {
     uint32_t gslots;        // segmented and two-pass units: lane slots (8 columns) per group
     uint32_t gpu;           // segmented units: groups per unit
     uint32_t gmagic;        // segmented units: ceil(2^32 / gslots), so that q / gslots = mulhi(q, gmagic)
+    uint32_t xcd_order;     // fused grid-stride kernels: 1 = XCD-contiguous block order (grid a multiple of 8)
 };
 
 // Scale layouts (the value kind -- fp32 or UE8M0 byte -- is the SFMT template):

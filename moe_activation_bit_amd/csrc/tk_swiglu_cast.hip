@@ -435,9 +435,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
     // b / 8 gives each XCD a contiguous share of the grid, so in every pass of
     // the grid-stride loop each XCD (and its L2) streams one contiguous eighth
     // of the window (FP4 workload 212 -> 206 us).  A bijection whenever the
-    // grid is a multiple of 8; other grids keep the plain order.
+    // grid is a multiple of 8; other grids, and launches the host marks (see
+    // xcd_order), keep the plain order.
     uint32_t block = blockIdx.x;
-    if ((gridDim.x & 7u) == 0)
+    if (p.xcd_order && (gridDim.x & 7u) == 0)
         block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     // wave-uniform by construction; readfirstlane lets the compiler keep all
     // unit bookkeeping (row, step, addresses) in scalar registers
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_xw_kernel(Params p)
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     uint32_t block = blockIdx.x;
-    if ((gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
+    if (p.xcd_order && (gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
         block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const uint32_t slot_in_pass = wib / W, part = wib % W;
     const uint32_t groups = p.units / W;
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_seg_kernel(Params p)
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
     const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     uint32_t block = blockIdx.x;
-    if ((gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
+    if (p.xcd_order && (gridDim.x & 7u) == 0) // XCD-contiguous order, as in the one-wave kernel
         block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(block * kWaves + wib);
     const uint32_t nwaves = gridDim.x * kWaves;
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_2p_kernel(Params p)
 
     const uint32_t lane = threadIdx.x & (kWaveSize - 1);
     uint32_t block = blockIdx.x;
-    if ((gridDim.x & 7u) == 0)
+    if (p.xcd_order && (gridDim.x & 7u) == 0)
         block = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(block * kWaves + (threadIdx.x / kWaveSize));
     const uint32_t nwaves = gridDim.x * kWaves;
@@ -1036,6 +1037,16 @@ tk_status swiglu_cast(int fmt, const void* x, const float* w, int64_t n, int64_t
     const uint32_t per_cu = small ? kBlocksPerCUSmall : kBlocksPerCU;
     const uint32_t cap = cus * per_cu;
     const int blocks = (int)(want < cap ? want : cap);
+    // The XCD-contiguous block order puts the units of a partial last pass of
+    // the grid-stride loop on the lowest-numbered XCDs; the plain order spreads
+    // them over all eight.  That matters for a small launch of a few passes:
+    // when its units do not fill the passes evenly it keeps the plain order
+    // (interleaved A/B replayed from graphs, outputs identical: 1000 x 7168
+    // per-block 9.18 -> 8.54 us, 2000 x 7168 15.72 -> 14.13, 600 x 7168
+    // 7.07 -> 6.91; every other shape measured within 1%), while small
+    // launches that fill their passes evenly, and every large one, keep the
+    // XCD order, which measured up to 4% faster for them.
+    p.xcd_order = (!small || p.units % ((uint32_t)blocks * waves_per_block) == 0) ? 1u : 0u;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool ok;

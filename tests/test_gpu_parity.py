@@ -7,6 +7,7 @@ Every output buffer is surrounded by canary bands that must stay untouched.
 import math
 import os
 import sys
+import types
 
 import numpy as np
 import pytest
@@ -337,6 +338,31 @@ def test_any_group_width(case, fmt, sfmt, clamp):
     wt = wl.make_w(base, 6)[:rows]
     got = run_cast(x, wt, hidden, group, clamp, fmt, sfmt)
     assert_same(got, oracle.swiglu_cast(x, wt, group, clamp, fmt, sfmt), f"{case} {fmt} {sfmt} {clamp}")
+
+
+# Small launches (at most 64 units per CU) that take more than one pass of the
+# grid-stride loop and leave the last pass partial: these run in the plain
+# workgroup order instead of the XCD-contiguous one.  One case per kernel form:
+# 4-step row-reduced units, streamed 8-step units, per-block 4-lane and
+# 64-lane groups, a row split over two waves, segmented groups.
+PARTIAL_PASS = [  # (rows, hidden, group, fmt, scale_fmt, clamp)
+    (4500, 2048, 0, 8, 0, 10.0), (4500, 4096, 0, 8, 1, 10.0), (2100, 4096, 32, 4, 1, None),
+    (2500, 4096, 512, 8, 0, None), (2100, 16384, 0, 8, 0, None), (700, 7168, 896, 8, 0, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_PASS, ids=str)
+def test_small_launch_partial_last_pass(case):
+    """Every row against the oracle where the last grid-stride pass is partial."""
+    rows, hidden, group, fmt, sfmt, clamp = case
+    say("partial last pass", case)
+    base = wl.WORKLOADS["fp8_per_token_clamp10_n131072_h2048"]
+    x = rows_of_width(base, 8, rows, hidden)
+    wt = wl.make_w(base, 8)[:rows]
+    got = run_cast(x, wt, hidden, group, clamp, fmt, sfmt)
+    wk = types.SimpleNamespace(group_size=group, clamp_limit=clamp, fmt="fp8" if fmt == 8 else "fp4",
+                               scale_fmt="fp32" if sfmt == tk.TK_SCALE_FP32 else "ue8m0")
+    assert_same(got, oracle_cast_all_rows(x, wt, wk), str(case))
 
 
 def test_batch_invariance_and_pointer_offsets():
