@@ -264,7 +264,11 @@ struct Unit {
     float w;
 };
 
-template <int SPU, bool ROWRED, bool PARTIAL>
+// NOBRANCH: a row-reduced unit shorter than SPU steps re-reads its last step
+// for the rest instead of skipping them, so that no branch surrounds the loads
+// (a branch would make a later wait for loads issued before these count the
+// worst case of both paths).
+template <int SPU, bool ROWRED, bool PARTIAL, bool NOBRANCH = false>
 __device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t lane, Unit<SPU>& d)
 {
     d.row = u / p.upr;
@@ -277,8 +281,9 @@ __device__ __forceinline__ void load_unit(const Params& p, uint32_t u, uint32_t 
     const uint32_t lane_off = (d.step0 * kWaveSize + lane) * 16u;
 #pragma unroll
     for (int s = 0; s < SPU; ++s) {
-        if (!ROWRED || s < (int)d.nst) {
-            uint32_t off = lane_off + (uint32_t)s * (kWaveSize * 16u);
+        if (NOBRANCH || !ROWRED || s < (int)d.nst) {
+            const uint32_t st = (ROWRED && NOBRANCH) ? min((uint32_t)s, d.nst - 1u) : (uint32_t)s;
+            uint32_t off = lane_off + st * (kWaveSize * 16u);
             if (PARTIAL) // lanes past the row end re-read its last slot
                 off = min(off, (p.slots - 1u) * 16u);
             d.g[s] = load16(reinterpret_cast<const uint4*>(xg + off));
@@ -421,7 +426,10 @@ __device__ __forceinline__ void streamed_rowred_loop(const Params& p, LutT* lut,
 // A/B, bit-identical: 349 x 7168 ragged 5.56 -> 5.24 us replayed from a graph,
 // 1000 x 7168 9.70 -> 9.03, 2400 x 2048 per-block 8.22 -> 7.98; on the large
 // launches it cost 1-3%).
-template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false, bool T16 = false>
+// TFIRST: a single-pass launch (no wave has more than one unit), which orders
+// the table fill differently (below).
+template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL, bool WIDE = false, bool T16 = false,
+          bool TFIRST = false>
 __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
 {
     constexpr int kTableBytes = T16 ? kLut16LdsBytes : kLutLdsBytes;
@@ -450,25 +458,66 @@ __global__ __launch_bounds__(kThreads) void swiglu_cast_kernel(Params p)
         return;
     }
 
-    // The table's global loads go out first and the first unit's loads right
-    // behind them; loads return in order, so the table reaches LDS without
-    // waiting for the unit, and the unit's latency overlaps the table fill
-    // (what a launch of a few hundred rows spends most of its time on).
+    // The table's global loads and the first unit's are in flight together,
+    // so the unit's latency overlaps the table fill (what a launch of a few
+    // hundred rows spends most of its time on).  Loads return in order, and
+    // the compiler issues the unit's loads first: the table's wait then waits
+    // for the unit as well, and the table reaches LDS (and the barrier
+    // passes) only once both are in.
     constexpr int kLutPerThread = kTableBytes / 16 / kThreads;
-    static_assert(kLutPerThread * 16 * kThreads == kTableBytes, "table split");
+    static_assert(kLutPerThread == 4 || kLutPerThread == 8, "table split");
     const uint4* table = T16 ? reinterpret_cast<const uint4*>(g_sigma_lut16) : reinterpret_cast<const uint4*>(g_sigma_lut);
-    uint4 lut_part[kLutPerThread];
-#pragma unroll
-    for (int i = 0; i < kLutPerThread; ++i)
-        lut_part[i] = table[i * kThreads + threadIdx.x];
     if (CLAMP && threadIdx.x == 0)
         wg_clamped = 0;
     Unit<SPU> first;
-    if (wave < p.units)
-        load_unit<SPU, ROWRED, PARTIAL>(p, wave, lane, first);
+    if constexpr (TFIRST) {
+        const uint4* tsrc = table + threadIdx.x;
+        uint4* tdst = reinterpret_cast<uint4*>(lut_raw) + threadIdx.x;
+        // A single-pass launch issues the table's loads first and the unit's
+        // behind them, so the table reaches LDS and the barrier passes while
+        // the unit is still in flight.  The table's wait is then a partial
+        // one (vmcnt of the unit's loads): the scheduling barrier keeps the
+        // unit's loads from being hoisted above the table's, and the unit's
+        // loads are issued without a branch (a wave past the last unit
+        // re-reads the last one and does not process it).  Interleaved A/B
+        // replayed from graphs, outputs identical: ragged 349 x 7168 per-block
+        // 5.23 -> 4.90 us, 17 x 7168 2.39 -> 2.21, 256 x 1024 per-token 2.72
+        // -> 2.61, 2400 x 2048 per-block 8.08 -> 7.43.  In launches of several
+        // passes the same order measured from 9% slower (700 x 7168) to 6%
+        // faster (5000 x 2048), so they keep the compiler's order.  Named
+        // registers rather than an array: with the scheduling barrier an
+        // array of them was kept in scratch memory.
+        const uint4 t0 = tsrc[0], t1 = tsrc[kThreads], t2 = tsrc[2 * kThreads], t3 = tsrc[3 * kThreads];
+        uint4 t4{}, t5{}, t6{}, t7{};
+        if constexpr (kLutPerThread == 8) {
+            t4 = tsrc[4 * kThreads];
+            t5 = tsrc[5 * kThreads];
+            t6 = tsrc[6 * kThreads];
+            t7 = tsrc[7 * kThreads];
+        }
+        __builtin_amdgcn_sched_barrier(0x0F); // arithmetic may cross, memory instructions may not
+        load_unit<SPU, ROWRED, PARTIAL, true>(p, wave < p.units ? wave : p.units - 1u, lane, first);
+        tdst[0] = t0;
+        tdst[kThreads] = t1;
+        tdst[2 * kThreads] = t2;
+        tdst[3 * kThreads] = t3;
+        if constexpr (kLutPerThread == 8) {
+            tdst[4 * kThreads] = t4;
+            tdst[5 * kThreads] = t5;
+            tdst[6 * kThreads] = t6;
+            tdst[7 * kThreads] = t7;
+        }
+    } else {
+        uint4 lut_part[kLutPerThread];
 #pragma unroll
-    for (int i = 0; i < kLutPerThread; ++i)
-        reinterpret_cast<uint4*>(lut_raw)[i * kThreads + threadIdx.x] = lut_part[i];
+        for (int i = 0; i < kLutPerThread; ++i)
+            lut_part[i] = table[i * kThreads + threadIdx.x];
+        if (wave < p.units)
+            load_unit<SPU, ROWRED, PARTIAL>(p, wave, lane, first);
+#pragma unroll
+        for (int i = 0; i < kLutPerThread; ++i)
+            reinterpret_cast<uint4*>(lut_raw)[i * kThreads + threadIdx.x] = lut_part[i];
+    }
     __syncthreads();
 
     float limit = 0.0f, a_limit = 0.0f;
@@ -821,9 +870,13 @@ template <int FMT, int SFMT, bool CLAMP, int SPU, bool ROWRED, bool PARTIAL>
 void launch_one(const Params& p, int blocks, bool small, hipStream_t stream)
 {
     constexpr bool kCanT16 = !(ROWRED && SPU >= kStreamMinSteps);
+    const bool single = p.units <= (uint32_t)blocks * (kThreads / kWaveSize); // one pass of the grid
     if constexpr (!ROWRED) {
         if (p.gl_log2 >= 5) { // per-block groups of 32 or 64 lanes
-            if (small)
+            if (small && single)
+                hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true, true, true>),
+                                   dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (small)
                 hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, true, true>),
                                    dim3(blocks), dim3(kThreads), 0, stream, p);
             else
@@ -833,6 +886,11 @@ void launch_one(const Params& p, int blocks, bool small, hipStream_t stream)
         }
     }
     if constexpr (kCanT16) {
+        if (small && single) {
+            hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, false, true, true>),
+                               dim3(blocks), dim3(kThreads), 0, stream, p);
+            return;
+        }
         if (small) {
             hipLaunchKernelGGL((swiglu_cast_kernel<FMT, SFMT, CLAMP, SPU, ROWRED, PARTIAL, false, true>), dim3(blocks),
                                dim3(kThreads), 0, stream, p);
