@@ -355,6 +355,56 @@ __device__ __forceinline__ void sort_lane(uint32_t (&key)[C], uint32_t (&idx)[C]
     }
 }
 
+// A lane's 8 raw scores (float bits, none NaN) sorted best first by (score,
+// smaller slot), as sort_lane<8> sorts their keys, on 64-bit doubles: the
+// high word is the score's own bits (-0 made +0), the low word the tie-break,
+// 7 - slot for a non-negative score and slot for a negative one (a double's
+// order runs backwards with its sign).  No NaN score makes a NaN or infinite
+// double (that needs the top three mantissa bits set under an all-ones
+// exponent), fp64 denormals are kept, and every word of a lane differs, so the
+// 19 comparators are a max and a min each (v_max_f64 / v_min_f64, written out
+// so that the compiler adds no canonicalising operation): 38 instructions
+// instead of a 64-bit compare and four selects per comparator.  Returns the
+// order-preserving keys and idx[j] = 7 - slot of entry j, as sort_lane does.
+__device__ __forceinline__ double dmax(double a, double b)
+{
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double dmin(double a, double b)
+{
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ void sort_lane_raw8(uint32_t (&key)[8], uint32_t (&idx)[8])
+{
+    double x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t h = fbits(ffrom(key[j]) + 0.0f); // -0 + +0 = +0
+        const uint32_t l = (uint32_t)(7 - j) ^ ((uint32_t)((int32_t)h >> 31) & 7u);
+        x[j] = __builtin_bit_cast(double, ((uint64_t)h << 32) | l);
+    }
+    constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                                {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+    for (int c = 0; c < 19; ++c) {
+        const double a = x[net[c][0]], b = x[net[c][1]];
+        x[net[c][0]] = dmax(a, b);
+        x[net[c][1]] = dmin(a, b);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x[j]);
+        const uint32_t h = (uint32_t)(u >> 32);
+        const uint32_t s = (uint32_t)((int32_t)h >> 31);
+        key[j] = h ^ (s | 0x80000000u);
+        idx[j] = (uint32_t)u ^ (s & 7u);
+    }
+}
+
 // The rank of this lane's group among its token's groups in the two-token
 // layout (a group is 2^gl_log2 <= 32 lanes inside its half), from the lane's
 // two best keys a1 >= a2 (0 = none); 0 is the best group.
@@ -532,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void topk_pair_kernel(const float* __rest
 // round's winners write their pick and its key into s_pick at the round's
 // position), and output lane q of row r stores pick q, its weight the key's
 // value.
-template <int C, bool K8>
+template <int C, bool K8, bool RAW8 = false>
 __device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, bool filled,
                                             const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
                                             uint32_t k, int normalise, int32_t* __restrict__ idx_out,
@@ -566,13 +616,13 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
             w8[4 * w + 3] = x.w;
         }
 #pragma unroll
-        for (int j = 0; j < C; ++j)
-            key[j] = RAW ? ordered(ffrom(w8[j])) : w8[j];
+        for (int j = 0; j < C; ++j) // eight raw scores go to rows_select as they are (sort_lane_raw8)
+            key[j] = (RAW && C != 8) ? ordered(ffrom(w8[j])) : w8[j];
     }
     // the expert index of this lane's first slot (read by every lane: an
     // empty lane never wins, since k is at most the candidates)
-    rows_select<C, K8>(key, s_src[lane], filled, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane,
-                       s_pick);
+    rows_select<C, K8, RAW && C == 8>(key, s_src[lane], filled, scores, tokens, experts, k, normalise, idx_out,
+                                      w_out, t0, lane, s_pick);
 }
 
 // The steps of the four-tokens-per-wave kernels from the sort on: row r =
@@ -583,7 +633,9 @@ __device__ __forceinline__ void quad_rows_finish(const float* __restrict__ score
 // so one round serves four tokens; a round's winners write their pick and its
 // key into s_pick at the round's position), and output lane q of row r stores
 // pick q, its weight the key's value.
-template <int C, bool K8>
+// RAW8: C = 8 and key[] holds the raw scores (float bits), which
+// sort_lane_raw8 sorts and turns into keys.
+template <int C, bool K8, bool RAW8>
 __device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, bool filled,
                                             const float* __restrict__ scores, uint32_t tokens, uint32_t experts,
                                             uint32_t k, int normalise, int32_t* __restrict__ idx_out,
@@ -592,7 +644,12 @@ __device__ __forceinline__ void rows_select(uint32_t (&key)[C], uint32_t base, b
     const uint32_t q = lane & 15u;
     const uint32_t row = lane >> 4;
     uint32_t idx[C];
-    sort_lane<C>(key, idx);
+    if constexpr (RAW8) {
+        static_assert(C == 8, "eight raw scores");
+        sort_lane_raw8(key, idx);
+    } else {
+        sort_lane<C>(key, idx);
+    }
     // a lane past the row's filled ones sorts whatever it was given; an empty
     // head keeps it from ever winning, so its other keys are never read
     key[0] = filled ? key[0] : 0u;
@@ -798,11 +855,14 @@ __global__ __launch_bounds__(kThreads) void topk_row1_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < C; ++j)
         v[j] = FULL ? s_row[q * C + j] : s_row[min(q * C + j, experts - 1u)];
+    // eight scores of a full row go to rows_select raw (sort_lane_raw8)
+    constexpr bool kRaw8 = C == 8 && FULL;
     uint32_t key[C];
 #pragma unroll
     for (int j = 0; j < C; ++j)
-        key[j] = (FULL || q * C + j < experts) ? ordered(v[j]) : 0u;
-    rows_select<C, K8>(key, q * C, true, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane, s_pick[wv]);
+        key[j] = kRaw8 ? fbits(v[j]) : (FULL || q * C + j < experts) ? ordered(v[j]) : 0u;
+    rows_select<C, K8, kRaw8>(key, q * C, true, scores, tokens, experts, k, normalise, idx_out, w_out, t0, lane,
+                              s_pick[wv]);
 }
 
 // Four tokens per wave without groups, 129 to 256 experts and k <= 16: lane q
@@ -832,13 +892,23 @@ __global__ __launch_bounds__(kThreads) void topk_row2_kernel(const float* __rest
     for (int j = 0; j < 2 * C; ++j)
         v[j] = FULL ? s_row[q * (2 * C) + j] : s_row[min(q * (2 * C) + j, experts - 1u)];
     uint32_t ka[C], kb[C], ia[C], ib[C];
+    if constexpr (C == 8 && FULL) { // full lists of eight: sorted from the raw scores
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-        ka[j] = (FULL || q * (2 * C) + j < experts) ? ordered(v[j]) : 0u;
-        kb[j] = (FULL || q * (2 * C) + C + j < experts) ? ordered(v[C + j]) : 0u;
+        for (int j = 0; j < C; ++j) {
+            ka[j] = fbits(v[j]);
+            kb[j] = fbits(v[C + j]);
+        }
+        sort_lane_raw8(ka, ia);
+        sort_lane_raw8(kb, ib);
+    } else {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            ka[j] = (FULL || q * (2 * C) + j < experts) ? ordered(v[j]) : 0u;
+            kb[j] = (FULL || q * (2 * C) + C + j < experts) ? ordered(v[C + j]) : 0u;
+        }
+        sort_lane<C>(ka, ia);
+        sort_lane<C>(kb, ib);
     }
-    sort_lane<C>(ka, ia);
-    sort_lane<C>(kb, ib);
     // slot lists, head lowest, 3 bits each
     uint32_t sa = 0, sb = 0;
 #pragma unroll
@@ -927,6 +997,7 @@ __global__ __launch_bounds__(kThreads) void topk_rowl_kernel(const float* __rest
 #pragma unroll
     for (int l = 0; l < L; ++l) {
         uint32_t id[C];
+        // (sort_lane_raw8 here: 512 experts 4% slower)
 #pragma unroll
         for (int j = 0; j < C; ++j)
             key[l][j] = (FULL || base + l * C + j < experts) ? ordered(v[l * C + j]) : 0u;
