@@ -190,6 +190,39 @@ def test_topk_special_values_and_extremes():
     assert gi[0, 0] == 0 and gw[0, 0] == 1.0
 
 
+# Values that stress the per-lane sort of the four-token kernels (eight
+# scores per lane sorted as doubles: score bits high, tie-break low): equal
+# negative scores (their tie-break runs backwards as doubles), signed zeros,
+# subnormals of both signs, the largest finite values and infinities.
+LANE_ALPHABET = np.array([-np.inf, -3.0e38, -1.5, -1.5, -1e-40, -1e-45, -0.0, 0.0, 1e-45, 1e-40, 1.5, 1.5, 3.0e38,
+                          np.inf], dtype=np.float32)
+
+
+@pytest.mark.parametrize("shape", [(256, 8, 8, 4), (256, 6, 8, 3), (128, 8, 1, 1), (256, 8, 1, 1), (256, 16, 1, 1),
+                                   (512, 8, 1, 1)], ids=str)
+@pytest.mark.parametrize("finite", [False, True], ids=["with-inf", "finite"])
+def test_topk_lane_sort_ties_and_special_values(shape, finite):
+    """Every lane's eight scores drawn from a small alphabet of special values,
+    so that ties, signed zeros, subnormals and infinities meet inside one lane's
+    sort; indices and weights against the oracle (normalised when finite)."""
+    E, k, ng, tg = shape
+    print("[gpu-case] topk lane sort", shape, finite, flush=True)
+    T = 257
+    alphabet = LANE_ALPHABET[2:-2] if finite else LANE_ALPHABET  # finite: sums stay finite too
+    u = wl.uniform(wl.stream_key("topk_test", E * 100 + k, "lane_sort"), 0, T * E).reshape(T, E)
+    s = alphabet[np.minimum((u * len(alphabet)).astype(np.int64), len(alphabet) - 1)]
+    s[3] = -1.5  # a row of equal negative scores
+    s[4, ::2] = -0.0
+    s[4, 1::2] = 0.0
+    normalise = 1 if finite else 0
+    gi, gw = run(s, k, ng, tg, normalise)
+    oi, ow = oracle.topk_gate(s, k, ng, tg, bool(normalise))
+    bad = np.argwhere(gi != oi)
+    assert bad.size == 0, f"indices differ at {bad[:4].tolist()}: {gi[bad[0][0]]} vs {oi[bad[0][0]]}"
+    same = (gw.view(np.uint32) == ow.view(np.uint32)) | (np.isnan(gw) & np.isnan(ow))
+    assert same.all(), np.argwhere(~same)[:4]
+
+
 @pytest.mark.parametrize("ng,tg", [(8, 4), (8, 7), (4, 2), (16, 3), (6, 3)])
 def test_topk_nan_group_sums(ng, tg):
     """A group whose two best scores are +inf and -inf sums to NaN and ranks
